@@ -1,0 +1,252 @@
+"""CPU oracle for the paged MLA latent-K path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product (the HIP library and its
+binding) never does, and this package never imports the product: the two
+share nothing but the seeded inputs from ``workloads``.
+
+The arithmetic lives in ``mla_oracle.c`` (plain scalar C, binary64 sums in k
+order); this module builds it with gcc and marshals numpy arrays.  Every
+function cites the page passage it follows in the C source.
+
+Parity pins (tests/test_oracle_*.py, all ``-m "not gpu"``):
+  * codecs: all 65536 bf16 and all 256 e4m3fn codes against torch's casts,
+    e4m3 rounding (ties, subnormals, saturation) against torch and closed forms;
+  * gather: tagged pools whose elements name their own page/slot/column, the
+    identity page table equal to a contiguous slice, page_size 1 equal to an
+    index_select, precondition errors;
+  * products: numpy float64 matmul, identity and selection weights, NaN rope
+    columns ignored, lossless fp8 blocks equal to the plain product, the
+    e4m3 relative error bound, all-zero blocks;
+  * write path: selection weight puts hidden columns into the named slots,
+    destinations are distinct and inside the pages the page table lists.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mla_oracle.c")
+_BUILD_DIR = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_BUILD_DIR, "liboracle.so")
+# tests that plant mistakes in a copy of the oracle point this at the mutant
+_OVERRIDE = os.environ.get("MLA_ORACLE_LIB_OVERRIDE")
+_lock = threading.Lock()
+_lib = None
+
+F32, BF16, E4M3 = 0, 1, 2
+_DT = {"f32": F32, "bf16": BF16, "e4m3": E4M3}
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_u32 = ctypes.c_uint32
+_int = ctypes.c_int
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math, no FMA contraction)."""
+    os.makedirs(_BUILD_DIR, exist_ok=True)
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+               "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if _OVERRIDE:
+            lib = ctypes.CDLL(_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB_PATH)
+        lib.or_bf16_decode.argtypes = [_p, _p, _i64]
+        lib.or_e4m3_decode.argtypes = [_p, _p, _i64]
+        lib.or_e4m3_encode.argtypes = [_p, _p, _i64]
+        lib.or_gather.argtypes = [_p, _int, _i64, _i64, _i64, _u32, _u32, _u32, _p, _u32, _u32,
+                                  _p, _p, _p, _i64, _u32, _i64, _p]
+        lib.or_gather.restype = _int
+        lib.or_matmul_nt.argtypes = [_p, _int, _i64, _p, _int, _i64, _i64, _i64, _p, _i64, _p]
+        lib.or_quantize_e4m3_rows.argtypes = [_p, _i64, _i64, _i64, _i64, _p, _p]
+        lib.or_fp8_matmul_nt.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _i64, _p]
+        lib.or_matmul_nn.argtypes = [_p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p]
+        lib.or_kv_destinations.argtypes = [_i64, _i64, _i64, _i64, _u32, _u32, _u32, _p, _u32,
+                                           _u32, _p, _p, _u32, _p]
+        lib.or_kv_destinations.restype = _int
+        _lib = lib
+        return lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+# ---------------------------------------------------------------------------
+# codecs
+# ---------------------------------------------------------------------------
+def bf16_decode(bits: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, np.float32)
+    _load().or_bf16_decode(_ptr(bits), _ptr(out), bits.size)
+    return out
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape, np.float64)
+    _load().or_e4m3_decode(_ptr(codes), _ptr(out), codes.size)
+    return out
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint8)
+    _load().or_e4m3_encode(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# gather
+# ---------------------------------------------------------------------------
+def gather(case, *, check_lengths: bool = True) -> np.ndarray:
+    """k_latent_buffer [M, D_c] (raw bits, the pool's element type)."""
+    c = case.cache
+    sp, sl, skv, st = c.strides()
+    M, D = case.M, case.D_c
+    out = np.empty((M, D), dtype=c.pool.dtype)
+    pt = np.ascontiguousarray(c.page_table, np.uint32)
+    cl = np.ascontiguousarray(c.cache_lengths, np.uint32)
+    bro = np.ascontiguousarray(case.buffer_row_offsets, np.uint32)
+    co = np.ascontiguousarray(case.cache_offsets, np.uint32)
+    rc = _load().or_gather(_ptr(c.pool), c.elem_bytes, sp, sl, st, c.num_pages, c.num_layers,
+                           c.page_size, _ptr(pt), c.max_pages_per_seq, case.batch,
+                           _ptr(cl) if check_lengths else None, _ptr(bro), _ptr(co), M,
+                           case.layer_idx, D, _ptr(out) if out.size else None)
+    if rc != 0:
+        raise OracleError(f"gather precondition failed ({rc})")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# products
+# ---------------------------------------------------------------------------
+def _rows_arg(rows, M):
+    if rows is None:
+        rows = np.arange(M, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    return rows
+
+
+def matmul_nt(A_bits, a_dtype, W_bits, w_dtype, K, rows=None) -> np.ndarray:
+    """out[j, n] = sum_{k<K} A[rows[j], k] * W[n, k] in binary64."""
+    A_bits = np.ascontiguousarray(A_bits)
+    W_bits = np.ascontiguousarray(W_bits)
+    rows = _rows_arg(rows, A_bits.shape[0])
+    N = W_bits.shape[0]
+    out = np.empty((len(rows), N), np.float64)
+    if len(rows) and N:
+        _load().or_matmul_nt(_ptr(A_bits), _DT[a_dtype], A_bits.shape[1], _ptr(W_bits),
+                             _DT[w_dtype], W_bits.shape[1], N, K, _ptr(rows), len(rows), _ptr(out))
+    return out
+
+
+def quantize_e4m3_rows(A_bf16_bits, K, k_gran=128):
+    """(codes uint8 [M, K], scales float32 [M, ceil(K/k_gran)]) of the first K columns."""
+    A = np.ascontiguousarray(A_bf16_bits, dtype=np.uint16)
+    M = A.shape[0]
+    nkb = -(-K // k_gran)
+    q = np.empty((M, K), np.uint8)
+    s = np.empty((M, nkb), np.float32)
+    if M:
+        _load().or_quantize_e4m3_rows(_ptr(A), A.shape[1], M, K, k_gran, _ptr(q), _ptr(s))
+    return q, s
+
+
+def fp8_matmul_nt(q_a, s_a, q_w, s_w, n_gran=128, k_gran=128, rows=None) -> np.ndarray:
+    q_a = np.ascontiguousarray(q_a, np.uint8)
+    s_a = np.ascontiguousarray(s_a, np.float32)
+    q_w = np.ascontiguousarray(q_w, np.uint8)
+    s_w = np.ascontiguousarray(s_w, np.float32)
+    M, K = q_a.shape
+    N = q_w.shape[0]
+    assert q_w.shape[1] == K and s_w.shape == (-(-N // n_gran), -(-K // k_gran))
+    rows = _rows_arg(rows, M)
+    out = np.empty((len(rows), N), np.float64)
+    if len(rows) and N:
+        _load().or_fp8_matmul_nt(_ptr(q_a), _ptr(s_a), _ptr(q_w), _ptr(s_w), N, K, n_gran, k_gran,
+                                 _ptr(rows), len(rows), _ptr(out))
+    return out
+
+
+def matmul_nn(H_bits, W_bits, rows=None) -> np.ndarray:
+    """out[j, n] = sum_k H[rows[j], k] * W[k, n] in binary64 (bf16 operands)."""
+    H = np.ascontiguousarray(H_bits, np.uint16)
+    W = np.ascontiguousarray(W_bits, np.uint16)
+    rows = _rows_arg(rows, H.shape[0])
+    K, N = W.shape
+    assert H.shape[1] == K
+    out = np.empty((len(rows), N), np.float64)
+    if len(rows) and N:
+        _load().or_matmul_nn(_ptr(H), K, _ptr(W), N, N, K, _ptr(rows), len(rows), _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# whole operations, composed from the steps above in the pages' order
+# ---------------------------------------------------------------------------
+def decompress_k(case, rows=None):
+    """(k_latent bits [M, D_c], k_buffer rows as binary64 [len(rows), N]).
+
+    Gather, then multiply the first K columns of each gathered row by W_k^T."""
+    lat = gather(case)
+    if case.weight_dtype == "e4m3":
+        raise OracleError("use decompress_k_fp8 for an e4m3 weight")
+    out = matmul_nt(lat, case.cache.dtype, case.weight, case.weight_dtype, case.K, rows)
+    return lat, out
+
+
+def decompress_k_fp8(case, rows=None):
+    """(k_latent bits, activation codes, activation scales, k_buffer rows binary64)."""
+    lat = gather(case)
+    q, s = quantize_e4m3_rows(lat, case.K, case.k_gran)
+    out = fp8_matmul_nt(q, s, case.weight_q, case.weight_scale, case.n_gran, case.k_gran, rows)
+    return lat, q, s, out
+
+
+def kv_destinations(case) -> np.ndarray:
+    """int64 [T, 2]: element offsets into the pool of each token's K and V rows."""
+    c = case.cache
+    sp, sl, skv, st = c.strides()
+    T = case.T
+    dst = np.empty((T, 2), np.int64)
+    pt = np.ascontiguousarray(c.page_table, np.uint32)
+    cl = np.ascontiguousarray(c.cache_lengths, np.uint32)
+    iro = np.ascontiguousarray(case.input_row_offsets, np.uint32)
+    rc = _load().or_kv_destinations(sp, sl, skv, st, c.num_pages, c.num_layers, c.page_size,
+                                    _ptr(pt), c.max_pages_per_seq, len(iro) - 1, _ptr(cl),
+                                    _ptr(iro), case.layer_idx, _ptr(dst) if T else None)
+    if rc != 0:
+        raise OracleError(f"kv destination precondition failed ({rc})")
+    return dst
+
+
+def kv_matmul(case, rows=None):
+    """(out rows binary64 [len(rows), N], destinations int64 [T, 2])."""
+    out = matmul_nn(case.hidden, case.weight, rows)
+    return out, kv_destinations(case)
