@@ -1,0 +1,263 @@
+"""Benchmark of the paged MLA latent-K path on one MI355X.
+
+A step is one call of mla_decompress_k_paged on the bf16 decode-sized batch
+(64 requests, cached lengths U{256..4096}, page_size 128, rows of 576 = 512
+latent + 64 rope, W_k [16384, 512]): the paged gather, the latent copy and
+the up-projection, all in one kernel.  Inputs are seeded synthetic data
+resident in HBM before timing starts.  The JSON line also carries the other
+rows of the path, each timed the same way:
+  c2_prefill   bf16, 4 x 16384 rows, copies starting mid-cache
+  c3_fp8       fp8 block-scaled form on the same shapes (quantise pass + product)
+  c4_kv_matmul write path, 128 lognormal requests, hidden 4096 -> 2 x 8 x 128
+  p64, p256    1 and 4 newest rows per request of the decode batch (weight-bound)
+
+Timing: HIP events recorded on the stream the library launches on (torch's
+current stream), per launch and around the whole timed region, bracketed by
+torch.cuda.synchronize().  The CPU baseline times the oracle on the host cores
+on a bounded sample of the same workload and is a reported baseline only.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decompressed K rows/sec + TFLOP/s (% MFMA peak) at kv_lora_rank=512, N=16384"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = {
+    "decompress_bf16_kernel": "mla_paged_latent_page_amd/csrc/decompress_bf16.hip",
+    "gemm_fp8_kernel": "mla_paged_latent_page_amd/csrc/decompress_fp8.hip",
+    "kv_matmul_kernel": "mla_paged_latent_page_amd/csrc/kv_matmul.hip",
+}
+
+
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for p in (KERNEL_SOURCES[kernel], "mla_paged_latent_page_amd/csrc/common.hpp"):
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Timed:
+    """Run fn() warmup + steps times on the current stream with HIP events."""
+
+    def __init__(self, torch, fn, steps, warmup):
+        self.torch = torch
+        stream = torch.cuda.current_stream()
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t0.record(stream)
+        for i in range(steps):
+            starts[i].record(stream)
+            fn()
+            ends[i].record(stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        self.wall_s = time.perf_counter() - wall0
+        self.total_ms = t0.elapsed_time(t1)
+        self.launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+        self.avg_launch_ms = float(np.mean(self.launch_ms))
+        self.min_launch_ms = float(np.min(self.launch_ms))
+        self.ms_per_step = self.total_ms / steps
+
+
+def decompress_runner(torch, mp, W, case):
+    dc, t = W.device_decompress(case)
+    M, D, N = case.M, case.D_c, case.N
+    lat = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    cache = mp.PagedKVCache(dc.pool, dc.page_table, dc.cache_lengths)
+    if case.weight_dtype == "e4m3":
+        ws = torch.empty(mp.mla_decompress_k_paged_fp8_workspace_size(M, case.K), dtype=torch.uint8, device="cuda")
+
+        def fn():
+            mp.mla_decompress_k_paged_fp8(t["buffer_row_offsets"], t["cache_offsets"], M, t["weight_q"],
+                                          t["weight_scale"], cache, case.layer_idx, lat, out, ws)
+    else:
+        def fn():
+            mp.mla_decompress_k_paged(t["buffer_row_offsets"], t["cache_offsets"], M, t["weight"], cache,
+                                      case.layer_idx, lat, out)
+    return fn
+
+
+def decompress_costs(case):
+    """(flops, algorithmic HBM bytes) of one call: read each gathered cache row,
+    write it to k_latent, write the k_buffer row, read the weight once."""
+    M, N, K, D = case.M, case.N, case.K, case.D_c
+    flops = 2.0 * M * N * K
+    if case.weight_dtype == "e4m3":
+        w_bytes = N * K + case.weight_scale.nbytes
+        out_b = 2
+    else:
+        w_bytes = N * K * 2
+        out_b = 2
+    return flops, M * (2 * D * 2 + N * out_b) + w_bytes
+
+
+def probe_case(W, base, newest):
+    """The decode batch with only each request's `newest` last cached rows."""
+    lens = base.cache.cache_lengths.astype(np.int64)
+    offs = lens - newest
+    bro = np.zeros(len(lens) + 1, np.uint32)
+    bro[1:] = np.cumsum(np.full(len(lens), newest))
+    return W.DecompressCase(f"p{newest * len(lens)}", base.cache, base.layer_idx, bro, offs.astype(np.uint32),
+                            base.K, base.N, base.weight, base.weight_dtype)
+
+
+def roofline(bound, achieved, peak, unit, traffic):
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+def cpu_baseline(case, n_rows):
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    rng = np.random.default_rng(123)
+    rows = np.sort(rng.choice(case.M, size=min(n_rows, case.M), replace=False))
+    t0 = time.perf_counter()
+    lat = oracle.gather(case)
+    oracle.matmul_nt(lat, case.cache.dtype, case.weight, case.weight_dtype, case.K, rows)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(rows) / dt, 2), "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"full gather of all {case.M} rows + up-projection of {len(rows)} random rows "
+                      f"({dt:.1f} s); rate = sampled rows / time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rows", choices=["all", "main"], default="all",
+                    help="also time the other rows of the path (default) or only the main workload")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="rows in the CPU-baseline sample (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: the path is measured on a single MI355X; "
+              "multi-GPU sharding is a design note, not a measured configuration.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mla_paged_latent_page_amd as mp
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    print(f"[bench] device {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+
+    # ---- main workload: bf16 decode-sized batch
+    case = W.c1_decode()
+    fn = decompress_runner(torch, mp, W, case)
+    tm = Timed(torch, fn, args.steps, args.warmup)
+    flops, alg_bytes = decompress_costs(case)
+    achieved = flops / (tm.avg_launch_ms * 1e-3) / 1e12
+    print(f"[bench] c1_decode M={case.M}: {tm.avg_launch_ms:.3f} ms/launch, {achieved:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
+    rows_per_s = case.M * args.steps / (tm.total_ms * 1e-3)
+    result = {
+        "metric": METRIC, "value": round(rows_per_s, 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(tm.ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "c1_decode: bf16 decode-sized batch, 64 requests with cached lengths "
+                               "U{256..4096} copied from position 0, page_size 128, 576-wide rows "
+                               "(kv_lora_rank 512 + rope 64), W_k [16384, 512]",
+                   "rows": case.M, "N": case.N, "K": case.K, "page_size": 128, "seed": 1},
+        "tflops": round(achieved, 2),
+        "mfma_frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "hbm_gbs_algorithmic": round(alg_bytes / (tm.avg_launch_ms * 1e-3) / 1e9, 1),
+        "roofline": roofline("mfma", achieved, PEAK_BF16_TFLOPS, "TFLOP/s",
+                             traffic_from_profile("decompress_bf16_kernel", "c1_decode")),
+        "kernel": "decompress_bf16_kernel",
+        "launch_ms": {"avg": round(tm.avg_launch_ms, 4), "min": round(tm.min_launch_ms, 4)},
+        "published_baseline": "none: the pages publish no performance numbers",
+    }
+
+    # ---- the other rows of the path
+    if args.rows == "all":
+        rows = {}
+        steps = max(3, args.steps // 2)
+        for probe_n in (1, 4):
+            pc = probe_case(W, case, probe_n)
+            t = Timed(torch, decompress_runner(torch, mp, W, pc), steps * 4, args.warmup)
+            f, b = decompress_costs(pc)
+            gbs = b / (t.avg_launch_ms * 1e-3) / 1e9
+            rows[pc.name] = {"rows": pc.M, "ms": round(t.avg_launch_ms, 4),
+                             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None),
+                             "tflops": round(f / (t.avg_launch_ms * 1e-3) / 1e12, 2)}
+        del fn
+        torch.cuda.empty_cache()
+        for name, make, bound in (("c2_prefill", W.c2_prefill, "mfma"), ("c3_fp8", W.c3_fp8, "hbm")):
+            c = make()
+            t = Timed(torch, decompress_runner(torch, mp, W, c), steps, args.warmup)
+            f, b = decompress_costs(c)
+            tf = f / (t.avg_launch_ms * 1e-3) / 1e12
+            gbs = b / (t.avg_launch_ms * 1e-3) / 1e9
+            entry = {"rows": c.M, "ms": round(t.avg_launch_ms, 4), "rows_per_s": round(c.M / (t.avg_launch_ms * 1e-3), 1),
+                     "tflops": round(tf, 2), "hbm_gbs_algorithmic": round(gbs, 1)}
+            if bound == "mfma":
+                entry["roofline"] = roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                             traffic_from_profile("decompress_bf16_kernel", name))
+            else:
+                entry["roofline"] = roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s",
+                                             traffic_from_profile("gemm_fp8_kernel", name))
+                entry["fp8_mfma_frac"] = round(tf / PEAK_FP8_TFLOPS, 4)
+                entry["note"] = "time per call: quantise pass + fp8 product"
+            rows[name] = entry
+            print(f"[bench] {name}: {t.avg_launch_ms:.3f} ms, {tf:.1f} TFLOP/s, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
+        kc = W.c4_kv_matmul()
+        dc, tt = W.device_kv(kc)
+        cache = mp.PagedKVCache(dc.pool, dc.page_table, dc.cache_lengths)
+
+        def kv_fn():
+            mp.kv_matmul_paged(tt["hidden"], tt["input_row_offsets"], tt["weight"], cache, kc.layer_idx)
+        t = Timed(torch, kv_fn, steps, args.warmup)
+        f = 2.0 * kc.T * kc.hidden_dim * kc.N
+        b = kc.T * (kc.hidden_dim * 2 + kc.N * 2) + kc.weight.nbytes
+        tf = f / (t.avg_launch_ms * 1e-3) / 1e12
+        rows["c4_kv_matmul"] = {"tokens": kc.T, "ms": round(t.avg_launch_ms, 4), "tflops": round(tf, 2),
+                                "hbm_gbs_algorithmic": round(b / (t.avg_launch_ms * 1e-3) / 1e9, 1),
+                                "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                                     traffic_from_profile("kv_matmul_kernel", "c4_kv_matmul"))}
+        print(f"[bench] c4_kv_matmul: {t.avg_launch_ms:.3f} ms, {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        result["rows"] = rows
+
+    if args.cpu_rows > 0:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+/*
+ * mla_paged.h -- C ABI of the MI355X (gfx950) paged MLA latent-K library.
+ *
+ * Three operations, after the MAX kernel API pages:
+ *
+ *   mla_decompress_k_paged      page "generic_flare_mla_decompress_k_cache_ragged_paged"
+ *                               (summary; Args buffer_row_offsets_1d, cache_offsets_1d,
+ *                               buffer_length, weight, kv_collection, layer_idx,
+ *                               k_latent_buffer, k_buffer, context)
+ *   mla_decompress_k_paged_fp8  the same operation with the fp8 block-scaled weight of
+ *                               page "mla_prefill_decode_graph_fp8" (Parameters fp8_dtype,
+ *                               fp8_scale_dtype, m/n/k_scale_granularity; Args w_k, w_k_scale)
+ *   kv_matmul_paged             page "kv_matmul_ragged_paged" (summary; Args hidden_state,
+ *                               input_row_offsets, weight, kv_collection, layer_idx, ctx)
+ *
+ * Conventions for every call:
+ *   - Pointers marked [device] are HIP device pointers; [host] pointers are read
+ *     during the call only.  The caller allocates and frees every buffer and keeps
+ *     it valid until the work queued on `stream` has finished.
+ *   - Matrices are row-major with the innermost dimension contiguous.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue work:
+ *     they never synchronise, never allocate device memory and keep no state
+ *     between calls.  They are safe to call from several host threads.
+ *   - Errors are returned synchronously, before anything is enqueued, in this
+ *     order: host pointers and shapes (MLA_ERR_NULL_POINTER, MLA_ERR_INVALID_SHAPE,
+ *     MLA_ERR_INVALID_DTYPE, MLA_ERR_MISALIGNED, MLA_ERR_OUT_OF_RANGE,
+ *     MLA_ERR_WORKSPACE), then the current device (MLA_ERR_UNSUPPORTED_DEVICE unless
+ *     it is a gfx950), then the launch (MLA_ERR_HIP; mla_last_hip_error() gives the
+ *     hipError_t).  A call with no rows to process returns MLA_OK after the host
+ *     checks and enqueues nothing.
+ *   - Index contents in device memory (offsets, page ids) are the caller's
+ *     contract and are not validated on the host.  Kernels clamp every page id,
+ *     page index and row to the buffers they were given, so a bad index yields
+ *     unspecified values in the rows it affects but never an access outside
+ *     the pool, the weight or the outputs.
+ */
+#ifndef MLA_PAGED_H
+#define MLA_PAGED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_PAGED_ABI_VERSION 1
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_NULL_POINTER = 1,
+    MLA_ERR_INVALID_SHAPE = 2,
+    MLA_ERR_INVALID_DTYPE = 3,
+    MLA_ERR_MISALIGNED = 4,
+    MLA_ERR_OUT_OF_RANGE = 5,
+    MLA_ERR_WORKSPACE = 6,
+    MLA_ERR_UNSUPPORTED_DEVICE = 7,
+    MLA_ERR_HIP = 8
+} mla_status_t;
+
+typedef enum {
+    MLA_DTYPE_F32 = 0,       /* IEEE binary32 */
+    MLA_DTYPE_BF16 = 1,      /* bfloat16 */
+    MLA_DTYPE_F8E4M3FN = 2   /* OCP OFP8 E4M3 (finite, max 448) */
+} mla_dtype_t;
+
+/*
+ * A paged KV cache collection (the `kv_collection` + `layer_idx` of the pages):
+ * one pool holds every layer.  Element (page, layer, kv, slot, i) of the pool is at
+ *   blocks + page*stride_page + layer*stride_layer + kv*stride_kv + slot*stride_token + i
+ * (strides in elements), where i < num_heads*head_dim indexes one token's row.
+ * Token position p of request b lives in physical page page_table[b][p / page_size]
+ * at slot p % page_size.
+ */
+typedef struct {
+    void* blocks;                   /* [device] pool base; 16-byte aligned */
+    int32_t dtype;                  /* mla_dtype_t of the pool: F32 or BF16 */
+    uint32_t num_layers;
+    uint32_t num_pages;
+    uint32_t page_size;             /* tokens per page, >= 1 */
+    uint32_t num_kv;                /* 1 = MLA latent cache, 2 = K then V */
+    uint32_t num_heads;             /* heads per token row */
+    uint32_t head_dim;              /* elements per head */
+    int64_t stride_page;            /* elements */
+    int64_t stride_layer;
+    int64_t stride_kv;
+    int64_t stride_token;           /* token rows are contiguous: row = num_heads*head_dim */
+    const uint32_t* page_table;     /* [device] [batch_size][max_pages_per_seq] page ids */
+    uint32_t batch_size;            /* requests in the batch */
+    uint32_t max_pages_per_seq;
+    const uint32_t* cache_lengths;  /* [device] [batch_size] tokens already cached
+                                       (read by kv_matmul_paged: where appends start;
+                                       may be NULL for the decompress calls) */
+} mla_paged_cache_t;
+
+/* [host] Fill the four strides for a contiguous pool laid out
+ * [page][layer][kv][slot][head][dim].  Returns MLA_ERR_NULL_POINTER or MLA_OK. */
+mla_status_t mla_paged_cache_default_strides(mla_paged_cache_t* cache);
+
+/*
+ * Gather each request's latent rows from the paged cache, then up-project them
+ * (page "generic_flare_mla_decompress_k_cache_ragged_paged", summary and Args;
+ * weight shape from page "mla_prefill_decode_graph_fp8", Args w_k).
+ *
+ *   For request b < cache->batch_size and i < rows_b = buffer_row_offsets[b+1] -
+ *   buffer_row_offsets[b], with r = buffer_row_offsets[b] + i and
+ *   p = cache_offsets[b] + i:
+ *     k_latent_buffer[r][0:D_c] = cache row of token p of request b in layer layer_idx
+ *                                 (a bit copy; D_c = num_heads*head_dim)
+ *     k_buffer[r][n]            = sum_{k<K} k_latent_buffer[r][k] * weight[n][k]
+ *   accumulated in fp32 and rounded to the cache dtype (round to nearest even).
+ *
+ * buffer_row_offsets  [device] uint32 [batch_size+1], [0] = 0, nondecreasing
+ * cache_offsets       [device] uint32 [>= batch_size]; a [batch_size+1] array is accepted
+ *                     (the last entry is not read)
+ * buffer_length       [host] M = buffer_row_offsets[batch_size], the rows to produce;
+ *                     the grid is sized from it, rows >= M are never written
+ * weight              [device] [N][K] in the cache dtype (F32 or BF16), 16-byte aligned
+ * N, K                N = num_heads*qk_nope_head_dim, K = kv_lora_rank; 1 <= K <= D_c.
+ *                     BF16: K % 64 == 0 and N % 64 == 0.  F32: K % 4 == 0 and N % 4 == 0.
+ * cache               [host] num_kv == 1; D_c*elem_size and stride_token*elem_size
+ *                     multiples of 16 bytes
+ * k_latent_buffer     [device] [>= M][D_c] cache dtype, written
+ * k_buffer            [device] [>= M][N] cache dtype, written
+ */
+mla_status_t mla_decompress_k_paged(const uint32_t* buffer_row_offsets,
+                                    const uint32_t* cache_offsets,
+                                    int32_t buffer_length,
+                                    const void* weight, int32_t N, int32_t K,
+                                    const mla_paged_cache_t* cache, uint32_t layer_idx,
+                                    void* k_latent_buffer, void* k_buffer,
+                                    void* stream);
+
+/*
+ * Bytes of device workspace mla_decompress_k_paged_fp8 needs for buffer_length rows
+ * (the activation codes and scales of the on-the-fly quantisation).  0 on bad
+ * arguments.
+ */
+size_t mla_decompress_k_paged_fp8_workspace_size(int32_t buffer_length, int32_t K, int32_t k_gran);
+
+/*
+ * The fp8 block-scaled form of mla_decompress_k_paged (page
+ * "mla_prefill_decode_graph_fp8": Parameters fp8_dtype, fp8_scale_dtype,
+ * m/n/k_scale_granularity; Args w_k, w_k_scale).
+ *
+ *   The gather is as in mla_decompress_k_paged (cache dtype BF16).  Each gathered
+ *   row is quantised per block of k_gran columns (m_gran = 1): amax = max|x|,
+ *   s_a = amax / 448, codes = e4m3fn(x * (448 / amax)) (binary32 quotients, round
+ *   to nearest even; an all-zero block takes s_a = 1).  Then
+ *     k_buffer[r][n] = bf16( sum_kb s_a[r][kb] * weight_scale[n / n_gran][kb]
+ *                                  * sum_{k in block kb} codes[r][k] * weight[n][k] )
+ *   with fp32 accumulation.
+ *
+ * weight_e4m3      [device] [N][K] e4m3fn codes, 16-byte aligned
+ * weight_scale     [device] float [N / n_gran][K / k_gran] multipliers (W ~= s * codes)
+ * m_gran, n_gran, k_gran  granularities along M, N, K; supported: 1, 128, 128
+ * N, K             N % 128 == 0, K % 128 == 0, K <= D_c
+ * workspace        [device] >= mla_decompress_k_paged_fp8_workspace_size(M, K, k_gran)
+ *                  bytes, 256-byte aligned; its contents on return are the activation
+ *                  codes [M][K] followed (at offset align256(M*K)) by the scales
+ *                  float [M][K / k_gran]
+ * other arguments  as in mla_decompress_k_paged; k_latent_buffer and k_buffer are BF16
+ */
+mla_status_t mla_decompress_k_paged_fp8(const uint32_t* buffer_row_offsets,
+                                        const uint32_t* cache_offsets,
+                                        int32_t buffer_length,
+                                        const void* weight_e4m3, const float* weight_scale,
+                                        int32_t N, int32_t K,
+                                        int32_t m_gran, int32_t n_gran, int32_t k_gran,
+                                        const mla_paged_cache_t* cache, uint32_t layer_idx,
+                                        void* k_latent_buffer, void* k_buffer,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/*
+ * Project hidden states and write them into the paged K/V cache (page
+ * "kv_matmul_ragged_paged", summary and Args).
+ *
+ *   out[t][n] = sum_k hidden_state[t][k] * weight[k][n], fp32 accumulation.
+ *   Token t of request b (input_row_offsets[b] <= t < input_row_offsets[b+1]) is
+ *   appended at position p = cache_lengths[b] + (t - input_row_offsets[b]):
+ *     K row of (page_table[b][p / page_size], slot p % page_size) = bf16(out[t][0 : HD])
+ *     V row of the same slot                                        = bf16(out[t][HD : 2HD])
+ *   with HD = num_heads*head_dim.  No other cache element is written, and
+ *   cache_lengths is not updated (that bookkeeping is the cache owner's).
+ *
+ * hidden_state       [device] bf16 [total_tokens][hidden_dim], 16-byte aligned
+ * input_row_offsets  [device] uint32 [batch_size+1], [0] = 0, nondecreasing,
+ *                    [batch_size] = total_tokens
+ * total_tokens       [host] T >= 0
+ * hidden_dim         [host] % 64 == 0
+ * weight             [device] bf16 [hidden_dim][2*HD], 16-byte aligned
+ * cache              [host] BF16, num_kv == 2, HD % 64 == 0, cache_lengths non-NULL;
+ *                    pages are written in place
+ */
+mla_status_t kv_matmul_paged(const void* hidden_state, const uint32_t* input_row_offsets,
+                             int32_t total_tokens, int32_t hidden_dim,
+                             const void* weight,
+                             const mla_paged_cache_t* cache, uint32_t layer_idx,
+                             void* stream);
+
+/* Static text for a status code. */
+const char* mla_status_string(mla_status_t status);
+
+/* hipError_t of the last MLA_ERR_HIP returned on this host thread (0 if none). */
+int32_t mla_last_hip_error(void);
+
+/* MLA_PAGED_ABI_VERSION of the loaded library. */
+int32_t mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_PAGED_H */

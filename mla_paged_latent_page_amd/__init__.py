@@ -1,0 +1,227 @@
+"""Python binding of the gfx950 paged MLA latent-K library (``include/mla_paged.h``).
+
+Argument marshalling only: every step of every operation runs in the HIP
+kernels of ``_build/libmla_paged.so``.  Tensors are torch tensors on the
+current HIP device; the current torch stream is passed as the HIP stream.
+There is no fallback: if the library has not been built, every call raises.
+
+Entry points (same names as the C ABI):
+  mla_decompress_k_paged       gather latent rows from a paged cache, up-project them
+  mla_decompress_k_paged_fp8   the fp8 block-scaled form (1x128 activation, 128x128 weight scales)
+  kv_matmul_paged              project hidden states and write them into K/V cache pages
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import threading
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "libmla_paged.so")
+
+MLA_DTYPE_F32, MLA_DTYPE_BF16, MLA_DTYPE_F8E4M3FN = 0, 1, 2
+STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL_POINTER", 2: "MLA_ERR_INVALID_SHAPE",
+          3: "MLA_ERR_INVALID_DTYPE", 4: "MLA_ERR_MISALIGNED", 5: "MLA_ERR_OUT_OF_RANGE",
+          6: "MLA_ERR_WORKSPACE", 7: "MLA_ERR_UNSUPPORTED_DEVICE", 8: "MLA_ERR_HIP"}
+EXPORTS = ("mla_paged_cache_default_strides", "mla_decompress_k_paged",
+           "mla_decompress_k_paged_fp8_workspace_size", "mla_decompress_k_paged_fp8",
+           "kv_matmul_paged", "mla_status_string", "mla_last_hip_error", "mla_abi_version")
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)}")
+
+
+class CacheDesc(ctypes.Structure):
+    """Mirror of ``mla_paged_cache_t``."""
+    _fields_ = [
+        ("blocks", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+        ("num_layers", ctypes.c_uint32), ("num_pages", ctypes.c_uint32),
+        ("page_size", ctypes.c_uint32), ("num_kv", ctypes.c_uint32),
+        ("num_heads", ctypes.c_uint32), ("head_dim", ctypes.c_uint32),
+        ("stride_page", ctypes.c_int64), ("stride_layer", ctypes.c_int64),
+        ("stride_kv", ctypes.c_int64), ("stride_token", ctypes.c_int64),
+        ("page_table", ctypes.c_void_p), ("batch_size", ctypes.c_uint32),
+        ("max_pages_per_seq", ctypes.c_uint32), ("cache_lengths", ctypes.c_void_p),
+    ]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib():
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"HIP library not built ({LIB_PATH}); run __graft_entry__.build() "
+                                   "or python -m mla_paged_latent_page_amd.build")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+            L.mla_paged_cache_default_strides.argtypes = [ctypes.POINTER(CacheDesc)]
+            L.mla_paged_cache_default_strides.restype = i32
+            L.mla_decompress_k_paged.argtypes = [vp, vp, i32, vp, i32, i32, ctypes.POINTER(CacheDesc), u32,
+                                                 vp, vp, vp]
+            L.mla_decompress_k_paged.restype = i32
+            L.mla_decompress_k_paged_fp8_workspace_size.argtypes = [i32, i32, i32]
+            L.mla_decompress_k_paged_fp8_workspace_size.restype = sz
+            L.mla_decompress_k_paged_fp8.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                                     ctypes.POINTER(CacheDesc), u32, vp, vp, vp, sz, vp]
+            L.mla_decompress_k_paged_fp8.restype = i32
+            L.kv_matmul_paged.argtypes = [vp, vp, i32, i32, vp, ctypes.POINTER(CacheDesc), u32, vp]
+            L.kv_matmul_paged.restype = i32
+            L.mla_status_string.argtypes = [i32]
+            L.mla_status_string.restype = ctypes.c_char_p
+            L.mla_last_hip_error.restype = i32
+            L.mla_abi_version.restype = i32
+            _lib = L
+        return _lib
+
+
+# ---------------------------------------------------------------------------
+# cache descriptor from torch tensors
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class PagedKVCache:
+    """A paged pool as torch tensors.
+
+    pool          [num_pages, num_layers, num_kv, page_size, num_heads, head_dim]
+                  (float32 or bfloat16; may be a strided view with contiguous token rows)
+    page_table    int32/uint32 [batch, max_pages_per_seq] page ids (raw 32-bit values)
+    cache_lengths int32/uint32 [batch] or None
+    """
+    pool: "object"
+    page_table: "object"
+    cache_lengths: Optional["object"] = None
+
+    def descriptor(self) -> CacheDesc:
+        import torch
+        p = self.pool
+        if p.dim() != 6:
+            raise ValueError("pool must be [pages, layers, kv, page_size, heads, head_dim]")
+        if p.stride(5) != 1 or p.stride(4) != p.shape[5]:
+            raise ValueError("token rows of the pool must be contiguous")
+        dt = {torch.float32: MLA_DTYPE_F32, torch.bfloat16: MLA_DTYPE_BF16}.get(p.dtype, -1)
+        d = CacheDesc()
+        d.blocks = p.data_ptr()
+        d.dtype = dt
+        d.num_pages, d.num_layers, d.num_kv, d.page_size, d.num_heads, d.head_dim = p.shape
+        d.stride_page, d.stride_layer, d.stride_kv, d.stride_token = p.stride(0), p.stride(1), p.stride(2), p.stride(3)
+        pt = self.page_table
+        if pt.dim() != 2 or not pt.is_contiguous() or pt.element_size() != 4:
+            raise ValueError("page_table must be a contiguous 32-bit [batch, max_pages] tensor")
+        d.page_table = pt.data_ptr()
+        d.batch_size, d.max_pages_per_seq = pt.shape
+        if self.cache_lengths is not None:
+            cl = self.cache_lengths
+            if not cl.is_contiguous() or cl.element_size() != 4 or cl.numel() != pt.shape[0]:
+                raise ValueError("cache_lengths must be a contiguous 32-bit [batch] tensor")
+            d.cache_lengths = cl.data_ptr()
+        return d
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _u32(t, what):
+    if t.element_size() != 4 or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous 32-bit tensor")
+    return t.data_ptr()
+
+
+def _check_outputs(M, desc, N, k_latent_buffer, k_buffer):
+    D = desc.num_heads * desc.head_dim
+    if k_latent_buffer.numel() < M * D or k_buffer.numel() < M * N:
+        raise ValueError(f"outputs must hold at least [{M}, {D}] and [{M}, {N}] elements")
+    if not (k_latent_buffer.is_contiguous() and k_buffer.is_contiguous()):
+        raise ValueError("outputs must be contiguous")
+
+
+def _check(status, what):
+    if status != 0:
+        if status == 8:
+            raise MlaError(status, f"{what} (hipError {lib().mla_last_hip_error()})")
+        raise MlaError(status, what)
+
+
+# ---------------------------------------------------------------------------
+# operations
+# ---------------------------------------------------------------------------
+def mla_decompress_k_paged(buffer_row_offsets, cache_offsets, buffer_length: int, weight,
+                           cache: PagedKVCache, layer_idx: int, k_latent_buffer, k_buffer,
+                           stream=None) -> None:
+    """k_latent_buffer[r] = paged cache row; k_buffer = k_latent_buffer[:, :K] @ weight.T."""
+    if weight.dim() != 2 or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous [N, K] tensor")
+    N, K = weight.shape
+    desc = cache.descriptor()
+    _check_outputs(buffer_length, desc, N, k_latent_buffer, k_buffer)
+    st = lib().mla_decompress_k_paged(_u32(buffer_row_offsets, "buffer_row_offsets"),
+                                      _u32(cache_offsets, "cache_offsets"), int(buffer_length),
+                                      weight.data_ptr(), N, K, ctypes.byref(desc), int(layer_idx),
+                                      k_latent_buffer.data_ptr(), k_buffer.data_ptr(), _stream(stream))
+    _check(st, "mla_decompress_k_paged")
+
+
+def mla_decompress_k_paged_fp8_workspace_size(buffer_length: int, K: int, k_gran: int = 128) -> int:
+    return int(lib().mla_decompress_k_paged_fp8_workspace_size(int(buffer_length), int(K), int(k_gran)))
+
+
+def mla_decompress_k_paged_fp8(buffer_row_offsets, cache_offsets, buffer_length: int, weight_e4m3,
+                               weight_scale, cache: PagedKVCache, layer_idx: int, k_latent_buffer,
+                               k_buffer, workspace, m_gran: int = 1, n_gran: int = 128,
+                               k_gran: int = 128, stream=None) -> None:
+    """The fp8 block-scaled form; ``workspace`` is a uint8 device tensor of at least
+    mla_decompress_k_paged_fp8_workspace_size(M, K) bytes."""
+    if weight_e4m3.dim() != 2 or not weight_e4m3.is_contiguous():
+        raise ValueError("weight_e4m3 must be a contiguous [N, K] tensor")
+    N, K = weight_e4m3.shape
+    desc = cache.descriptor()
+    _check_outputs(buffer_length, desc, N, k_latent_buffer, k_buffer)
+    if weight_scale.numel() < -(-N // n_gran) * -(-K // k_gran) or weight_scale.element_size() != 4:
+        raise ValueError("weight_scale must hold float32 [N/n_gran, K/k_gran]")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().mla_decompress_k_paged_fp8(_u32(buffer_row_offsets, "buffer_row_offsets"),
+                                          _u32(cache_offsets, "cache_offsets"), int(buffer_length),
+                                          weight_e4m3.data_ptr(), weight_scale.data_ptr(), N, K,
+                                          m_gran, n_gran, k_gran, ctypes.byref(desc), int(layer_idx),
+                                          k_latent_buffer.data_ptr(), k_buffer.data_ptr(),
+                                          workspace.data_ptr() if workspace is not None else None,
+                                          ws_bytes, _stream(stream))
+    _check(st, "mla_decompress_k_paged_fp8")
+
+
+def kv_matmul_paged(hidden_state, input_row_offsets, weight, cache: PagedKVCache, layer_idx: int,
+                    stream=None) -> None:
+    """Append bf16(hidden_state @ weight) as K ([:HD]) and V ([HD:]) rows into the cache pages."""
+    if hidden_state.dim() != 2 or not hidden_state.is_contiguous():
+        raise ValueError("hidden_state must be a contiguous [T, hidden] tensor")
+    T, Kd = hidden_state.shape
+    desc = cache.descriptor()
+    hd = desc.num_heads * desc.head_dim
+    if tuple(weight.shape) != (Kd, 2 * hd) or not weight.is_contiguous():
+        raise ValueError(f"weight must be a contiguous [{Kd}, {2 * hd}] tensor")
+    if input_row_offsets.numel() != desc.batch_size + 1:
+        raise ValueError("input_row_offsets must have batch_size + 1 entries")
+    st = lib().kv_matmul_paged(hidden_state.data_ptr(), _u32(input_row_offsets, "input_row_offsets"),
+                               T, Kd, weight.data_ptr(), ctypes.byref(desc), int(layer_idx),
+                               _stream(stream))
+    _check(st, "kv_matmul_paged")
+
+
+def status_string(status: int) -> str:
+    return lib().mla_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(lib().mla_abi_version())

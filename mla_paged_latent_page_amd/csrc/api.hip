@@ -1,0 +1,296 @@
+// C ABI of the paged MLA latent-K library (include/mla_paged.h): host-side
+// argument validation, device check, and dispatch to one launcher.
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/mla_paged.h"
+#include "launch.hpp"
+
+#define MLA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+mla_status_t hip_failed(hipError_t e)
+{
+    g_last_hip_error = (int32_t)e;
+    return MLA_ERR_HIP;
+}
+
+int elem_bytes(int32_t dtype)
+{
+    switch (dtype) {
+    case MLA_DTYPE_F32: return 4;
+    case MLA_DTYPE_BF16: return 2;
+    case MLA_DTYPE_F8E4M3FN: return 1;
+    default: return 0;
+    }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The current device must be a gfx950; the answer is cached per device.
+mla_status_t check_device()
+{
+    static std::atomic<int> verdict[64];  // 0 unknown, 1 gfx950, 2 other
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return MLA_ERR_UNSUPPORTED_DEVICE;
+    if (dev < 64) {
+        const int v = verdict[dev].load(std::memory_order_relaxed);
+        if (v == 1)
+            return MLA_OK;
+        if (v == 2)
+            return MLA_ERR_UNSUPPORTED_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return MLA_ERR_UNSUPPORTED_DEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64)
+        verdict[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? MLA_OK : MLA_ERR_UNSUPPORTED_DEVICE;
+}
+
+// Checks of the cache descriptor shared by every call.  `row_check` holds
+// the expected num_kv; `work` says whether device pointers must be present.
+mla_status_t check_cache_shape(const mla_paged_cache_t* c, uint32_t num_kv)
+{
+    if (c->num_layers == 0 || c->num_pages == 0 || c->page_size == 0 || c->num_heads == 0 ||
+        c->head_dim == 0 || c->batch_size == 0 || c->max_pages_per_seq == 0 || c->num_kv != num_kv)
+        return MLA_ERR_INVALID_SHAPE;
+    const int64_t row = (int64_t)c->num_heads * c->head_dim;
+    if (c->stride_token < row || c->stride_page <= 0 || c->stride_layer < 0 || c->stride_kv < 0 ||
+        (num_kv > 1 && c->stride_kv < row))
+        return MLA_ERR_INVALID_SHAPE;
+    return MLA_OK;
+}
+
+mla_status_t check_cache_alignment(const mla_paged_cache_t* c)
+{
+    const int eb = elem_bytes(c->dtype);
+    if (!aligned16(c->blocks) || (c->stride_token * eb) % 16 || (c->stride_page * eb) % 16 ||
+        (c->stride_layer * eb) % 16 || (c->stride_kv * eb) % 16 ||
+        ((int64_t)c->num_heads * c->head_dim * eb) % 16)
+        return MLA_ERR_MISALIGNED;
+    return MLA_OK;
+}
+
+mla::PagedLayer layer_view(const mla_paged_cache_t* c, uint32_t layer)
+{
+    const int eb = elem_bytes(c->dtype);
+    mla::PagedLayer L;
+    L.base = static_cast<const char*>(c->blocks) + (int64_t)layer * c->stride_layer * eb;
+    L.page_table = c->page_table;
+    L.stride_page = c->stride_page * eb;
+    L.stride_token = c->stride_token * eb;
+    L.stride_kv = c->stride_kv * eb;
+    L.num_pages = c->num_pages;
+    L.page_size = c->page_size;
+    L.max_pages = c->max_pages_per_seq;
+    L.batch = c->batch_size;
+    return L;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+MLA_API mla_status_t mla_paged_cache_default_strides(mla_paged_cache_t* c)
+{
+    if (!c)
+        return MLA_ERR_NULL_POINTER;
+    c->stride_token = (int64_t)c->num_heads * c->head_dim;
+    c->stride_kv = c->stride_token * c->page_size;
+    c->stride_layer = c->stride_kv * c->num_kv;
+    c->stride_page = c->stride_layer * c->num_layers;
+    return MLA_OK;
+}
+
+MLA_API mla_status_t mla_decompress_k_paged(const uint32_t* buffer_row_offsets,
+                                            const uint32_t* cache_offsets, int32_t buffer_length,
+                                            const void* weight, int32_t N, int32_t K,
+                                            const mla_paged_cache_t* cache, uint32_t layer_idx,
+                                            void* k_latent_buffer, void* k_buffer, void* stream)
+{
+    if (!cache)
+        return MLA_ERR_NULL_POINTER;
+    const bool work = buffer_length > 0;
+    if (work && (!buffer_row_offsets || !cache_offsets || !weight || !k_latent_buffer || !k_buffer ||
+                 !cache->blocks || !cache->page_table))
+        return MLA_ERR_NULL_POINTER;
+    if (buffer_length < 0 || N <= 0 || K <= 0)
+        return MLA_ERR_INVALID_SHAPE;
+    if (mla_status_t st = check_cache_shape(cache, 1))
+        return st;
+    const int64_t D = (int64_t)cache->num_heads * cache->head_dim;
+    if (K > D)
+        return MLA_ERR_INVALID_SHAPE;
+    if (cache->dtype == MLA_DTYPE_BF16) {
+        if (K % 64 || N % 64 || (int64_t)N * K * 2 >= (int64_t(1) << 31))
+            return MLA_ERR_INVALID_SHAPE;
+    } else if (cache->dtype == MLA_DTYPE_F32) {
+        if (K % 4 || N % 4)
+            return MLA_ERR_INVALID_SHAPE;
+    } else {
+        return MLA_ERR_INVALID_DTYPE;
+    }
+    if (!aligned16(weight) || !aligned16(k_latent_buffer) || !aligned16(k_buffer))
+        return MLA_ERR_MISALIGNED;
+    if (mla_status_t st = check_cache_alignment(cache))
+        return st;
+    if (layer_idx >= cache->num_layers)
+        return MLA_ERR_OUT_OF_RANGE;
+    if (!work)
+        return MLA_OK;
+    if (mla_status_t st = check_device())
+        return st;
+
+    mla::DecompressArgs a{};
+    a.bro = buffer_row_offsets;
+    a.co = cache_offsets;
+    a.L = layer_view(cache, layer_idx);
+    a.W = weight;
+    a.lat = k_latent_buffer;
+    a.out = k_buffer;
+    a.M = buffer_length;
+    a.N = N;
+    a.K = K;
+    a.D = (int)D;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = cache->dtype == MLA_DTYPE_BF16 ? mla::launch_decompress_bf16(a, s)
+                                                        : mla::launch_decompress_f32(a, s);
+    return e == hipSuccess ? MLA_OK : hip_failed(e);
+}
+
+MLA_API size_t mla_decompress_k_paged_fp8_workspace_size(int32_t buffer_length, int32_t K, int32_t k_gran)
+{
+    if (buffer_length < 0 || K <= 0 || k_gran != 128 || K % k_gran)
+        return 0;
+    const size_t M = (size_t)buffer_length;
+    return align256(M * (size_t)K) + align256(M * (size_t)(K / k_gran) * sizeof(float));
+}
+
+MLA_API mla_status_t mla_decompress_k_paged_fp8(const uint32_t* buffer_row_offsets,
+                                                const uint32_t* cache_offsets, int32_t buffer_length,
+                                                const void* weight_e4m3, const float* weight_scale,
+                                                int32_t N, int32_t K, int32_t m_gran, int32_t n_gran,
+                                                int32_t k_gran, const mla_paged_cache_t* cache,
+                                                uint32_t layer_idx, void* k_latent_buffer, void* k_buffer,
+                                                void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!cache)
+        return MLA_ERR_NULL_POINTER;
+    const bool work = buffer_length > 0;
+    if (work && (!buffer_row_offsets || !cache_offsets || !weight_e4m3 || !weight_scale ||
+                 !k_latent_buffer || !k_buffer || !workspace || !cache->blocks || !cache->page_table))
+        return MLA_ERR_NULL_POINTER;
+    if (buffer_length < 0 || N <= 0 || K <= 0 || m_gran != 1 || n_gran != 128 || k_gran != 128 ||
+        N % 128 || K % 128 || (int64_t)N * K >= (int64_t(1) << 31))
+        return MLA_ERR_INVALID_SHAPE;
+    if (mla_status_t st = check_cache_shape(cache, 1))
+        return st;
+    const int64_t D = (int64_t)cache->num_heads * cache->head_dim;
+    if (K > D)
+        return MLA_ERR_INVALID_SHAPE;
+    if (cache->dtype != MLA_DTYPE_BF16)
+        return MLA_ERR_INVALID_DTYPE;
+    if (!aligned16(weight_e4m3) || !aligned16(k_latent_buffer) || !aligned16(k_buffer) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) || (reinterpret_cast<uintptr_t>(weight_scale) & 3u))
+        return MLA_ERR_MISALIGNED;
+    if (mla_status_t st = check_cache_alignment(cache))
+        return st;
+    if (layer_idx >= cache->num_layers)
+        return MLA_ERR_OUT_OF_RANGE;
+    const size_t need = mla_decompress_k_paged_fp8_workspace_size(buffer_length, K, k_gran);
+    if (work && workspace_bytes < need)
+        return MLA_ERR_WORKSPACE;
+    if (!work)
+        return MLA_OK;
+    if (mla_status_t st = check_device())
+        return st;
+
+    mla::DecompressArgs a{};
+    a.bro = buffer_row_offsets;
+    a.co = cache_offsets;
+    a.L = layer_view(cache, layer_idx);
+    a.W = weight_e4m3;
+    a.W_scale = weight_scale;
+    a.lat = k_latent_buffer;
+    a.out = k_buffer;
+    a.q = workspace;
+    a.q_scale = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         align256((size_t)buffer_length * (size_t)K));
+    a.M = buffer_length;
+    a.N = N;
+    a.K = K;
+    a.D = (int)D;
+    const hipError_t e = mla::launch_decompress_fp8(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MLA_OK : hip_failed(e);
+}
+
+MLA_API mla_status_t kv_matmul_paged(const void* hidden_state, const uint32_t* input_row_offsets,
+                                     int32_t total_tokens, int32_t hidden_dim, const void* weight,
+                                     const mla_paged_cache_t* cache, uint32_t layer_idx, void* stream)
+{
+    if (!cache)
+        return MLA_ERR_NULL_POINTER;
+    const bool work = total_tokens > 0;
+    if (work && (!hidden_state || !input_row_offsets || !weight || !cache->blocks || !cache->page_table ||
+                 !cache->cache_lengths))
+        return MLA_ERR_NULL_POINTER;
+    if (total_tokens < 0 || hidden_dim <= 0 || hidden_dim % 64)
+        return MLA_ERR_INVALID_SHAPE;
+    if (mla_status_t st = check_cache_shape(cache, 2))
+        return st;
+    const int64_t HD = (int64_t)cache->num_heads * cache->head_dim;
+    if (HD % 64 || (int64_t)hidden_dim * 2 * HD * 2 >= (int64_t(1) << 31))
+        return MLA_ERR_INVALID_SHAPE;
+    if (cache->dtype != MLA_DTYPE_BF16)
+        return MLA_ERR_INVALID_DTYPE;
+    if (!aligned16(hidden_state) || !aligned16(weight))
+        return MLA_ERR_MISALIGNED;
+    if (mla_status_t st = check_cache_alignment(cache))
+        return st;
+    if (layer_idx >= cache->num_layers)
+        return MLA_ERR_OUT_OF_RANGE;
+    if (!work)
+        return MLA_OK;
+    if (mla_status_t st = check_device())
+        return st;
+
+    mla::KvMatmulArgs a{};
+    a.H = static_cast<const uint16_t*>(hidden_state);
+    a.iro = input_row_offsets;
+    a.W = static_cast<const uint16_t*>(weight);
+    a.cache_len = cache->cache_lengths;
+    a.L = layer_view(cache, layer_idx);
+    a.T = total_tokens;
+    a.Kd = hidden_dim;
+    a.N = (int)(2 * HD);
+    a.HD = (int)HD;
+    const hipError_t e = mla::launch_kv_matmul(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MLA_OK : hip_failed(e);
+}
+
+MLA_API const char* mla_status_string(mla_status_t s)
+{
+    switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL_POINTER: return "null pointer";
+    case MLA_ERR_INVALID_SHAPE: return "invalid shape";
+    case MLA_ERR_INVALID_DTYPE: return "invalid dtype";
+    case MLA_ERR_MISALIGNED: return "misaligned pointer or stride";
+    case MLA_ERR_OUT_OF_RANGE: return "index out of range";
+    case MLA_ERR_WORKSPACE: return "workspace too small";
+    case MLA_ERR_UNSUPPORTED_DEVICE: return "current device is not a gfx950";
+    case MLA_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+MLA_API int32_t mla_last_hip_error(void) { return g_last_hip_error; }
+
+MLA_API int32_t mla_abi_version(void) { return MLA_PAGED_ABI_VERSION; }

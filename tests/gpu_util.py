@@ -1,0 +1,104 @@
+"""Helpers for the GPU parity tests: run an operation through the binding on
+seeded inputs, bring results back as raw bits / float64, pick sampled rows."""
+import sys
+
+import numpy as np
+import torch
+
+import mla_paged_latent_page_amd as mp
+import workloads as W
+
+BF16_TOL = 1e-2   # max|gpu - ref| <= BF16_TOL * max|ref|   (bf16 outputs)
+FP8_TOL = 3e-2    # same form, fp8 block-scaled outputs
+POISON_OUT = 0x7FC3  # NaN bf16 pattern pre-filled into outputs to catch stray writes
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_bits(t):
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.cpu().numpy().view(np.uint32)
+    if t.dtype == torch.uint8:
+        return t.cpu().numpy()
+    raise ValueError(t.dtype)
+
+
+def run_decompress(case, extra_rows=0, fp8=None):
+    """Run the HIP op on a case.  Outputs are over-allocated by extra_rows rows
+    pre-filled with a poison pattern.  Returns a dict of device tensors."""
+    fp8 = case.weight_dtype == "e4m3" if fp8 is None else fp8
+    dc, t = W.device_decompress(case)
+    M, D, N = case.M, case.D_c, case.N
+    dt = torch.float32 if case.cache.dtype == "f32" else torch.bfloat16
+    lat = torch.empty((M + extra_rows, D), dtype=dt, device="cuda")
+    out = torch.empty((M + extra_rows, N), dtype=dt, device="cuda")
+    if dt == torch.bfloat16:
+        lat.view(torch.int16).fill_(POISON_OUT)
+        out.view(torch.int16).fill_(POISON_OUT)
+    else:
+        lat.fill_(float("nan"))
+        out.fill_(float("nan"))
+    cache = mp.PagedKVCache(dc.pool, dc.page_table, dc.cache_lengths)
+    say(f"[gpu] {case.name}: M={M} N={N} K={case.K} D={D} fp8={fp8}")
+    res = {"lat": lat, "out": out, "pool": dc.pool}
+    if fp8:
+        ws_bytes = mp.mla_decompress_k_paged_fp8_workspace_size(M, case.K)
+        ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        mp.mla_decompress_k_paged_fp8(t["buffer_row_offsets"], t["cache_offsets"], M, t["weight_q"],
+                                      t["weight_scale"], cache, case.layer_idx, lat, out, ws)
+        res["ws"] = ws
+    else:
+        mp.mla_decompress_k_paged(t["buffer_row_offsets"], t["cache_offsets"], M, t["weight"], cache,
+                                  case.layer_idx, lat, out)
+    torch.cuda.synchronize()
+    return res
+
+
+def workspace_views(ws, M, K):
+    """(codes uint8 [M, K], scales float32 [M, K/128]) inside an fp8 workspace."""
+    a = ws.cpu().numpy()
+    off = (M * K + 255) // 256 * 256
+    q = a[:M * K].reshape(M, K)
+    s = a[off:off + M * (K // 128) * 4].view(np.float32).reshape(M, K // 128)
+    return q, s
+
+
+def rows_as_f64(t, rows):
+    idx = torch.as_tensor(np.asarray(rows, np.int64), device=t.device)
+    return t.index_select(0, idx).double().cpu().numpy()
+
+
+def sample_rows(case, n_random=256, seed=0):
+    """Every request's first and last row, rows at page boundaries (up to 256),
+    and n_random uniform rows."""
+    bro = case.buffer_row_offsets.astype(np.int64)
+    co = case.cache_offsets.astype(np.int64)
+    ps = case.cache.page_size
+    rows = set()
+    boundary = []
+    for b in range(case.batch):
+        lo, hi = bro[b], bro[b + 1]
+        if hi > lo:
+            rows.update([lo, hi - 1])
+            first = (-co[b]) % ps
+            boundary.extend(range(lo + first, hi, ps))
+    rng = np.random.default_rng(seed)
+    if boundary:
+        rows.update(rng.choice(boundary, size=min(256, len(boundary)), replace=False).tolist())
+    if case.M:
+        rows.update(rng.integers(0, case.M, size=min(n_random, case.M)).tolist())
+    return np.array(sorted(rows), np.int64)
+
+
+def check_close(got, ref, tol, what):
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
+    scale = np.abs(ref).max() if ref.size else 0.0
+    err = np.abs(got - ref).max() if ref.size else 0.0
+    say(f"[gpu] {what}: max|err|={err:.3e} max|ref|={scale:.3e} ratio={err / max(scale, 1e-30):.2e} (tol {tol})")
+    assert err <= tol * scale, f"{what}: max|err| {err} > {tol} * {scale}"
+    return err, scale

@@ -1,0 +1,159 @@
+"""The C-ABI library loads, exports every function include/mla_paged.h declares,
+and returns the documented status for every host-side error -- all without a
+GPU (no call here reaches a kernel launch: validation fails first, or the
+device check refuses a machine without a gfx950)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_paged_latent_page_amd as mp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_paged.h")
+
+OK, NULLP, SHAPE, DTYPE, MISAL, RANGE, WS, DEV, HIP = range(9)
+FAKE = 0x100000  # an aligned non-null address; never dereferenced by the host checks
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mp.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return mp.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:mla_status_t|size_t|const char\s*\*|int32_t)\s+(\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(mp.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.mla_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        assert lib.mla_status_string(s)
+    assert b"gfx950" in lib.mla_status_string(DEV)
+
+
+def cache_desc(dtype=1, num_kv=1, heads=1, head_dim=576, page_size=128, layers=2, pages=16, batch=2, maxp=4,
+               with_lengths=False):
+    d = mp.CacheDesc()
+    d.blocks = FAKE
+    d.dtype = dtype
+    d.num_layers, d.num_pages, d.page_size, d.num_kv = layers, pages, page_size, num_kv
+    d.num_heads, d.head_dim = heads, head_dim
+    d.page_table = FAKE
+    d.batch_size, d.max_pages_per_seq = batch, maxp
+    d.cache_lengths = FAKE if with_lengths else None
+    assert mp.lib().mla_paged_cache_default_strides(ctypes.byref(d)) == OK
+    return d
+
+
+def decompress(lib, d, M=100, N=512, K=512, layer=1, **ptrs):
+    p = dict(bro=FAKE, co=FAKE, w=FAKE, lat=FAKE, out=FAKE)
+    p.update(ptrs)
+    return lib.mla_decompress_k_paged(p["bro"], p["co"], M, p["w"], N, K,
+                                      ctypes.byref(d) if d is not None else None, layer, p["lat"], p["out"], None)
+
+
+def test_default_strides(lib):
+    d = cache_desc(num_kv=2, heads=8, head_dim=128, page_size=16, layers=3)
+    assert (d.stride_token, d.stride_kv, d.stride_layer, d.stride_page) == (1024, 16 * 1024, 2 * 16 * 1024,
+                                                                           3 * 2 * 16 * 1024)
+    assert lib.mla_paged_cache_default_strides(None) == NULLP
+
+
+def test_decompress_error_paths(lib):
+    d = cache_desc()
+    assert decompress(lib, None) == NULLP
+    for k in ("bro", "co", "w", "lat", "out"):
+        assert decompress(lib, d, **{k: None}) == NULLP
+    assert decompress(lib, d, M=-1) == SHAPE
+    assert decompress(lib, d, K=1024) == SHAPE          # K > D_c
+    assert decompress(lib, d, K=96) == SHAPE            # bf16 needs K % 64
+    assert decompress(lib, d, N=100) == SHAPE           # bf16 needs N % 64
+    assert decompress(lib, cache_desc(num_kv=2)) == SHAPE
+    assert decompress(lib, cache_desc(page_size=0)) == SHAPE
+    assert decompress(lib, cache_desc(dtype=2)) == DTYPE
+    assert decompress(lib, d, w=FAKE + 8) == MISAL
+    assert decompress(lib, d, out=FAKE + 2) == MISAL
+    assert decompress(lib, cache_desc(head_dim=572)) == MISAL   # bf16 row of 1144 bytes
+    assert decompress(lib, d, layer=2) == RANGE
+    # zero rows: host checks only, nothing enqueued, OK even without pointers
+    assert decompress(lib, d, M=0, bro=None, co=None, w=None, lat=None, out=None) == OK
+    # a valid call on a machine without a gfx950
+    assert decompress(lib, d) == DEV
+    assert decompress(lib, cache_desc(dtype=0, head_dim=80, page_size=16), N=128, K=64) == DEV
+
+
+def fp8(lib, d, M=100, N=512, K=512, grans=(1, 128, 128), ws=None, ws_bytes=None, layer=1, **ptrs):
+    p = dict(bro=FAKE, co=FAKE, w=FAKE, sw=FAKE, lat=FAKE, out=FAKE)
+    p.update(ptrs)
+    need = lib.mla_decompress_k_paged_fp8_workspace_size(max(M, 0), K, 128)
+    return lib.mla_decompress_k_paged_fp8(p["bro"], p["co"], M, p["w"], p["sw"], N, K, *grans,
+                                          ctypes.byref(d), layer, p["lat"], p["out"],
+                                          FAKE if ws is None else ws,
+                                          need if ws_bytes is None else ws_bytes, None)
+
+
+def test_fp8_workspace_size(lib):
+    assert lib.mla_decompress_k_paged_fp8_workspace_size(65536, 512, 128) == 65536 * 512 + 65536 * 4 * 4
+    assert lib.mla_decompress_k_paged_fp8_workspace_size(3, 256, 128) == 768 + 256  # align256(3*256) + align256(3*2*4)
+    assert lib.mla_decompress_k_paged_fp8_workspace_size(3, 256, 64) == 0
+    assert lib.mla_decompress_k_paged_fp8_workspace_size(-1, 256, 128) == 0
+
+
+def test_fp8_error_paths(lib):
+    d = cache_desc()
+    for k in ("bro", "co", "w", "sw", "lat", "out"):
+        assert fp8(lib, d, **{k: None}) == NULLP
+    assert fp8(lib, d, ws=0) == NULLP
+    assert fp8(lib, d, grans=(1, 128, 64)) == SHAPE
+    assert fp8(lib, d, grans=(128, 128, 128)) == SHAPE
+    assert fp8(lib, d, N=320) == SHAPE
+    assert fp8(lib, d, K=640) == SHAPE
+    assert fp8(lib, cache_desc(dtype=0)) == DTYPE
+    assert fp8(lib, d, ws=FAKE + 16) == MISAL
+    assert fp8(lib, d, layer=5) == RANGE
+    assert fp8(lib, d, ws_bytes=1000) == WS
+    assert fp8(lib, d, M=0, ws_bytes=0) == OK
+    assert fp8(lib, d) == DEV
+
+
+def kv(lib, d, T=50, Kd=4096, layer=1, **ptrs):
+    p = dict(h=FAKE, iro=FAKE, w=FAKE)
+    p.update(ptrs)
+    return lib.kv_matmul_paged(p["h"], p["iro"], T, Kd, p["w"], ctypes.byref(d), layer, None)
+
+
+def test_kv_matmul_error_paths(lib):
+    d = cache_desc(num_kv=2, heads=8, head_dim=128, with_lengths=True)
+    for k in ("h", "iro", "w"):
+        assert kv(lib, d, **{k: None}) == NULLP
+    assert kv(lib, cache_desc(num_kv=2, heads=8, head_dim=128)) == NULLP   # no cache_lengths
+    assert kv(lib, d, T=-3) == SHAPE
+    assert kv(lib, d, Kd=100) == SHAPE
+    assert kv(lib, cache_desc(num_kv=1, heads=8, head_dim=128, with_lengths=True)) == SHAPE
+    assert kv(lib, cache_desc(num_kv=2, heads=1, head_dim=96, with_lengths=True)) == SHAPE
+    assert kv(lib, cache_desc(dtype=0, num_kv=2, heads=8, head_dim=128, with_lengths=True)) == DTYPE
+    assert kv(lib, d, h=FAKE + 4) == MISAL
+    assert kv(lib, d, layer=2) == RANGE
+    assert kv(lib, d, T=0) == OK
+    assert kv(lib, d) == DEV
+
+
+def test_binding_refuses_missing_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(mp, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(mp, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        mp.lib()

@@ -1,0 +1,89 @@
+"""GPU parity of mla_decompress_k_paged_fp8 against the CPU oracle.
+
+The activation codes and scales the kernel leaves in its workspace are an
+integer decision taken in binary32 on both sides (amax, 448/amax, x*inv, e4m3
+round-to-nearest-even), so they must match the oracle bit for bit; gathered
+rows bit for bit; k_buffer within 3e-2 * max|ref| of the oracle's block-scaled
+product.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from caselib import elem_f64
+from gpu_util import FP8_TOL, POISON_OUT, check_close, rows_as_f64, run_decompress, sample_rows, say, to_bits, \
+    workspace_views
+
+pytestmark = pytest.mark.gpu
+
+
+def _same_codes(got, ref):
+    # +0/-0 codes (0x00/0x80) are the same value; everything else must match exactly
+    g = np.where(got == 0x80, 0, got)
+    r = np.where(ref == 0x80, 0, ref)
+    return np.array_equal(g, r)
+
+
+def _check(case, rows=None):
+    res = run_decompress(case, extra_rows=5)
+    M, K = case.M, case.K
+    ref_lat = oracle.gather(case)
+    lat_bits = to_bits(res["lat"])
+    assert np.array_equal(lat_bits[:M], ref_lat)
+    assert np.all(lat_bits[M:] == POISON_OUT)
+    q_ref, s_ref = oracle.quantize_e4m3_rows(ref_lat, K, 128)
+    q_got, s_got = workspace_views(res["ws"], M, K)
+    assert np.array_equal(s_got.view(np.uint32), s_ref.view(np.uint32)), "activation scales differ"
+    assert _same_codes(q_got, q_ref), "activation codes differ"
+    ref = oracle.fp8_matmul_nt(q_ref, s_ref, case.weight_q, case.weight_scale, 128, 128, rows)
+    got = res["out"][:M].double().cpu().numpy() if rows is None else rows_as_f64(res["out"], rows)
+    check_close(got, ref, FP8_TOL, f"{case.name} k_buffer fp8")
+    assert np.all(to_bits(res["out"])[M:] == POISON_OUT)
+    return res, ref_lat
+
+
+@pytest.mark.parametrize("seed,ps,N", [(0, 16, 512), (1, 128, 1024), (2, 5, 256)])
+def test_small_fp8_full_compare(seed, ps, N):
+    case = W.small_decompress(seed, batch=5, max_len=400, page_size=ps, K=512, rope=64, N=N, fp8=True)
+    _check(case)
+
+
+def test_fp8_k256_and_zero_rows():
+    case = W.decompress_case("fp8_k256", seed=11, cache_lengths=[100, 9, 250], cache_offsets=[1, 9, 0],
+                             page_size=16, kv_lora_rank=256, rope_dim=64, N=384, fp8=True)
+    # an all-zero latent block must give scale 1 and zero codes
+    c = case.cache
+    pg = c.page_table[2, 0]
+    c.pool[pg, case.layer_idx, 0, 3, 0, 128:256] = 0
+    _check(case)
+
+
+def test_fp8_exactly_representable_blocks_match_unquantised_product():
+    """Latent blocks built from e4m3 values times 2^e with the block max at 448*2^e
+    quantise losslessly, so the fp8 result equals the plain product of the latent
+    with the dequantised weight (to bf16 output rounding)."""
+    rng = np.random.default_rng(12)
+    case = W.small_decompress(12, batch=3, max_len=120, page_size=16, K=256, rope=0, N=256, fp8=True)
+    c = case.cache
+    used = c.page_table[c.page_table != W.PAGE_NONE].astype(np.int64)
+    codes = rng.integers(0, 0x7E, size=(len(used), c.page_size, 256)).astype(np.uint8)
+    vals = elem_f64(codes, "e4m3") * np.where(rng.integers(0, 2, size=codes.shape) == 1, 1.0, -1.0)
+    vals[..., 0] = 448.0
+    vals[..., 128] = -448.0
+    vals[..., :128] *= 2.0 ** -7
+    vals[..., 128:] *= 2.0 ** -3
+    c.pool[used, case.layer_idx, 0, :, 0, :] = W.to_bf16_bits(vals.astype(np.float32))
+    res, ref_lat = _check(case)
+    w_deq = elem_f64(case.weight_q, "e4m3") * np.repeat(np.repeat(case.weight_scale.astype(np.float64), 128, 0), 128, 1)
+    plain = elem_f64(ref_lat, "bf16")[:, :256] @ w_deq.T
+    got = res["out"][:case.M].double().cpu().numpy()
+    check_close(got, plain, 2.0 ** -7, "lossless fp8 vs plain product")
+
+
+@pytest.mark.slow
+def test_c3_fp8_full_size_sampled():
+    case = W.c3_fp8()
+    rows = sample_rows(case)
+    say(f"[gpu] c3: {len(rows)} sampled rows")
+    _check(case, rows)

@@ -1,0 +1,90 @@
+"""GPU parity of kv_matmul_paged against the CPU oracle.
+
+Written K/V rows must be within 1e-2 * max|ref| of the oracle's product at the
+slots the oracle's destinations name; every other element of the pool (other
+layer, other kv half, cached tokens, spare pages, slack slots) must be
+bit-identical to its value before the call.  A selection weight turns the
+product into a copy, so placement is checked bit-exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mla_paged_latent_page_amd as mp
+import oracle
+import workloads as W
+from gpu_util import BF16_TOL, check_close, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_kv(case):
+    dc, t = W.device_kv(case)
+    before = dc.pool.clone()
+    say(f"[gpu] {case.name}: T={case.T} hidden={case.hidden_dim} N={case.N}")
+    mp.kv_matmul_paged(t["hidden"], t["input_row_offsets"], t["weight"],
+                       mp.PagedKVCache(dc.pool, dc.page_table, dc.cache_lengths), case.layer_idx)
+    torch.cuda.synchronize()
+    return before, dc.pool
+
+
+def _written_rows(pool, dst, HD):
+    """[T, 2*HD] of the rows the oracle names, gathered from a device pool."""
+    flat = pool.reshape(-1)
+    idx = torch.as_tensor(dst.reshape(-1), device=pool.device)[:, None] + torch.arange(HD, device=pool.device)[None, :]
+    return flat[idx.reshape(-1)].reshape(dst.shape[0], 2 * HD)
+
+
+def _check(case, rows=None):
+    before, after = run_kv(case)
+    dst = oracle.kv_destinations(case)
+    HD = case.cache.num_heads * case.cache.head_dim
+    got_rows = _written_rows(after, dst, HD)
+    # nothing else changed
+    expect = before.clone().reshape(-1)
+    idx = torch.as_tensor(dst.reshape(-1), device=after.device)[:, None] + torch.arange(HD, device=after.device)[None, :]
+    expect[idx.reshape(-1)] = got_rows.reshape(-1)
+    assert torch.equal(expect.view(torch.int16), after.reshape(-1).view(torch.int16)), "bytes outside the written slots changed"
+    sel = np.arange(case.T) if rows is None else rows
+    ref = oracle.matmul_nn(case.hidden, case.weight, sel)
+    got = got_rows[torch.as_tensor(sel, device=after.device)].double().cpu().numpy()
+    check_close(got, ref, BF16_TOL, f"{case.name} written K/V rows")
+    return got_rows, dst
+
+
+@pytest.mark.parametrize("seed,ps,start", [(0, 16, "random"), (1, 128, "zero"), (2, 3, "random")])
+def test_small_kv_full_compare(seed, ps, start):
+    case = W.small_kv_matmul(seed, batch=6, max_len=300, hidden_dim=256, num_kv_heads=2, head_dim=128,
+                             page_size=ps, start=start)
+    _check(case)
+
+
+def test_selection_weight_places_hidden_columns_exactly():
+    rng = np.random.default_rng(3)
+    Kd, H, D = 512, 2, 128
+    N = 2 * H * D
+    perm = rng.permutation(Kd)[:N]
+    sel = np.zeros((Kd, N), np.float32)
+    sel[perm, np.arange(N)] = 1.0
+    base = W.small_kv_matmul(4, batch=5, max_len=200, hidden_dim=Kd, num_kv_heads=H, head_dim=D, page_size=16)
+    case = W.KvMatmulCase(base.name, base.cache, base.layer_idx, base.hidden, base.input_row_offsets,
+                          W.to_bf16_bits(sel))
+    got_rows, dst = _check(case)
+    bits = got_rows.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(bits, case.hidden[:, perm])
+
+
+@pytest.mark.slow
+def test_c4_full_size_sampled():
+    case = W.c4_kv_matmul()
+    rng = np.random.default_rng(0)
+    iro = case.input_row_offsets.astype(np.int64)
+    rows = set(iro[:-1].tolist()) | set((iro[1:] - 1).tolist()) | set(rng.integers(0, case.T, 512).tolist())
+    _check(case, np.array(sorted(rows), np.int64))
+
+
+@pytest.mark.slow
+def test_c4_with_cached_prefix_sampled():
+    case = W.c4_kv_matmul(start="random")
+    rng = np.random.default_rng(1)
+    _check(case, np.sort(rng.choice(case.T, 400, replace=False)))

@@ -350,3 +350,53 @@ def small_kv_matmul(seed, *, batch=6, max_len=200, hidden_dim=256, num_kv_heads=
     return kv_matmul_case(f"small_kv_s{seed}", seed=seed, seq_lens=lens, start_lengths=starts,
                           hidden_dim=hidden_dim, num_kv_heads=num_kv_heads, head_dim=head_dim,
                           page_size=page_size)
+
+
+# --------------------------------------------------------------------------
+# device copies (torch tensors on the current HIP device)
+# --------------------------------------------------------------------------
+def _bits_to_torch(bits: np.ndarray, device):
+    if bits.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+    if bits.dtype == np.uint32:
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.float32)).to(device)
+    if bits.dtype == np.uint8:
+        return torch.from_numpy(np.ascontiguousarray(bits)).to(device)
+    raise ValueError(bits.dtype)
+
+
+def _u32_to_torch(a: np.ndarray, device):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint32).view(np.int32)).to(device)
+
+
+@dataclasses.dataclass
+class DeviceCache:
+    pool: "torch.Tensor"
+    page_table: "torch.Tensor"
+    cache_lengths: "torch.Tensor"
+
+
+def device_cache(cache: PagedCache, device="cuda") -> DeviceCache:
+    return DeviceCache(_bits_to_torch(cache.pool, device), _u32_to_torch(cache.page_table, device),
+                       _u32_to_torch(cache.cache_lengths, device))
+
+
+def device_decompress(case: DecompressCase, device="cuda"):
+    """(DeviceCache, dict of device tensors) for a decompress case."""
+    dc = device_cache(case.cache, device)
+    t = {"buffer_row_offsets": _u32_to_torch(case.buffer_row_offsets, device),
+         "cache_offsets": _u32_to_torch(case.cache_offsets, device)}
+    if case.weight_dtype == "e4m3":
+        t["weight_q"] = _bits_to_torch(case.weight_q, device)
+        t["weight_scale"] = torch.from_numpy(case.weight_scale).to(device)
+    else:
+        t["weight"] = _bits_to_torch(case.weight, device)
+    return dc, t
+
+
+def device_kv(case: KvMatmulCase, device="cuda"):
+    dc = device_cache(case.cache, device)
+    t = {"hidden": _bits_to_torch(case.hidden, device),
+         "input_row_offsets": _u32_to_torch(case.input_row_offsets, device),
+         "weight": _bits_to_torch(case.weight, device)}
+    return dc, t
