@@ -4,7 +4,7 @@
 #include <cstdlib>
 #include <cstring>
 
-#include "../../include/mla_paged.h"
+#include "mla_paged.h"
 #include "launch.hpp"
 
 #define MLA_API extern "C" __attribute__((visibility("default")))

@@ -57,12 +57,22 @@ __device__ inline int64_t token_offset(const PagedLayer& L, uint32_t b, uint32_t
     return (int64_t)pg * L.stride_page + (int64_t)slot * L.stride_token;
 }
 
-// Round-to-nearest-even float -> bf16 of two values, packed low/high.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even float -> bf16 of two values, packed low/high (one
+// v_cvt_pk_bf16_f32).
 __device__ inline uint32_t pack_bf16x2(float lo, float hi)
 {
-    __bf16 a = static_cast<__bf16>(lo);
-    __bf16 b = static_cast<__bf16>(hi);
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// Wait for this wave's LDS operations, then meet the other waves of the block.
+// Unlike __syncthreads() this carries no memory fence for global memory, so
+// global loads and stores in flight stay in flight.
+__device__ inline void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -83,6 +93,36 @@ __device__ inline void lds_st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p)
 __device__ inline void lds_st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Raw buffer access.  A resource covers [base, base + bytes); a 16-byte access
+// at or past the end reads zeros / writes nothing, which handles ragged tile
+// edges without branches.  Offsets are 32-bit: a per-lane part (VGPR) plus a
+// wave-uniform part (SGPR).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;  // raw 32-bit data format
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset past every resource we build
+
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcFlags);
+}
+__device__ inline u32x4 buf_ld16(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+}
+// 16 bytes per lane straight from memory into LDS: lane l's bytes land at
+// lds + 16 * l (lds is wave-uniform).  No VGPRs are involved.
+__device__ inline void buf_ld16_lds(rsrc_t r, void* lds, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff,
+                                             (int)soff, 0, 0);
+}
+
+// Non-temporal store: output rows are written once and not read back.
+__device__ inline void buf_st16_nt(rsrc_t r, u32x4 v, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, 2);
+}
 
 // Swizzled position of 16-byte granule g in a tile row with `gpr` granules
 // (a power of two): XOR with the row index spreads the rows that one MFMA

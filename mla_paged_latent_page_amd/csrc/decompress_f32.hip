@@ -3,27 +3,12 @@
 // element type of weight, k_latent_buffer and k_buffer alike).
 //
 // fp32 has no dense MFMA advantage worth a tiled kernel at the small sizes this
-// type is used for, so the path is two plain kernels: a row gather (one 16-byte
-// granule per thread, the request found by binary search over the ragged offsets)
-// and an LDS-tiled FMA product reading the gathered rows.
+// type is used for, so the path is two plain kernels: the paged row gather of
+// gather.hip and an LDS-tiled FMA product reading the gathered rows.
 #include "launch.hpp"
 
 namespace mla {
 namespace {
-
-__global__ void __launch_bounds__(256) gather_rows_kernel(DecompressArgs a, int granules_per_row)
-{
-    const int64_t total = (int64_t)a.M * granules_per_row;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * blockDim.x) {
-        const int r = (int)(idx / granules_per_row);
-        const int g = (int)(idx - (int64_t)r * granules_per_row);
-        const uint32_t b = find_request(a.bro, a.L.batch, (uint32_t)r);
-        const uint32_t p = a.co[b] + ((uint32_t)r - a.bro[b]);
-        const int64_t off = token_offset(a.L, b, p);
-        st16(static_cast<char*>(a.lat) + idx * 16, ld16(a.L.base + off + (int64_t)g * 16));
-    }
-}
 
 // out[m][n] = sum_k lat[m][k] * W[n][k]; 16x16 threads, each one output, 16-wide k tiles.
 __global__ void __launch_bounds__(256) matmul_f32_kernel(DecompressArgs a, int tiles_n)
@@ -56,12 +41,7 @@ __global__ void __launch_bounds__(256) matmul_f32_kernel(DecompressArgs a, int t
 
 hipError_t launch_decompress_f32(const DecompressArgs& a, hipStream_t s)
 {
-    const int gpr = a.D * 4 / 16;
-    const int64_t total = (int64_t)a.M * gpr;
-    const int64_t blocks = (total + 255) / 256;
-    const int grid = (int)(blocks < 65536 ? blocks : 65536);
-    hipLaunchKernelGGL(gather_rows_kernel, dim3(grid), dim3(256), 0, s, a, gpr);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_gather_rows(a, 4, s);
     if (e != hipSuccess)
         return e;
     const int tiles_n = (a.N + 15) / 16, tiles_m = (a.M + 15) / 16;

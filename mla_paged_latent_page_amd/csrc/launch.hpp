@@ -32,6 +32,8 @@ struct KvMatmulArgs {
     int T, Kd, N, HD;          // N = 2*HD
 };
 
+hipError_t launch_gather_rows(const DecompressArgs& a, int elem_bytes, hipStream_t s);
+hipError_t launch_product_bf16(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_decompress_bf16(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_decompress_f32(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_decompress_fp8(const DecompressArgs& a, hipStream_t s);
