@@ -1,0 +1,132 @@
+// Pieces shared by the two persistent bf16 product kernels (decompress_bf16.hip,
+// decompress_bf16_ring.hip): problem description, the per-block tile list with
+// its XCD-aware order, the accumulator drain used by the epilogues, barrier
+// helpers and the launch geometry.
+#pragma once
+
+#include "launch.hpp"
+
+namespace mla {
+
+struct GemmParams {
+    const uint16_t* A;   // [M][lda] bf16 (gathered rows)
+    const uint16_t* W;   // [N][K] bf16
+    uint16_t* C;         // [M][N] bf16
+    int lda;
+    int M, N, K;
+    int tiles_m, tiles_n;
+    int xcd_map;
+};
+
+// The tiles of one persistent block, in the order it processes them.
+// Blocks are dispatched to the 8 XCDs round-robin (block b runs on XCD b % 8).
+// With the XCD map, XCD x owns N-tiles [x*G, (x+1)*G) and walks the M-tiles:
+// its 1/8 of W stays in its own L2 while the activation rows stream past, and
+// the N-tiles of one M-tile, running side by side, share those rows in L2.
+struct TileList {
+    int first, step, count, Gn, x, tiles_n;
+    bool xcd;
+    __device__ void coords(int i, int& tm, int& tn) const
+    {
+        const int u = first + i * step;
+        if (xcd) {
+            tm = u / Gn;
+            tn = x * Gn + (u - tm * Gn);
+        } else {
+            tm = u / tiles_n;
+            tn = u - tm * tiles_n;
+        }
+    }
+};
+
+__device__ inline TileList make_tiles(const GemmParams& P)
+{
+    TileList L;
+    L.tiles_n = P.tiles_n;
+    L.xcd = P.xcd_map != 0;
+    int total;
+    if (L.xcd) {
+        L.x = blockIdx.x & 7;
+        L.first = blockIdx.x >> 3;
+        L.step = gridDim.x >> 3;
+        L.Gn = P.tiles_n >> 3;
+        total = P.tiles_m * L.Gn;
+    } else {
+        L.x = 0;
+        L.Gn = 1;
+        L.first = blockIdx.x;
+        L.step = gridDim.x;
+        total = P.tiles_m * P.tiles_n;
+    }
+    L.count = L.first < total ? (total - L.first + L.step - 1) / L.step : 0;
+    return L;
+}
+
+// Order this wave's LDS writes before its later LDS reads (a wave's LDS
+// operations are performed in order; this only stops compiler reordering).
+__device__ inline void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Read accumulator element E of a 32x32 block.  The volatile asm keeps the
+// reads in program order with the LDS writes that consume them, so a tile is
+// drained block by block instead of copying all 256 accumulators out at once.
+template <int E>
+__device__ inline float acc_read(const f32x16& a)
+{
+    float x;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(a[E]));
+    return x;
+}
+
+// Accumulators 4Q..4Q+3 of a block (4 consecutive output columns) as bf16.
+template <int Q>
+__device__ inline u32x2 acc_pack4(const f32x16& a)
+{
+    u32x2 v;
+    v[0] = pack_bf16x2(acc_read<4 * Q + 0>(a), acc_read<4 * Q + 1>(a));
+    v[1] = pack_bf16x2(acc_read<4 * Q + 2>(a), acc_read<4 * Q + 3>(a));
+    return v;
+}
+
+// Wait until at most N of this thread's vector-memory operations are in
+// flight and its LDS operations are done, then meet at the block barrier.
+template <int N>
+__device__ inline void vm_barrier()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Launch geometry: one block per CU; with the XCD map every XCD gets the same
+// number of blocks (surplus blocks find no tile and exit at once).
+inline GemmParams make_gemm_params(const DecompressArgs& a, int BM, int BN, int cus)
+{
+    GemmParams P;
+    P.A = static_cast<const uint16_t*>(a.lat);
+    P.W = static_cast<const uint16_t*>(a.W);
+    P.C = static_cast<uint16_t*>(a.out);
+    P.lda = a.D;
+    P.M = a.M;
+    P.N = a.N;
+    P.K = a.K;
+    P.tiles_m = (a.M + BM - 1) / BM;
+    P.tiles_n = (a.N + BN - 1) / BN;
+    P.xcd_map = (P.tiles_n % 8 == 0 && cus % 8 == 0) ? 1 : 0;
+    return P;
+}
+
+inline int gemm_grid(const GemmParams& P, int cus)
+{
+    const int tiles = P.tiles_m * P.tiles_n;
+    if (P.xcd_map)
+        return cus;
+    return tiles < cus ? tiles : cus;
+}
+
+hipError_t launch_product_bf16_ring(const DecompressArgs& a, int cus, hipStream_t s);
+
+}  // namespace mla

@@ -4,10 +4,13 @@
 // from page "mla_prefill_decode_graph_fp8", Args w_k):
 //   k_buffer[r][n] = sum_{k<K} k_latent[r][k] * W[n][k]   (fp32 accumulate, bf16 RNE out)
 //
-// The call runs the paged gather (gather.hip) into k_latent_buffer, then this
-// persistent product kernel over k_latent_buffer.
+// The call runs the paged gather (gather.hip) into k_latent_buffer, then a
+// persistent product kernel over k_latent_buffer: the LDS-ring kernel of
+// decompress_bf16_ring.hip when K is a multiple of 128, else the register-staged
+// kernel below.
 //
-// Design of the product (one block of 4 waves per CU, persistent over tiles):
+// Design of the register-staged product (one block of 4 waves per CU,
+// persistent over tiles):
 //  * 256 x 256 output tiles, each wave 128 x 128 with its 16 32x32 accumulators
 //    (256 fp32 per lane) held in AGPRs; v_mfma_f32_32x32x16_bf16 with the weight
 //    as the row operand, so a lane's accumulators hold 4 consecutive output
@@ -35,7 +38,7 @@
 //    N-tiles of one M-tile, running side by side, share the A rows in L2.
 #include <type_traits>
 
-#include "launch.hpp"
+#include "bf16_tile_common.hpp"
 
 namespace mla {
 namespace {
@@ -55,87 +58,11 @@ constexpr int LDS_ELEMS = 2 * STAGE + 4 * EPI;
 static_assert(LDS_ELEMS * 2 <= 163840, "LDS budget");
 static_assert(BK == 64, "the stage body is written for four 16-wide k steps");
 
-struct GemmParams {
-    const uint16_t* A;   // [M][lda] bf16 (gathered rows)
-    const uint16_t* W;   // [N][K] bf16
-    uint16_t* C;         // [M][N] bf16
-    int lda;
-    int M, N, K;
-    int tiles_m, tiles_n;
-    int xcd_map;
-};
-
-// The tiles of one persistent block, in the order it processes them.
-struct TileList {
-    int first, step, count, Gn, x, tiles_n;
-    bool xcd;
-    __device__ void coords(int i, int& tm, int& tn) const
-    {
-        const int u = first + i * step;
-        if (xcd) {
-            tm = u / Gn;
-            tn = x * Gn + (u - tm * Gn);
-        } else {
-            tm = u / tiles_n;
-            tn = u - tm * tiles_n;
-        }
-    }
-};
-
-__device__ inline TileList make_tiles(const GemmParams& P)
-{
-    TileList L;
-    L.tiles_n = P.tiles_n;
-    L.xcd = P.xcd_map != 0;
-    int total;
-    if (L.xcd) {
-        L.x = blockIdx.x & 7;
-        L.first = blockIdx.x >> 3;
-        L.step = gridDim.x >> 3;
-        L.Gn = P.tiles_n >> 3;
-        total = P.tiles_m * L.Gn;
-    } else {
-        L.x = 0;
-        L.Gn = 1;
-        L.first = blockIdx.x;
-        L.step = gridDim.x;
-        total = P.tiles_m * P.tiles_n;
-    }
-    L.count = L.first < total ? (total - L.first + L.step - 1) / L.step : 0;
-    return L;
-}
-
-__device__ inline void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Read accumulator element E of a 32x32 block.  The volatile asm keeps the
-// reads in program order with the LDS writes that consume them, so a tile is
-// drained block by block instead of copying all 256 accumulators out at once.
-template <int E>
-__device__ inline float acc_read(const f32x16& a)
-{
-    float x;
-    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(a[E]));
-    return x;
-}
-
-template <int Q>
-__device__ inline u32x2 acc_pack4(const f32x16& a)
-{
-    u32x2 v;
-    v[0] = pack_bf16x2(acc_read<4 * Q + 0>(a), acc_read<4 * Q + 1>(a));
-    v[1] = pack_bf16x2(acc_read<4 * Q + 2>(a), acc_read<4 * Q + 3>(a));
-    return v;
-}
-
 __global__ void __launch_bounds__(NT, 1) gemm_bf16_persistent(GemmParams P)
 {
     __shared__ __attribute__((aligned(16))) uint16_t smem[LDS_ELEMS];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps derived offsets in SGPRs
     const int wm = wave >> 1, wn = wave & 1;
     const int gcol = tid % GPR, rsub = tid / GPR;
 
@@ -301,6 +228,8 @@ __global__ void __launch_bounds__(NT, 1) gemm_bf16_persistent(GemmParams P)
     }
 }
 
+}  // namespace
+
 int num_cus()
 {
     static int n = [] {
@@ -312,27 +241,14 @@ int num_cus()
     return n;
 }
 
-}  // namespace
-
+// K a multiple of 128: the LDS-ring kernel; otherwise the register-staged one.
 hipError_t launch_product_bf16(const DecompressArgs& a, hipStream_t s)
 {
-    GemmParams P;
-    P.A = static_cast<const uint16_t*>(a.lat);
-    P.W = static_cast<const uint16_t*>(a.W);
-    P.C = static_cast<uint16_t*>(a.out);
-    P.lda = a.D;
-    P.M = a.M;
-    P.N = a.N;
-    P.K = a.K;
-    P.tiles_m = (a.M + BM - 1) / BM;
-    P.tiles_n = (a.N + BN - 1) / BN;
     const int cus = num_cus();
-    P.xcd_map = (P.tiles_n % 8 == 0 && cus % 8 == 0) ? 1 : 0;
-    const int tiles = P.tiles_m * P.tiles_n;
-    int grid = tiles < cus ? tiles : cus;
-    if (P.xcd_map)
-        grid = cus;  // every XCD gets the same number of blocks; idle blocks exit at once
-    hipLaunchKernelGGL(gemm_bf16_persistent, dim3(grid), dim3(NT), 0, s, P);
+    if (a.K % 128 == 0)
+        return launch_product_bf16_ring(a, cus, s);
+    GemmParams P = make_gemm_params(a, BM, BN, cus);
+    hipLaunchKernelGGL(gemm_bf16_persistent, dim3(gemm_grid(P, cus)), dim3(NT), 0, s, P);
     return hipGetLastError();
 }
 

@@ -1,0 +1,308 @@
+// LDS-ring variant of the persistent bf16 product (k_buffer = k_latent[:, :K] W^T;
+// page "generic_flare_mla_decompress_k_cache_ragged_paged", summary, and page
+// "mla_prefill_decode_graph_fp8", Args w_k), used when K is a multiple of 128.
+//
+//  * Same 256 x 256 tiles, epilogue, buffer resources and XCD-aware tile order
+//    as the register-staged kernel in decompress_bf16.hip.  Two wave layouts:
+//    4 waves of 128 x 128 (256 accumulators, one wave per SIMD) or 8 waves of
+//    128 x 64 (128 accumulators, two waves per SIMD, so one wave's LDS and
+//    memory stalls are covered by the other's MFMAs).
+//  * K advances in 32-wide stages through a ring of four LDS slots (4 x 32 KB).
+//    Operand tiles go from memory straight into LDS (buffer loads with an LDS
+//    destination, 16 bytes per lane, no VGPR staging), three stages ahead of the
+//    MFMAs, so a load has about three stage times to land; the stream of stages
+//    runs straight across tile boundaries.
+//  * Per stage: read the fragments of k step 1 and issue step 0's 16 MFMAs;
+//    wait for this thread's loads of the next stage and meet at the block
+//    barrier (the next stage is then complete in LDS and the oldest slot is
+//    free); issue the loads three stages ahead into the free slot, read the next
+//    stage's step-0 fragments, and issue step 1's 16 MFMAs over them.
+//  * Each ring slot is a separate LDS array, so the compiler's own waits for the
+//    LDS-bound loads stay exact; the waits before the barrier are explicit.
+//  * Rows of 64 bytes hold four 16-byte granules XOR-swizzled by (row / 4) % 4:
+//    a 1 KB load chunk covers 16 rows, and 16 lanes reading one granule column
+//    of 16 rows hit 16 different bank groups.
+//  * K is a multiple of 128, so every tile spans a whole number of ring turns
+//    and the ring slot of each stage is known at compile time.
+#include <type_traits>
+
+#include "bf16_tile_common.hpp"
+
+namespace mla {
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 32, NBUF = 4;
+constexpr int ROWB = BK * 2;                  // bytes per tile row in a stage
+constexpr int CHUNK_ROWS = 1024 / ROWB;       // rows covered by one 1 KB load chunk
+constexpr int A_BYTES = BM * ROWB, SLOT_BYTES = (BM + BN) * ROWB;
+constexpr int EPI_ROWS = 32;
+
+template <int WAVES_M, int WAVES_N>
+struct RingCfg {
+    static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
+    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;   // wave tile
+    static constexpr int FM = WTM / 32, FN = WTN / 32;
+    static constexpr int CA = BM / CHUNK_ROWS / NW, CB = BN / CHUNK_ROWS / NW;  // load chunks per wave
+    static constexpr int LOADS = CA + CB;     // vector-memory operations per thread per stage
+    static constexpr int EPI = EPI_ROWS * WTN;             // elements of one wave's epilogue strip
+    static constexpr int EG = WTN / 8;                     // 16-byte granules per strip row
+    static constexpr int EPI_PER_LANE = EPI_ROWS * EG / 64;
+    static constexpr int STORES_PER_TILE = FM * EPI_PER_LANE;  // buffer stores per thread per tile
+    static_assert(NBUF * SLOT_BYTES + NW * EPI * 2 <= 163840, "LDS budget");
+    static_assert(CA * NW * CHUNK_ROWS == BM && CB * NW * CHUNK_ROWS == BN, "loader shape");
+    static_assert(LOADS + STORES_PER_TILE <= 63, "vmcnt range");
+};
+
+// Scheduling pattern for one k step of NMF MFMAs: one LDS read after each of
+// the first NDS MFMAs and one memory load after each of the NVM MFMAs that
+// follow them (or alongside them when there are not enough MFMAs).  Spreading
+// the memory instructions over the MFMAs keeps the waves, released together by
+// the barrier, from flooding the LDS and address queues while the matrix pipe
+// idles.
+template <int NMF, int NDS, int NVM>
+__device__ inline void interleave()
+{
+    constexpr bool split = NDS + NVM <= NMF;
+#pragma unroll
+    for (int i = 0; i < NMF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+        if (i < NDS)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        if (split ? (i >= NDS && i < NDS + NVM) : (i < NVM))
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+    }
+}
+
+// Where the loader of the next stages stands.
+struct LoadCursor {
+    int tile, ks;
+    rsrc_t ar, wr;
+};
+
+template <int WAVES_M, int WAVES_N>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_bf16_ring(GemmParams P)
+{
+    using C = RingCfg<WAVES_M, WAVES_N>;
+    constexpr int WTM = C::WTM, WTN = C::WTN, FM = C::FM, FN = C::FN, CA = C::CA, CB = C::CB;
+    constexpr int EPI = C::EPI, EG = C::EG, EPI_PER_LANE = C::EPI_PER_LANE;
+    constexpr int LOADS = C::LOADS, STORES_PER_TILE = C::STORES_PER_TILE;
+    __shared__ __attribute__((aligned(1024))) char slot0[SLOT_BYTES];
+    __shared__ __attribute__((aligned(1024))) char slot1[SLOT_BYTES];
+    __shared__ __attribute__((aligned(1024))) char slot2[SLOT_BYTES];
+    __shared__ __attribute__((aligned(1024))) char slot3[SLOT_BYTES];
+    __shared__ __attribute__((aligned(16))) uint16_t strips[C::NW * EPI];
+    auto slot = [&](auto b) __attribute__((always_inline)) -> char* {
+        constexpr int i = decltype(b)::value;
+        if constexpr (i == 0) return slot0;
+        else if constexpr (i == 1) return slot1;
+        else if constexpr (i == 2) return slot2;
+        else return slot3;
+    };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps derived offsets in SGPRs
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+    const TileList tl = make_tiles(P);
+    const int KT = P.K / BK;
+    if (tl.count == 0)
+        return;
+
+    // Loader lane offsets: in a 1 KB chunk lane l fills row l/4 at granule
+    // position l%4, i.e. logical granule (l%4) ^ ((l/16)%4) of that row.
+    const int lrow = lane >> 2, lgran = (lane & 3) ^ ((lane >> 4) & 3);
+    const uint32_t a_lane = (uint32_t)(lrow * P.lda * 2 + lgran * 16);
+    const uint32_t w_lane = (uint32_t)(lrow * P.K * 2 + lgran * 16);
+    const uint32_t a_chunk = (uint32_t)(CHUNK_ROWS * P.lda * 2), w_chunk = (uint32_t)(CHUNK_ROWS * P.K * 2);
+
+    auto cursor_at = [&](int tile, LoadCursor& c) __attribute__((always_inline)) {
+        int tm, tn;
+        tl.coords(tile, tm, tn);
+        const int mrows = min(P.M - tm * BM, BM), nrows = min(P.N - tn * BN, BN);
+        c.tile = tile;
+        c.ks = 0;
+        c.ar = make_rsrc(P.A + (int64_t)tm * BM * P.lda, (uint32_t)(mrows * P.lda * 2));
+        c.wr = make_rsrc(P.W + (int64_t)tn * BN * P.K, (uint32_t)(nrows * P.K * 2));
+    };
+    // Issue the loads of the cursor's stage into ring slot b and advance the
+    // cursor.  Past the last tile the last stage is loaded again (never read).
+    auto issue = [&](auto b, LoadCursor& c) __attribute__((always_inline)) {
+        char* s = slot(b);
+        const uint32_t kb = c.ks * BK * 2;
+#pragma unroll
+        for (int q = 0; q < CA; ++q) {
+            const int ch = wave * CA + q;
+            buf_ld16_lds(c.ar, s + ch * 1024, a_lane, ch * a_chunk + kb);
+        }
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+            const int ch = wave * CB + q;
+            buf_ld16_lds(c.wr, s + A_BYTES + ch * 1024, w_lane, ch * w_chunk + kb);
+        }
+        ++c.ks;
+    };
+    // Move a cursor that ran off its tile to the next tile (kept out of the
+    // stage's MFMA block so the loads can interleave with the MFMAs).
+    auto settle = [&](LoadCursor& c) __attribute__((always_inline)) {
+        if (c.ks == KT) {
+            if (c.tile + 1 < tl.count)
+                cursor_at(c.tile + 1, c);
+            else
+                c.ks = KT - 1;
+        }
+    };
+
+    f32x16 acc[FN][FM];
+
+    // Fragment byte offsets (lane part) for the two 16-wide k steps of a stage.
+    const int frow = lane & 31;
+    int fr_off[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+        fr_off[kk] = frow * ROWB + ((2 * kk + (lane >> 5)) ^ ((frow >> 2) & 3)) * 16;
+
+    bf16x8 fa0[FN], fb0[FM], fa1[FN], fb1[FM];
+    auto load_frags = [&](auto b, int kk, bf16x8 (&fa)[FN], bf16x8 (&fb)[FM]) {
+        const char* s = slot(b);
+        const char* as = s + wm * WTM * ROWB + fr_off[kk];
+        const char* bs = s + A_BYTES + wn * WTN * ROWB + fr_off[kk];
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+            fa[i] = as_bf16x8(lds_ld16(bs + i * 32 * ROWB));
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+            fb[j] = as_bf16x8(lds_ld16(as + j * 32 * ROWB));
+    };
+    auto mfmas = [&](const bf16x8 (&fa)[FN], const bf16x8 (&fb)[FM], auto first) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                if constexpr (decltype(first)::value)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], f32x16{}, 0, 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            }
+    };
+
+    // Write the finished tile through this wave's strip.
+    auto epilogue = [&](int tile) __attribute__((always_inline)) {
+        int tm, tn;
+        tl.coords(tile, tm, tn);
+        const int mrows = min(P.M - tm * BM, BM);
+        const rsrc_t cr = make_rsrc(P.C + (int64_t)tm * BM * P.N, (uint32_t)(mrows * P.N * 2));
+        uint16_t* E = strips + wave * EPI;
+        const int ncol0 = tn * BN + wn * WTN;
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int row = lane & 31;
+#pragma unroll
+            for (int i = 0; i < FN; ++i) {
+                const int col = i * 32 + 4 * (lane >> 5);
+                uint16_t* e = E + row * WTN + (col & 7);
+                lds_st8(e + swz(row, (col >> 3) + 0, EG) * 8, acc_pack4<0>(acc[i][j]));
+                lds_st8(e + swz(row, (col >> 3) + 1, EG) * 8, acc_pack4<1>(acc[i][j]));
+                lds_st8(e + swz(row, (col >> 3) + 2, EG) * 8, acc_pack4<2>(acc[i][j]));
+                lds_st8(e + swz(row, (col >> 3) + 3, EG) * 8, acc_pack4<3>(acc[i][j]));
+            }
+            wave_lds_sync();
+            u32x4 v[EPI_PER_LANE];
+#pragma unroll
+            for (int p = 0; p < EPI_PER_LANE; ++p) {
+                const int idx = p * 64 + lane;
+                const int r = idx / EG, g = idx % EG;
+                v[p] = lds_ld16(E + r * WTN + swz(r, g, EG) * 8);
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int p = 0; p < EPI_PER_LANE; ++p) {
+                const int idx = p * 64 + lane;
+                const int r = idx / EG, g = idx % EG;
+                const int n = ncol0 + g * 8;
+                const uint32_t off = n < P.N ? (uint32_t)(((wm * WTM + j * 32 + r) * P.N + n) * 2) : kOutOfRange;
+                buf_st16_nt(cr, v[p], off, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using first_t = std::integral_constant<bool, true>;
+    using rest_t = std::integral_constant<bool, false>;
+
+    // Prologue: stages 0..2 in flight, wait for stage 0, read its first fragments.
+    LoadCursor lc;
+    cursor_at(0, lc);
+    issue(I0{}, lc);
+    settle(lc);
+    issue(I1{}, lc);
+    settle(lc);
+    issue(I2{}, lc);
+    settle(lc);
+    vm_barrier<2 * LOADS>();
+    load_frags(I0{}, 0, fa0, fb0);
+
+    // One stage in ring slot B: the next stage sits in slot (B+1)%4 and the
+    // loads issued here go to slot (B+3)%4, the slot of the previous stage.
+    // In the first two stages of a tile after the first, the previous tile's
+    // stores sit in the vector-memory queue behind the awaited loads, and the
+    // wait lets them stay in flight (`relaxed`); otherwise it would wait for
+    // them too.
+    auto stage = [&](auto b, auto first, bool relaxed) __attribute__((always_inline)) {
+        constexpr int B = decltype(b)::value;
+        using Bn = std::integral_constant<int, (B + 1) % NBUF>;
+        using Bp = std::integral_constant<int, (B + 3) % NBUF>;
+        load_frags(b, 1, fa1, fb1);
+        mfmas(fa0, fb0, first);
+        interleave<FN * FM, FN + FM, 0>();
+        __builtin_amdgcn_sched_barrier(0);
+        if (relaxed)
+            vm_barrier<LOADS + STORES_PER_TILE>();
+        else
+            vm_barrier<LOADS>();
+        issue(Bp{}, lc);
+        load_frags(Bn{}, 0, fa0, fb0);
+        mfmas(fa1, fb1, rest_t{});
+        interleave<FN * FM, FN + FM, LOADS>();
+        __builtin_amdgcn_sched_barrier(0);
+        settle(lc);
+    };
+    for (int tile = 0; tile < tl.count; ++tile) {
+        const bool relaxed = tile > 0;
+        stage(I0{}, first_t{}, relaxed);
+        stage(I1{}, rest_t{}, relaxed);
+        stage(I2{}, rest_t{}, false);
+        stage(I3{}, rest_t{}, false);
+        for (int ks = 4; ks < KT; ks += 4) {
+            stage(I0{}, rest_t{}, false);
+            stage(I1{}, rest_t{}, false);
+            stage(I2{}, rest_t{}, false);
+            stage(I3{}, rest_t{}, false);
+        }
+        epilogue(tile);
+    }
+}
+
+}  // namespace
+
+// MLA_PAGED_RING_WAVES=4|8 picks the wave layout (for tuning); the default is
+// the faster one measured on MI355X.
+hipError_t launch_product_bf16_ring(const DecompressArgs& a, int cus, hipStream_t s)
+{
+    static const int waves = [] {
+        const char* e = getenv("MLA_PAGED_RING_WAVES");
+        return e ? atoi(e) : 8;
+    }();
+    GemmParams P = make_gemm_params(a, BM, BN, cus);
+    if (waves == 4)
+        hipLaunchKernelGGL((gemm_bf16_ring<2, 2>), dim3(gemm_grid(P, cus)), dim3(256), 0, s, P);
+    else
+        hipLaunchKernelGGL((gemm_bf16_ring<2, 4>), dim3(gemm_grid(P, cus)), dim3(512), 0, s, P);
+    return hipGetLastError();
+}
+
+}  // namespace mla
