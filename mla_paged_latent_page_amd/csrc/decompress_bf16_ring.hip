@@ -31,7 +31,7 @@
 namespace mla {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32, NBUF = 4;
+constexpr int BM = 256, BN = 256, BK = 64, NBUF = 2;
 constexpr int ROWB = BK * 2;                  // bytes per tile row in a stage
 constexpr int CHUNK_ROWS = 1024 / ROWB;       // rows covered by one 1 KB load chunk
 constexpr int A_BYTES = BM * ROWB, SLOT_BYTES = (BM + BN) * ROWB;
@@ -51,6 +51,7 @@ struct RingCfg {
     static_assert(NBUF * SLOT_BYTES + NW * EPI * 2 <= 163840, "LDS budget");
     static_assert(CA * NW * CHUNK_ROWS == BM && CB * NW * CHUNK_ROWS == BN, "loader shape");
     static_assert(LOADS + STORES_PER_TILE <= 63, "vmcnt range");
+    static_assert(CA % 2 == 0 && CB % 2 == 0, "chunks alternate between the two swizzle phases");
 };
 
 // Scheduling pattern for one k step of NMF MFMAs: one LDS read after each of
@@ -88,15 +89,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_bf16_ring(Gemm
     constexpr int LOADS = C::LOADS, STORES_PER_TILE = C::STORES_PER_TILE;
     __shared__ __attribute__((aligned(1024))) char slot0[SLOT_BYTES];
     __shared__ __attribute__((aligned(1024))) char slot1[SLOT_BYTES];
-    __shared__ __attribute__((aligned(1024))) char slot2[SLOT_BYTES];
-    __shared__ __attribute__((aligned(1024))) char slot3[SLOT_BYTES];
     __shared__ __attribute__((aligned(16))) uint16_t strips[C::NW * EPI];
     auto slot = [&](auto b) __attribute__((always_inline)) -> char* {
         constexpr int i = decltype(b)::value;
         if constexpr (i == 0) return slot0;
-        else if constexpr (i == 1) return slot1;
-        else if constexpr (i == 2) return slot2;
-        else return slot3;
+        else return slot1;
     };
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -108,11 +105,14 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_bf16_ring(Gemm
     if (tl.count == 0)
         return;
 
-    // Loader lane offsets: in a 1 KB chunk lane l fills row l/4 at granule
-    // position l%4, i.e. logical granule (l%4) ^ ((l/16)%4) of that row.
-    const int lrow = lane >> 2, lgran = (lane & 3) ^ ((lane >> 4) & 3);
-    const uint32_t a_lane = (uint32_t)(lrow * P.lda * 2 + lgran * 16);
-    const uint32_t w_lane = (uint32_t)(lrow * P.K * 2 + lgran * 16);
+    // Loader lane offsets: in a 1 KB chunk (8 rows of 128 bytes) lane l fills
+    // row l/8 at granule position l%8, i.e. logical granule (l%8) ^ ((row/2)%8)
+    // of that row.  Chunk c starts at row 8c, so (row/2)%8 has 4 added in odd
+    // chunks: two lane offsets, for even and odd chunks.
+    const int lrow = lane >> 3;
+    const int lg_even = (lane & 7) ^ ((lrow >> 1) & 7), lg_odd = (lane & 7) ^ (((lrow >> 1) + 4) & 7);
+    const uint32_t a_lane[2] = {(uint32_t)(lrow * P.lda * 2 + lg_even * 16), (uint32_t)(lrow * P.lda * 2 + lg_odd * 16)};
+    const uint32_t w_lane[2] = {(uint32_t)(lrow * P.K * 2 + lg_even * 16), (uint32_t)(lrow * P.K * 2 + lg_odd * 16)};
     const uint32_t a_chunk = (uint32_t)(CHUNK_ROWS * P.lda * 2), w_chunk = (uint32_t)(CHUNK_ROWS * P.K * 2);
 
     auto cursor_at = [&](int tile, LoadCursor& c) __attribute__((always_inline)) {
@@ -132,12 +132,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_bf16_ring(Gemm
 #pragma unroll
         for (int q = 0; q < CA; ++q) {
             const int ch = wave * CA + q;
-            buf_ld16_lds(c.ar, s + ch * 1024, a_lane, ch * a_chunk + kb);
+            buf_ld16_lds(c.ar, s + ch * 1024, a_lane[q & 1], ch * a_chunk + kb);
         }
 #pragma unroll
         for (int q = 0; q < CB; ++q) {
             const int ch = wave * CB + q;
-            buf_ld16_lds(c.wr, s + A_BYTES + ch * 1024, w_lane, ch * w_chunk + kb);
+            buf_ld16_lds(c.wr, s + A_BYTES + ch * 1024, w_lane[q & 1], ch * w_chunk + kb);
         }
         ++c.ks;
     };
@@ -154,12 +154,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_bf16_ring(Gemm
 
     f32x16 acc[FN][FM];
 
-    // Fragment byte offsets (lane part) for the two 16-wide k steps of a stage.
+    // Fragment byte offsets (lane part) for the four 16-wide k steps of a stage.
     const int frow = lane & 31;
-    int fr_off[2];
+    int fr_off[4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-        fr_off[kk] = frow * ROWB + ((2 * kk + (lane >> 5)) ^ ((frow >> 2) & 3)) * 16;
+    for (int kk = 0; kk < 4; ++kk)
+        fr_off[kk] = frow * ROWB + ((2 * kk + (lane >> 5)) ^ ((frow >> 1) & 7)) * 16;
 
     bf16x8 fa0[FN], fb0[FM], fa1[FN], fb1[FM];
     auto load_frags = [&](auto b, int kk, bf16x8 (&fa)[FN], bf16x8 (&fb)[FM]) {
@@ -229,59 +229,59 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_bf16_ring(Gemm
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
     using first_t = std::integral_constant<bool, true>;
     using rest_t = std::integral_constant<bool, false>;
 
-    // Prologue: stages 0..2 in flight, wait for stage 0, read its first fragments.
+    // Prologue: stage 0 in flight.
     LoadCursor lc;
     cursor_at(0, lc);
     issue(I0{}, lc);
     settle(lc);
-    issue(I1{}, lc);
-    settle(lc);
-    issue(I2{}, lc);
-    settle(lc);
-    vm_barrier<2 * LOADS>();
-    load_frags(I0{}, 0, fa0, fb0);
 
-    // One stage in ring slot B: the next stage sits in slot (B+1)%4 and the
-    // loads issued here go to slot (B+3)%4, the slot of the previous stage.
-    // In the first two stages of a tile after the first, the previous tile's
-    // stores sit in the vector-memory queue behind the awaited loads, and the
-    // wait lets them stay in flight (`relaxed`); otherwise it would wait for
-    // them too.
-    auto stage = [&](auto b, auto first, bool relaxed) __attribute__((always_inline)) {
+    // One stage in slot B.  At its start this thread's loads of the stage have
+    // landed (after the first stage of a tile other than the first, the
+    // previous tile's stores are still queued behind them and may stay in
+    // flight: `relaxed`); the barrier then makes the stage visible to all waves
+    // and frees the other slot (everyone is done with the previous stage), so
+    // the next stage's loads go there while this one is multiplied.  Fragments
+    // of k step kk+1 are read under step kk's MFMAs.
+    auto stage = [&](auto b, auto first, auto relaxed) __attribute__((always_inline)) {
         constexpr int B = decltype(b)::value;
         using Bn = std::integral_constant<int, (B + 1) % NBUF>;
-        using Bp = std::integral_constant<int, (B + 3) % NBUF>;
+        if constexpr (decltype(relaxed)::value)
+            vm_barrier<STORES_PER_TILE>();
+        else
+            vm_barrier<0>();
+        issue(Bn{}, lc);
+        load_frags(b, 0, fa0, fb0);
         load_frags(b, 1, fa1, fb1);
         mfmas(fa0, fb0, first);
+        interleave<FN * FM, FN + FM, LOADS / 2>();
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(b, 2, fa0, fb0);
+        mfmas(fa1, fb1, rest_t{});
+        interleave<FN * FM, FN + FM, LOADS - LOADS / 2>();
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(b, 3, fa1, fb1);
+        mfmas(fa0, fb0, rest_t{});
         interleave<FN * FM, FN + FM, 0>();
         __builtin_amdgcn_sched_barrier(0);
-        if (relaxed)
-            vm_barrier<LOADS + STORES_PER_TILE>();
-        else
-            vm_barrier<LOADS>();
-        issue(Bp{}, lc);
-        load_frags(Bn{}, 0, fa0, fb0);
         mfmas(fa1, fb1, rest_t{});
-        interleave<FN * FM, FN + FM, LOADS>();
         __builtin_amdgcn_sched_barrier(0);
         settle(lc);
     };
+    using yes_t = std::integral_constant<bool, true>;
+    using no_t = std::integral_constant<bool, false>;
+    // K is a multiple of 128: a tile is an even number of 64-wide stages.
     for (int tile = 0; tile < tl.count; ++tile) {
-        const bool relaxed = tile > 0;
-        stage(I0{}, first_t{}, relaxed);
-        stage(I1{}, rest_t{}, relaxed);
-        stage(I2{}, rest_t{}, false);
-        stage(I3{}, rest_t{}, false);
-        for (int ks = 4; ks < KT; ks += 4) {
-            stage(I0{}, rest_t{}, false);
-            stage(I1{}, rest_t{}, false);
-            stage(I2{}, rest_t{}, false);
-            stage(I3{}, rest_t{}, false);
+        if (tile == 0)
+            stage(I0{}, first_t{}, no_t{});
+        else
+            stage(I0{}, first_t{}, yes_t{});
+        stage(I1{}, rest_t{}, no_t{});
+        for (int ks = 2; ks < KT; ks += 2) {
+            stage(I0{}, rest_t{}, no_t{});
+            stage(I1{}, rest_t{}, no_t{});
         }
         epilogue(tile);
     }
