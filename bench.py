@@ -2,10 +2,16 @@
 
 A step is one call of mla_decompress_k_paged on the bf16 decode-sized batch
 (64 requests, cached lengths U{256..4096}, page_size 128, rows of 576 = 512
-latent + 64 rope, W_k [16384, 512]): the paged gather, the latent copy and
-the up-projection, all in one kernel.  Inputs are seeded synthetic data
-resident in HBM before timing starts.  The JSON line also carries the other
-rows of the path, each timed the same way:
+latent + 64 rope, W_k [16384, 512]): the paged gather into k_latent_buffer and
+the up-projection into k_buffer.  Inputs are seeded synthetic data resident in
+HBM before timing starts.  `value` is rows per second of whole calls.
+
+The roofline object is for the dominant kernel, the bf16 product: its launches
+are timed on their own through mla_latent_matmul (one kernel per call) over the
+rows the gather produced, and `achieved` = 2*M*N*K / average launch time.  The
+gather step is timed the same way through mla_gather_latent_paged.
+
+The JSON line also carries the other rows of the path, each timed the same way:
   c2_prefill   bf16, 4 x 16384 rows, copies starting mid-cache
   c3_fp8       fp8 block-scaled form on the same shapes (quantise pass + product)
   c4_kv_matmul write path, 128 lognormal requests, hidden 4096 -> 2 x 8 x 128
@@ -33,17 +39,20 @@ METRIC = "decompressed K rows/sec + TFLOP/s (% MFMA peak) at kv_lora_rank=512, N
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
+CSRC = "mla_paged_latent_page_amd/csrc/"
 KERNEL_SOURCES = {
-    "decompress_bf16_kernel": "mla_paged_latent_page_amd/csrc/decompress_bf16.hip",
-    "gemm_fp8_kernel": "mla_paged_latent_page_amd/csrc/decompress_fp8.hip",
-    "kv_matmul_kernel": "mla_paged_latent_page_amd/csrc/kv_matmul.hip",
+    "gemm_bf16_ring": ("decompress_bf16_ring.hip", "bf16_tile_common.hpp", "decompress_bf16.hip"),
+    "gather_rows_kernel": ("gather.hip",),
+    "gemm_fp8_kernel": ("decompress_fp8.hip",),
+    "kv_matmul_kernel": ("kv_matmul.hip",),
 }
 
 
 def source_hash(kernel):
+    """Hash of the sources a kernel is built from (its own files + common.hpp)."""
     h = hashlib.sha256()
-    for p in (KERNEL_SOURCES[kernel], "mla_paged_latent_page_amd/csrc/common.hpp"):
-        with open(os.path.join(ROOT, p), "rb") as f:
+    for p in KERNEL_SOURCES[kernel] + ("common.hpp", "launch.hpp"):
+        with open(os.path.join(ROOT, CSRC, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -140,18 +149,29 @@ def roofline(bound, achieved, peak, unit, traffic):
             "frac": round(achieved / peak, 4), "traffic": traffic}
 
 
-def cpu_baseline(case, n_rows):
+def cpu_baseline(case, seconds):
+    """Time the oracle on the host: the gather of every row, then the product of
+    randomly chosen rows in chunks until about `seconds` have been spent on it.
+    rate = rows / (product time + gather time * rows / M)."""
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
     rng = np.random.default_rng(123)
-    rows = np.sort(rng.choice(case.M, size=min(n_rows, case.M), replace=False))
+    order = rng.permutation(case.M)
     t0 = time.perf_counter()
     lat = oracle.gather(case)
-    oracle.matmul_nt(lat, case.cache.dtype, case.weight, case.weight_dtype, case.K, rows)
-    dt = time.perf_counter() - t0
-    return {"value": round(len(rows) / dt, 2), "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "sample": f"full gather of all {case.M} rows + up-projection of {len(rows)} random rows "
-                      f"({dt:.1f} s); rate = sampled rows / time"}
+    t_gather = time.perf_counter() - t0
+    done, chunk, t_mm = 0, 256, 0.0
+    while done < case.M and t_mm < seconds:
+        rows = np.sort(order[done:done + chunk])
+        t1 = time.perf_counter()
+        oracle.matmul_nt(lat, case.cache.dtype, case.weight, case.weight_dtype, case.K, rows)
+        t_mm += time.perf_counter() - t1
+        done += len(rows)
+        chunk = min(chunk * 2, 2048)
+    eff = t_mm + t_gather * done / case.M
+    return {"value": round(done / eff, 2), "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"gather of all {case.M} rows ({t_gather:.1f} s) + up-projection of {done} random rows "
+                      f"({t_mm:.1f} s); rate = rows / (product time + gather time x rows/M)"}
 
 
 def main():
@@ -161,7 +181,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rows", choices=["all", "main"], default="all",
                     help="also time the other rows of the path (default) or only the main workload")
-    ap.add_argument("--cpu-rows", type=int, default=4096, help="rows in the CPU-baseline sample (0: skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="time budget of the CPU-baseline sample (0: skip)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the path is measured on a single MI355X; "
@@ -174,15 +197,36 @@ def main():
 
     torch.cuda.set_device(0)
     print(f"[bench] device {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        t = Timed(torch, lambda: dst.copy_(src), 5, 1)
+        print(json.dumps({"copy_bytes_each_way": src.nbytes, "ms": round(t.avg_launch_ms, 4),
+                          "read_plus_write_gbs": round(2 * src.nbytes / (t.avg_launch_ms * 1e-3) / 1e9, 1)}))
+        return
 
     # ---- main workload: bf16 decode-sized batch
     case = W.c1_decode()
     fn = decompress_runner(torch, mp, W, case)
     tm = Timed(torch, fn, args.steps, args.warmup)
     flops, alg_bytes = decompress_costs(case)
-    achieved = flops / (tm.avg_launch_ms * 1e-3) / 1e12
-    print(f"[bench] c1_decode M={case.M}: {tm.avg_launch_ms:.3f} ms/launch, {achieved:.1f} TFLOP/s",
+    call_tf = flops / (tm.avg_launch_ms * 1e-3) / 1e12
+    print(f"[bench] c1_decode M={case.M}: {tm.avg_launch_ms:.3f} ms/call, {call_tf:.1f} TFLOP/s",
           file=sys.stderr, flush=True)
+
+    # the two steps on their own: gather (HBM copy) and the product (dominant kernel)
+    dc, t = W.device_decompress(case)
+    cache = mp.PagedKVCache(dc.pool, dc.page_table, dc.cache_lengths)
+    lat = torch.empty((case.M, case.D_c), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((case.M, case.N), dtype=torch.bfloat16, device="cuda")
+    tg = Timed(torch, lambda: mp.mla_gather_latent_paged(t["buffer_row_offsets"], t["cache_offsets"], case.M,
+                                                         cache, case.layer_idx, lat), args.steps, args.warmup)
+    tp = Timed(torch, lambda: mp.mla_latent_matmul(lat, case.M, t["weight"], out), args.steps, args.warmup)
+    gather_bytes = case.M * case.D_c * 2 * 2
+    prod_tf = flops / (tp.avg_launch_ms * 1e-3) / 1e12
+    print(f"[bench] gather {tg.avg_launch_ms:.3f} ms ({gather_bytes / tg.avg_launch_ms / 1e6:.0f} GB/s), "
+          f"product {tp.avg_launch_ms:.3f} ms ({prod_tf:.1f} TFLOP/s)", file=sys.stderr, flush=True)
+    del lat, out, dc, t, cache
     rows_per_s = case.M * args.steps / (tm.total_ms * 1e-3)
     result = {
         "metric": METRIC, "value": round(rows_per_s, 1), "unit": "rows/s", "n_gpus": 1,
@@ -193,13 +237,18 @@ def main():
                                "U{256..4096} copied from position 0, page_size 128, 576-wide rows "
                                "(kv_lora_rank 512 + rope 64), W_k [16384, 512]",
                    "rows": case.M, "N": case.N, "K": case.K, "page_size": 128, "seed": 1},
-        "tflops": round(achieved, 2),
-        "mfma_frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "tflops": round(call_tf, 2),
+        "mfma_frac": round(call_tf / PEAK_BF16_TFLOPS, 4),
         "hbm_gbs_algorithmic": round(alg_bytes / (tm.avg_launch_ms * 1e-3) / 1e9, 1),
-        "roofline": roofline("mfma", achieved, PEAK_BF16_TFLOPS, "TFLOP/s",
-                             traffic_from_profile("decompress_bf16_kernel", "c1_decode")),
-        "kernel": "decompress_bf16_kernel",
-        "launch_ms": {"avg": round(tm.avg_launch_ms, 4), "min": round(tm.min_launch_ms, 4)},
+        "roofline": roofline("mfma", prod_tf, PEAK_BF16_TFLOPS, "TFLOP/s",
+                             traffic_from_profile("gemm_bf16_ring", "c1_decode")),
+        "kernel": "gemm_bf16_ring<2,4> (the product step; 2*M*N*K flop per launch)",
+        "launch_ms": {"call_avg": round(tm.avg_launch_ms, 4), "call_min": round(tm.min_launch_ms, 4),
+                      "product_avg": round(tp.avg_launch_ms, 4), "product_min": round(tp.min_launch_ms, 4),
+                      "gather_avg": round(tg.avg_launch_ms, 4), "gather_min": round(tg.min_launch_ms, 4)},
+        "gather": {"kernel": "gather_rows_kernel", "bytes_per_launch": gather_bytes,
+                   "roofline": roofline("hbm", gather_bytes / (tg.avg_launch_ms * 1e-3) / 1e9, PEAK_HBM_GBS,
+                                        "GB/s", traffic_from_profile("gather_rows_kernel", "c1_decode"))},
         "published_baseline": "none: the pages publish no performance numbers",
     }
 
@@ -226,8 +275,8 @@ def main():
             entry = {"rows": c.M, "ms": round(t.avg_launch_ms, 4), "rows_per_s": round(c.M / (t.avg_launch_ms * 1e-3), 1),
                      "tflops": round(tf, 2), "hbm_gbs_algorithmic": round(gbs, 1)}
             if bound == "mfma":
-                entry["roofline"] = roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
-                                             traffic_from_profile("decompress_bf16_kernel", name))
+                entry["roofline"] = roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", None)
+                entry["note"] = "time per call: gather + product"
             else:
                 entry["roofline"] = roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s",
                                              traffic_from_profile("gemm_fp8_kernel", name))
@@ -253,9 +302,9 @@ def main():
         print(f"[bench] c4_kv_matmul: {t.avg_launch_ms:.3f} ms, {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
         result["rows"] = rows
 
-    if args.cpu_rows > 0:
+    if args.cpu_seconds > 0:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(case, args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

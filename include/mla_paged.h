@@ -1,7 +1,8 @@
 /*
  * mla_paged.h -- C ABI of the MI355X (gfx950) paged MLA latent-K library.
  *
- * Three operations, after the MAX kernel API pages:
+ * Three operations, after the MAX kernel API pages (and the two steps of the
+ * first one as calls of their own: mla_gather_latent_paged, mla_latent_matmul):
  *
  *   mla_decompress_k_paged      page "generic_flare_mla_decompress_k_cache_ragged_paged"
  *                               (summary; Args buffer_row_offsets_1d, cache_offsets_1d,
@@ -132,6 +133,41 @@ mla_status_t mla_decompress_k_paged(const uint32_t* buffer_row_offsets,
                                     void* stream);
 
 /*
+ * The first step of mla_decompress_k_paged on its own: the paged gather
+ * (page "generic_flare_mla_decompress_k_cache_ragged_paged", Args
+ * buffer_row_offsets_1d, cache_offsets_1d, k_latent_buffer).
+ *
+ *   k_latent_buffer[r][0:D_c] = cache row of token cache_offsets[b] + i of request b
+ *   (r = buffer_row_offsets[b] + i), a bit copy.
+ *
+ * Arguments as in mla_decompress_k_paged; the cache dtype is F32 or BF16.
+ */
+mla_status_t mla_gather_latent_paged(const uint32_t* buffer_row_offsets,
+                                     const uint32_t* cache_offsets,
+                                     int32_t buffer_length,
+                                     const mla_paged_cache_t* cache, uint32_t layer_idx,
+                                     void* k_latent_buffer, void* stream);
+
+/*
+ * The second step of mla_decompress_k_paged on its own: the up-projection of
+ * rows already gathered (page "generic_flare_mla_decompress_k_cache_ragged_paged",
+ * Args weight, k_buffer; shape from page "mla_prefill_decode_graph_fp8", Args w_k).
+ *
+ *   k_buffer[r][n] = sum_{k<K} k_latent_buffer[r * ld_latent + k] * weight[n][k],
+ *   fp32 accumulation, rounded to `dtype` (round to nearest even).
+ *
+ * k_latent_buffer  [device] [buffer_length][ld_latent] in `dtype`; columns >= K are not read
+ * ld_latent        row stride in elements, K <= ld_latent <= 2^20, ld_latent*elem % 16 == 0
+ * weight           [device] [N][K] in `dtype`
+ * dtype            MLA_DTYPE_BF16 (K % 64 == 0, N % 64 == 0) or MLA_DTYPE_F32 (K, N % 4 == 0)
+ * k_buffer         [device] [>= buffer_length][N] in `dtype`, written
+ * All pointers 16-byte aligned.
+ */
+mla_status_t mla_latent_matmul(const void* k_latent_buffer, int64_t ld_latent, int32_t buffer_length,
+                               const void* weight, int32_t N, int32_t K, int32_t dtype,
+                               void* k_buffer, void* stream);
+
+/*
  * Bytes of device workspace mla_decompress_k_paged_fp8 needs for buffer_length rows
  * (the activation codes and scales of the on-the-fly quantisation).  0 on bad
  * arguments.
@@ -198,6 +234,27 @@ mla_status_t kv_matmul_paged(const void* hidden_state, const uint32_t* input_row
                              const void* weight,
                              const mla_paged_cache_t* cache, uint32_t layer_idx,
                              void* stream);
+
+/*
+ * Debug check of the index arrays of a call (the preconditions the pages leave to
+ * the caller: offsets start at 0 and never decrease, every position a request
+ * touches lies inside its page-table row and maps to a page id < num_pages).
+ * Copies the arrays to the host and synchronises `stream`; meant for debugging,
+ * not for the hot path.
+ *
+ * row_offsets    [device] uint32 [batch_size+1] (buffer_row_offsets or input_row_offsets)
+ * cache_offsets  [device] uint32 [>= batch_size]: positions read start there
+ *                (decompress calls), and when cache->cache_lengths is non-NULL they
+ *                must also end at or before cache_lengths[b].  NULL: positions
+ *                written start at cache_lengths[b] (kv_matmul_paged).
+ * rows           [host] must equal row_offsets[batch_size]
+ * bad_request    [host] optional; receives the first failing request (-1 if none)
+ * Returns MLA_OK, MLA_ERR_INVALID_SHAPE (offsets), MLA_ERR_OUT_OF_RANGE (positions
+ * or page ids), MLA_ERR_NULL_POINTER, MLA_ERR_UNSUPPORTED_DEVICE or MLA_ERR_HIP.
+ */
+mla_status_t mla_check_indices(const uint32_t* row_offsets, const uint32_t* cache_offsets,
+                               int32_t rows, const mla_paged_cache_t* cache, int64_t* bad_request,
+                               void* stream);
 
 /* Static text for a status code. */
 const char* mla_status_string(mla_status_t status);

@@ -9,6 +9,9 @@ Entry points (same names as the C ABI):
   mla_decompress_k_paged       gather latent rows from a paged cache, up-project them
   mla_decompress_k_paged_fp8   the fp8 block-scaled form (1x128 activation, 128x128 weight scales)
   kv_matmul_paged              project hidden states and write them into K/V cache pages
+  mla_gather_latent_paged      the gather step alone
+  mla_latent_matmul            the up-projection step alone (rows already gathered)
+  mla_check_indices            debug validation of index arrays (synchronous)
 """
 from __future__ import annotations
 
@@ -25,9 +28,10 @@ MLA_DTYPE_F32, MLA_DTYPE_BF16, MLA_DTYPE_F8E4M3FN = 0, 1, 2
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL_POINTER", 2: "MLA_ERR_INVALID_SHAPE",
           3: "MLA_ERR_INVALID_DTYPE", 4: "MLA_ERR_MISALIGNED", 5: "MLA_ERR_OUT_OF_RANGE",
           6: "MLA_ERR_WORKSPACE", 7: "MLA_ERR_UNSUPPORTED_DEVICE", 8: "MLA_ERR_HIP"}
-EXPORTS = ("mla_paged_cache_default_strides", "mla_decompress_k_paged",
-           "mla_decompress_k_paged_fp8_workspace_size", "mla_decompress_k_paged_fp8",
-           "kv_matmul_paged", "mla_status_string", "mla_last_hip_error", "mla_abi_version")
+EXPORTS = ("mla_paged_cache_default_strides", "mla_decompress_k_paged", "mla_gather_latent_paged",
+           "mla_latent_matmul", "mla_decompress_k_paged_fp8_workspace_size", "mla_decompress_k_paged_fp8",
+           "kv_matmul_paged", "mla_check_indices", "mla_status_string", "mla_last_hip_error",
+           "mla_abi_version")
 
 
 class MlaError(RuntimeError):
@@ -76,6 +80,13 @@ def lib():
             L.mla_decompress_k_paged_fp8.restype = i32
             L.kv_matmul_paged.argtypes = [vp, vp, i32, i32, vp, ctypes.POINTER(CacheDesc), u32, vp]
             L.kv_matmul_paged.restype = i32
+            L.mla_gather_latent_paged.argtypes = [vp, vp, i32, ctypes.POINTER(CacheDesc), u32, vp, vp]
+            L.mla_gather_latent_paged.restype = i32
+            L.mla_latent_matmul.argtypes = [vp, ctypes.c_int64, i32, vp, i32, i32, i32, vp, vp]
+            L.mla_latent_matmul.restype = i32
+            L.mla_check_indices.argtypes = [vp, vp, i32, ctypes.POINTER(CacheDesc),
+                                            ctypes.POINTER(ctypes.c_int64), vp]
+            L.mla_check_indices.restype = i32
             L.mla_status_string.argtypes = [i32]
             L.mla_status_string.restype = ctypes.c_char_p
             L.mla_last_hip_error.restype = i32
@@ -171,6 +182,52 @@ def mla_decompress_k_paged(buffer_row_offsets, cache_offsets, buffer_length: int
                                       weight.data_ptr(), N, K, ctypes.byref(desc), int(layer_idx),
                                       k_latent_buffer.data_ptr(), k_buffer.data_ptr(), _stream(stream))
     _check(st, "mla_decompress_k_paged")
+
+
+def mla_gather_latent_paged(buffer_row_offsets, cache_offsets, buffer_length: int, cache: PagedKVCache,
+                            layer_idx: int, k_latent_buffer, stream=None) -> None:
+    """k_latent_buffer[r] = paged cache row (the gather step alone)."""
+    desc = cache.descriptor()
+    D = desc.num_heads * desc.head_dim
+    if k_latent_buffer.numel() < buffer_length * D or not k_latent_buffer.is_contiguous():
+        raise ValueError(f"k_latent_buffer must be contiguous and hold at least [{buffer_length}, {D}]")
+    st = lib().mla_gather_latent_paged(_u32(buffer_row_offsets, "buffer_row_offsets"),
+                                       _u32(cache_offsets, "cache_offsets"), int(buffer_length),
+                                       ctypes.byref(desc), int(layer_idx), k_latent_buffer.data_ptr(),
+                                       _stream(stream))
+    _check(st, "mla_gather_latent_paged")
+
+
+def mla_latent_matmul(k_latent_buffer, buffer_length: int, weight, k_buffer, stream=None) -> None:
+    """k_buffer[:M] = k_latent_buffer[:M, :K] @ weight.T (the up-projection step alone).
+    k_latent_buffer is a 2-D tensor with unit column stride (its row stride is passed)."""
+    import torch
+    if weight.dim() != 2 or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous [N, K] tensor")
+    N, K = weight.shape
+    if k_latent_buffer.dim() != 2 or k_latent_buffer.stride(1) != 1 or k_latent_buffer.shape[0] < buffer_length:
+        raise ValueError("k_latent_buffer must be a [>= M, >= K] tensor with unit column stride")
+    if k_latent_buffer.shape[1] < K or k_latent_buffer.dtype != weight.dtype or k_buffer.dtype != weight.dtype:
+        raise ValueError("k_latent_buffer, weight and k_buffer must share a dtype, and K <= latent width")
+    if k_buffer.numel() < buffer_length * N or not k_buffer.is_contiguous():
+        raise ValueError(f"k_buffer must be contiguous and hold at least [{buffer_length}, {N}]")
+    dt = {torch.float32: MLA_DTYPE_F32, torch.bfloat16: MLA_DTYPE_BF16}.get(weight.dtype, -1)
+    st = lib().mla_latent_matmul(k_latent_buffer.data_ptr(), k_latent_buffer.stride(0), int(buffer_length),
+                                 weight.data_ptr(), N, K, dt, k_buffer.data_ptr(), _stream(stream))
+    _check(st, "mla_latent_matmul")
+
+
+def mla_check_indices(row_offsets, cache_offsets, rows: int, cache: PagedKVCache, stream=None):
+    """Debug validation of a call's index arrays (synchronous).  Returns
+    (status, first failing request or -1); never raises on a failed check."""
+    desc = cache.descriptor()
+    bad = ctypes.c_int64(-1)
+    st = lib().mla_check_indices(_u32(row_offsets, "row_offsets"),
+                                 _u32(cache_offsets, "cache_offsets") if cache_offsets is not None else None,
+                                 int(rows), ctypes.byref(desc), ctypes.byref(bad), _stream(stream))
+    if st in (1, 7, 8):
+        _check(st, "mla_check_indices")
+    return st, int(bad.value)
 
 
 def mla_decompress_k_paged_fp8_workspace_size(buffer_length: int, K: int, k_gran: int = 128) -> int:

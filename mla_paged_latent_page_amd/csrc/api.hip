@@ -3,6 +3,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <vector>
 
 #include "mla_paged.h"
 #include "launch.hpp"
@@ -165,6 +166,85 @@ MLA_API mla_status_t mla_decompress_k_paged(const uint32_t* buffer_row_offsets,
     return e == hipSuccess ? MLA_OK : hip_failed(e);
 }
 
+MLA_API mla_status_t mla_gather_latent_paged(const uint32_t* buffer_row_offsets,
+                                             const uint32_t* cache_offsets, int32_t buffer_length,
+                                             const mla_paged_cache_t* cache, uint32_t layer_idx,
+                                             void* k_latent_buffer, void* stream)
+{
+    if (!cache)
+        return MLA_ERR_NULL_POINTER;
+    const bool work = buffer_length > 0;
+    if (work && (!buffer_row_offsets || !cache_offsets || !k_latent_buffer || !cache->blocks ||
+                 !cache->page_table))
+        return MLA_ERR_NULL_POINTER;
+    if (buffer_length < 0)
+        return MLA_ERR_INVALID_SHAPE;
+    if (mla_status_t st = check_cache_shape(cache, 1))
+        return st;
+    const int eb = elem_bytes(cache->dtype);
+    if (cache->dtype != MLA_DTYPE_BF16 && cache->dtype != MLA_DTYPE_F32)
+        return MLA_ERR_INVALID_DTYPE;
+    if (!aligned16(k_latent_buffer))
+        return MLA_ERR_MISALIGNED;
+    if (mla_status_t st = check_cache_alignment(cache))
+        return st;
+    if (layer_idx >= cache->num_layers)
+        return MLA_ERR_OUT_OF_RANGE;
+    if (!work)
+        return MLA_OK;
+    if (mla_status_t st = check_device())
+        return st;
+
+    mla::DecompressArgs a{};
+    a.bro = buffer_row_offsets;
+    a.co = cache_offsets;
+    a.L = layer_view(cache, layer_idx);
+    a.lat = k_latent_buffer;
+    a.M = buffer_length;
+    a.D = (int)((int64_t)cache->num_heads * cache->head_dim);
+    const hipError_t e = mla::launch_gather_rows(a, eb, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MLA_OK : hip_failed(e);
+}
+
+MLA_API mla_status_t mla_latent_matmul(const void* k_latent_buffer, int64_t ld_latent, int32_t buffer_length,
+                                       const void* weight, int32_t N, int32_t K, int32_t dtype,
+                                       void* k_buffer, void* stream)
+{
+    const bool work = buffer_length > 0;
+    if (work && (!k_latent_buffer || !weight || !k_buffer))
+        return MLA_ERR_NULL_POINTER;
+    if (buffer_length < 0 || N <= 0 || K <= 0 || ld_latent < K || ld_latent > (int64_t(1) << 20))
+        return MLA_ERR_INVALID_SHAPE;
+    const int eb = elem_bytes(dtype);
+    if (dtype == MLA_DTYPE_BF16) {
+        if (K % 64 || N % 64 || (int64_t)N * K * 2 >= (int64_t(1) << 31))
+            return MLA_ERR_INVALID_SHAPE;
+    } else if (dtype == MLA_DTYPE_F32) {
+        if (K % 4 || N % 4)
+            return MLA_ERR_INVALID_SHAPE;
+    } else {
+        return MLA_ERR_INVALID_DTYPE;
+    }
+    if (!aligned16(weight) || !aligned16(k_latent_buffer) || !aligned16(k_buffer) || (ld_latent * eb) % 16)
+        return MLA_ERR_MISALIGNED;
+    if (!work)
+        return MLA_OK;
+    if (mla_status_t st = check_device())
+        return st;
+
+    mla::DecompressArgs a{};
+    a.W = weight;
+    a.lat = const_cast<void*>(k_latent_buffer);
+    a.out = k_buffer;
+    a.M = buffer_length;
+    a.N = N;
+    a.K = K;
+    a.D = (int)ld_latent;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = dtype == MLA_DTYPE_BF16 ? mla::launch_product_bf16(a, s) : mla::launch_product_f32(a, s);
+    return e == hipSuccess ? MLA_OK : hip_failed(e);
+}
+
 MLA_API size_t mla_decompress_k_paged_fp8_workspace_size(int32_t buffer_length, int32_t K, int32_t k_gran)
 {
     if (buffer_length < 0 || K <= 0 || k_gran != 128 || K % k_gran)
@@ -273,6 +353,67 @@ MLA_API mla_status_t kv_matmul_paged(const void* hidden_state, const uint32_t* i
     a.HD = (int)HD;
     const hipError_t e = mla::launch_kv_matmul(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MLA_OK : hip_failed(e);
+}
+
+MLA_API mla_status_t mla_check_indices(const uint32_t* row_offsets, const uint32_t* cache_offsets,
+                                       int32_t rows, const mla_paged_cache_t* cache, int64_t* bad_request,
+                                       void* stream)
+{
+    if (bad_request)
+        *bad_request = -1;
+    if (!cache || !row_offsets || !cache->page_table)
+        return MLA_ERR_NULL_POINTER;
+    if (!cache_offsets && !cache->cache_lengths)
+        return MLA_ERR_NULL_POINTER;
+    if (rows < 0 || cache->batch_size == 0 || cache->max_pages_per_seq == 0 || cache->page_size == 0 ||
+        cache->num_pages == 0)
+        return MLA_ERR_INVALID_SHAPE;
+    if (mla_status_t st = check_device())
+        return st;
+    const size_t B = cache->batch_size, P = cache->max_pages_per_seq;
+    std::vector<uint32_t> off(B + 1), co(cache_offsets ? B : 0), len(cache->cache_lengths ? B : 0), pt(B * P);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(off.data(), row_offsets, off.size() * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess && cache_offsets)
+        e = hipMemcpyAsync(co.data(), cache_offsets, co.size() * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess && cache->cache_lengths)
+        e = hipMemcpyAsync(len.data(), cache->cache_lengths, len.size() * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(pt.data(), cache->page_table, pt.size() * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(s);
+    if (e != hipSuccess)
+        return hip_failed(e);
+
+    auto fail = [&](int64_t b, mla_status_t st) {
+        if (bad_request)
+            *bad_request = b;
+        return st;
+    };
+    if (off[0] != 0)
+        return fail(0, MLA_ERR_INVALID_SHAPE);
+    for (size_t b = 0; b < B; ++b)
+        if (off[b + 1] < off[b])
+            return fail((int64_t)b, MLA_ERR_INVALID_SHAPE);
+    if (off[B] != (uint32_t)rows)
+        return fail((int64_t)B, MLA_ERR_INVALID_SHAPE);
+    for (size_t b = 0; b < B; ++b) {
+        const uint64_t n = off[b + 1] - off[b];
+        if (n == 0)
+            continue;
+        // Positions [first, first + n) of request b are read (cache_offsets given)
+        // or written (appended after cache_lengths).
+        const uint64_t first = cache_offsets ? co[b] : len[b];
+        const uint64_t end = first + n;
+        if (cache_offsets && cache->cache_lengths && end > len[b])
+            return fail((int64_t)b, MLA_ERR_OUT_OF_RANGE);
+        if (end > (uint64_t)P * cache->page_size)
+            return fail((int64_t)b, MLA_ERR_OUT_OF_RANGE);
+        for (uint64_t lp = first / cache->page_size; lp <= (end - 1) / cache->page_size; ++lp)
+            if (pt[b * P + lp] >= cache->num_pages)
+                return fail((int64_t)b, MLA_ERR_OUT_OF_RANGE);
+    }
+    return MLA_OK;
 }
 
 MLA_API const char* mla_status_string(mla_status_t s)

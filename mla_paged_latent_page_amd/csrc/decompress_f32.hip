@@ -39,14 +39,19 @@ __global__ void __launch_bounds__(256) matmul_f32_kernel(DecompressArgs a, int t
 
 }  // namespace
 
+hipError_t launch_product_f32(const DecompressArgs& a, hipStream_t s)
+{
+    const int tiles_n = (a.N + 15) / 16, tiles_m = (a.M + 15) / 16;
+    hipLaunchKernelGGL(matmul_f32_kernel, dim3(tiles_n * tiles_m), dim3(256), 0, s, a, tiles_n);
+    return hipGetLastError();
+}
+
 hipError_t launch_decompress_f32(const DecompressArgs& a, hipStream_t s)
 {
     hipError_t e = launch_gather_rows(a, 4, s);
     if (e != hipSuccess)
         return e;
-    const int tiles_n = (a.N + 15) / 16, tiles_m = (a.M + 15) / 16;
-    hipLaunchKernelGGL(matmul_f32_kernel, dim3(tiles_n * tiles_m), dim3(256), 0, s, a, tiles_n);
-    return hipGetLastError();
+    return launch_product_f32(a, s);
 }
 
 }  // namespace mla

@@ -20,7 +20,7 @@ struct DecompressArgs {
     void* out;             // k_buffer [M][N]
     void* q;               // fp8 only: activation codes [M][K]
     float* q_scale;        // fp8 only: activation scales [M][K/128]
-    int M, N, K, D;        // D = elements per cache token row
+    int M, N, K, D;        // D = elements per cache token row = row stride of lat
 };
 
 struct KvMatmulArgs {
@@ -34,6 +34,7 @@ struct KvMatmulArgs {
 
 hipError_t launch_gather_rows(const DecompressArgs& a, int elem_bytes, hipStream_t s);
 hipError_t launch_product_bf16(const DecompressArgs& a, hipStream_t s);
+hipError_t launch_product_f32(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_decompress_bf16(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_decompress_f32(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_decompress_fp8(const DecompressArgs& a, hipStream_t s);

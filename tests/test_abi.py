@@ -152,6 +152,58 @@ def test_kv_matmul_error_paths(lib):
     assert kv(lib, d) == DEV
 
 
+def test_gather_error_paths(lib):
+    d = cache_desc()
+
+    def gather(dd, M=100, layer=1, **ptrs):
+        p = dict(bro=FAKE, co=FAKE, lat=FAKE)
+        p.update(ptrs)
+        return lib.mla_gather_latent_paged(p["bro"], p["co"], M, ctypes.byref(dd) if dd is not None else None,
+                                           layer, p["lat"], None)
+    assert gather(None) == NULLP
+    for k in ("bro", "co", "lat"):
+        assert gather(d, **{k: None}) == NULLP
+    assert gather(d, M=-1) == SHAPE
+    assert gather(cache_desc(num_kv=2)) == SHAPE
+    assert gather(cache_desc(dtype=2)) == DTYPE
+    assert gather(d, lat=FAKE + 8) == MISAL
+    assert gather(d, layer=2) == RANGE
+    assert gather(d, M=0, bro=None, co=None, lat=None) == OK
+    assert gather(d) == DEV
+    assert gather(cache_desc(dtype=0, head_dim=80, page_size=16)) == DEV
+
+
+def test_latent_matmul_error_paths(lib):
+    def mm(M=100, ld=576, N=512, K=512, dtype=1, **ptrs):
+        p = dict(lat=FAKE, w=FAKE, out=FAKE)
+        p.update(ptrs)
+        return lib.mla_latent_matmul(p["lat"], ld, M, p["w"], N, K, dtype, p["out"], None)
+    for k in ("lat", "w", "out"):
+        assert mm(**{k: None}) == NULLP
+    assert mm(M=-1) == SHAPE
+    assert mm(ld=256) == SHAPE          # ld < K
+    assert mm(ld=1 << 21) == SHAPE
+    assert mm(K=96, ld=96) == SHAPE     # bf16 needs K % 64
+    assert mm(N=100) == SHAPE
+    assert mm(dtype=2) == DTYPE
+    assert mm(ld=580) == MISAL          # 1160-byte rows
+    assert mm(w=FAKE + 2) == MISAL
+    assert mm(M=0, lat=None, w=None, out=None) == OK
+    assert mm() == DEV
+    assert mm(dtype=0, ld=80, N=128, K=64) == DEV
+
+
+def test_check_indices_host_paths(lib):
+    d = cache_desc(with_lengths=True)
+    bad = ctypes.c_int64(7)
+    assert lib.mla_check_indices(None, FAKE, 10, ctypes.byref(d), ctypes.byref(bad), None) == NULLP
+    assert bad.value == -1
+    no_len = cache_desc()
+    assert lib.mla_check_indices(FAKE, None, 10, ctypes.byref(no_len), None, None) == NULLP
+    assert lib.mla_check_indices(FAKE, FAKE, -1, ctypes.byref(d), None, None) == SHAPE
+    assert lib.mla_check_indices(FAKE, FAKE, 10, ctypes.byref(d), None, None) == DEV
+
+
 def test_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mp, "LIB_PATH", str(tmp_path / "nope.so"))
     monkeypatch.setattr(mp, "_lib", None)
