@@ -1,5 +1,5 @@
-// Pieces shared by the two persistent bf16 product kernels (decompress_bf16.hip,
-// decompress_bf16_ring.hip): problem description, the per-block tile list with
+// Pieces shared by the persistent product kernels (decompress_bf16.hip,
+// decompress_bf16_ring.hip, decompress_fp8_ring.hip): problem description, the per-block tile list with
 // its XCD-aware order, the accumulator drain used by the epilogues, barrier
 // helpers and the launch geometry.
 #pragma once
@@ -39,7 +39,9 @@ struct TileList {
     }
 };
 
-__device__ inline TileList make_tiles(const GemmParams& P)
+// PT: any parameter block with tiles_m, tiles_n and xcd_map.
+template <class PT>
+__device__ inline TileList make_tiles(const PT& P)
 {
     TileList L;
     L.tiles_n = P.tiles_n;

@@ -118,6 +118,46 @@ __device__ inline void buf_ld16_lds(rsrc_t r, void* lds, uint32_t voff, uint32_t
                                              (int)soff, 0, 0);
 }
 
+// The same buffer resource as four SGPR words, for inline assembly: base,
+// stride 0, num_records = bytes, raw 32-bit format.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ inline i32x4 make_srd(const void* base, uint32_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = kRsrcFlags;
+    return r;
+}
+// LDS address (byte offset in the workgroup's LDS) of a __shared__ location.
+__device__ inline uint32_t lds_addr(const void* p)
+{
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+// 16 bytes per lane from memory into LDS at lds + 16 * lane, issued from inline
+// assembly: the compiler does not know this instruction writes LDS, so it adds
+// no waits of its own for it.  The caller orders it against LDS reads with
+// explicit s_waitcnt vmcnt and barriers.
+__device__ inline void asm_ld16_lds(i32x4 srd, uint32_t lds, uint32_t voff, uint32_t soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(srd), "s"(soff)
+                 : "memory", "m0");
+}
+
+// 4 bytes per lane from memory into LDS at lds + 4 * lane (same rules as above).
+__device__ inline void asm_ld4_lds(i32x4 srd, uint32_t lds, uint32_t voff, uint32_t soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(srd), "s"(soff)
+                 : "memory", "m0");
+}
+
 // Non-temporal store: output rows are written once and not read back.
 __device__ inline void buf_st16_nt(rsrc_t r, u32x4 v, uint32_t voff, uint32_t soff)
 {

@@ -285,6 +285,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_bf16_ring(Gemm
         }
         epilogue(tile);
     }
+    // The last stage's spare loads may still be landing in LDS.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 }  // namespace

@@ -1,0 +1,349 @@
+// Persistent fp8 block-scaled product for gfx950 (page "mla_prefill_decode_graph_fp8":
+// Parameters fp8_dtype, fp8_scale_dtype, m/n/k_scale_granularity; Args w_k, w_k_scale):
+//
+//   k_buffer[m][n] = bf16( sum_kb s_a[m][kb] * s_w[n/128][kb] * sum_{k in kb} q_a[m][k] * q_w[n][k] )
+//
+// with q_a, s_a the e4m3fn codes and fp32 scales the gather pass wrote to the
+// workspace (1 x 128 blocks) and q_w, s_w the weight codes and 128 x 128 scales.
+//
+//  * One 512-thread block per CU walks 256 x 128 output tiles in the XCD-aware
+//    order of the bf16 kernels; 8 waves in a 4 x 2 grid own 64 x 64 each.
+//  * K advances one scale block (128 codes = 128 bytes per row) per stage.  A
+//    stage's operand tiles (256 + 128 rows of 128 bytes) and its scales go from
+//    memory straight into one of three LDS slots (buffer loads with an LDS
+//    destination), two stages ahead, so a load has two stage times to land;
+//    rows are 8 granules of 16 bytes XOR-swizzled by (row / 2) % 8.  The stream
+//    of stages runs straight across tile boundaries.
+//  * v_mfma_scale_f32_32x32x64_f8f6f4: two per 32 x 32 block and scale block.
+//    The fp32 scales are not powers of two, so they cannot ride on the MFMA's
+//    E8M0 scale inputs; instead the accumulators are kept in units of the
+//    current stage's scale sig = s_a * s_w: before a stage's MFMAs add its
+//    products, the accumulators are multiplied by ref / sig (ref: the previous
+//    stage's scale), and the epilogue multiplies by the last ref.  The weight is
+//    the MFMA's row operand, so a lane's 16 results lie in one output row (one
+//    s_a per 32-row block) and a wave's 64 columns lie in one 128-wide weight
+//    block (s_w is uniform).  A zero s_w makes its stage add nothing: the MFMAs
+//    then run with E8M0 operand scales 2^-127 each, so every product underflows
+//    to zero, and the accumulators keep their scale.
+//  * Epilogue as in the bf16 ring kernel (bf16 pairs into a per-wave LDS strip,
+//    read back as 16-byte row pieces, non-temporal stores), 8 rows at a time.
+//    The product is bound by these stores: 2 bytes out per 1024 flop of fp8 work.
+#include "bf16_tile_common.hpp"
+
+namespace mla {
+namespace {
+
+constexpr int BM = 256, BN = 128, BK = 128;       // BK: codes (bytes) per row per stage = one scale block
+constexpr int WAVES_M = 4, WAVES_N = 2, NW = WAVES_M * WAVES_N, NT = 64 * NW;
+constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // 64 x 64 per wave
+constexpr int FM = WTM / 32, FN = WTN / 32;
+constexpr int ROWB = BK;
+constexpr int CHUNK_ROWS = 1024 / ROWB;           // rows per 1 KB load chunk
+// A slot holds one stage: the activation rows, the weight rows, the stage's
+// activation scales (one float per row) and 64 copies of its weight scale.
+constexpr int A_BYTES = BM * ROWB, W_BYTES = BN * ROWB, SA_OFF = A_BYTES + W_BYTES, SW_OFF = SA_OFF + BM * 4;
+constexpr int SLOT_BYTES = SW_OFF + 256, NSLOT = 3;
+constexpr int CA = BM / CHUNK_ROWS / NW, CB = BN / CHUNK_ROWS / NW;
+constexpr int EPI_ROWS = 8, EPI = EPI_ROWS * WTN, EG = WTN / 8, EPI_PER_LANE = EPI_ROWS * EG / 64;
+constexpr int STORES_PER_TILE = (WTM / EPI_ROWS) * EPI_PER_LANE;
+static_assert(NSLOT * SLOT_BYTES + NW * EPI * 2 <= 163840, "LDS budget");
+static_assert(CA * NW * CHUNK_ROWS == BM && CB * NW * CHUNK_ROWS == BN, "loader shape");
+static_assert(CA % 2 == 0 && CB % 2 == 0, "chunks alternate between the two swizzle phases");
+static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's columns sit inside one weight scale block");
+static_assert(STORES_PER_TILE <= 63, "vmcnt range");
+static_assert(SLOT_BYTES % 256 == 0 && BM / 64 < NW, "slot layout");
+constexpr int LOADS = CA + CB + 1;  // loads per wave per stage
+
+struct Fp8GemmParams {
+    const uint8_t* A;     // [M][K] activation codes
+    const float* SA;      // [M][K/128] activation scales
+    const uint8_t* W;     // [N][K] weight codes
+    const float* SW;      // [N/128][K/128] weight scales
+    uint16_t* C;          // [M][N] bf16
+    int M, N, K;
+    int tiles_m, tiles_n;
+    int xcd_map;
+};
+
+struct Cursor {
+    int tile, ks, tn, row0;
+    i32x4 ar, wr;   // operand tiles, as resources for the inline-assembly loads
+};
+// Every load of the main loop is issued from inline assembly into LDS, so the
+// compiler sees no vector-memory loads there and inserts no waits of its own:
+// the only waits are the explicit ones before each stage's barrier.
+
+__device__ inline u32x2 pack4(float a, float b, float c, float d)
+{
+    return u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+}
+
+__device__ inline i32x8 join(u32x4 lo, u32x4 hi)
+{
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+__global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
+{
+    __shared__ __attribute__((aligned(1024))) char ring[NSLOT * SLOT_BYTES];
+    __shared__ __attribute__((aligned(16))) uint16_t strips[NW * EPI];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const TileList tl = make_tiles(P);
+    const int KT = P.K / BK;
+    if (tl.count == 0)
+        return;
+    const int total = tl.count * KT;  // stages this block runs
+
+    // Loader lanes: in a 1 KB chunk (8 rows of 128 bytes) lane l fills row l/8 at
+    // granule position l%8, i.e. logical granule (l%8) ^ ((row/2)%8); odd chunks
+    // start 8 rows further, which adds 4 to (row/2)%8.
+    const int lrow = lane >> 3;
+    const int lg_even = (lane & 7) ^ ((lrow >> 1) & 7), lg_odd = (lane & 7) ^ (((lrow >> 1) + 4) & 7);
+    const uint32_t k_lane[2] = {(uint32_t)(lrow * P.K + lg_even * 16), (uint32_t)(lrow * P.K + lg_odd * 16)};
+    const uint32_t chunk = (uint32_t)(CHUNK_ROWS * P.K);
+    const i32x4 sar = make_srd(P.SA, (uint32_t)((int64_t)P.M * KT * 4));
+    const i32x4 swr = make_srd(P.SW, (uint32_t)((P.N / 128) * KT * 4));
+    const uint32_t ring_lds = lds_addr(ring);
+
+    auto cursor_at = [&](int tile, Cursor& c) __attribute__((always_inline)) {
+        int tm, tn;
+        tl.coords(tile, tm, tn);
+        const int mrows = min(P.M - tm * BM, BM);
+        c.tile = tile;
+        c.ks = 0;
+        c.tn = tn;
+        c.row0 = tm * BM;
+        c.ar = make_srd(P.A + (int64_t)tm * BM * P.K, (uint32_t)(mrows * P.K));
+        c.wr = make_srd(P.W + (int64_t)tn * BN * P.K, (uint32_t)(BN * P.K));
+    };
+    // The cursor's stage into ring slot `sl`: operand tiles, the activation
+    // scales of the tile's rows (0 past M; waves 0..3 take 64 rows each) and
+    // the weight scale (wave 4, every lane the same value).  Past the last tile
+    // the last stage is loaded again (never used).
+    auto issue = [&](int sl, Cursor& c) __attribute__((always_inline)) {
+        const uint32_t s = ring_lds + sl * SLOT_BYTES;
+        const uint32_t kb = c.ks * BK;
+#pragma unroll
+        for (int q = 0; q < CA; ++q) {
+            const int ch = wave * CA + q;
+            asm_ld16_lds(c.ar, s + ch * 1024, k_lane[q & 1], ch * chunk + kb);
+        }
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+            const int ch = wave * CB + q;
+            asm_ld16_lds(c.wr, s + A_BYTES + ch * 1024, k_lane[q & 1], ch * chunk + kb);
+        }
+        // Every wave issues the same number of loads (the weight-scale copies
+        // of waves 4..7 are identical), so one vmcnt value fits all waves.
+        if (wave < BM / 64)
+            asm_ld4_lds(sar, s + SA_OFF + wave * 256, (uint32_t)((c.row0 + wave * 64 + lane) * KT) * 4,
+                        (uint32_t)c.ks * 4);
+        else
+            asm_ld4_lds(swr, s + SW_OFF, 0u, (uint32_t)(c.tn * KT + c.ks) * 4);
+        if (++c.ks == KT) {
+            if (c.tile + 1 < tl.count)
+                cursor_at(c.tile + 1, c);
+            else
+                c.ks = KT - 1;
+        }
+    };
+
+    // Fragment byte offsets (lane part): k step kk of a stage covers codes
+    // [64 kk, 64 kk + 64); lane l takes row l%32, codes 32*(l/32) .. +32 of it,
+    // i.e. granules 4 kk + 2 (l/32) + h, h = 0, 1.
+    const int frow = lane & 31;
+    int fr_off[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            fr_off[kk][h] = frow * ROWB + (((4 * kk + 2 * (lane >> 5) + h) ^ ((frow >> 1) & 7)) * 16);
+
+    // This stage's fragments and scales.
+    i32x8 fw[2][FN], fa[2][FM];
+    float sa_c[FM], sw_c;
+    auto load_frags = [&](int sl) __attribute__((always_inline)) {
+        const char* s = ring + sl * SLOT_BYTES;
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+            sa_c[j] = *reinterpret_cast<const float*>(s + SA_OFF + (wm * WTM + j * 32 + (lane & 31)) * 4);
+        sw_c = *reinterpret_cast<const float*>(s + SW_OFF + lane * 4);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int i = 0; i < FN; ++i) {
+                const char* p = s + A_BYTES + (wn * WTN + i * 32) * ROWB;
+                fw[kk][i] = join(lds_ld16(p + fr_off[kk][0]), lds_ld16(p + fr_off[kk][1]));
+            }
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                const char* p = s + (wm * WTM + j * 32) * ROWB;
+                fa[kk][j] = join(lds_ld16(p + fr_off[kk][0]), lds_ld16(p + fr_off[kk][1]));
+            }
+        }
+    };
+
+    f32x16 acc[FN][FM];
+    float ref[FM];  // scale the accumulators are expressed in (0: nothing added yet)
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+            acc[i][j] = f32x16{};
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+        ref[j] = 0.0f;
+
+    auto epilogue = [&](int tile) __attribute__((always_inline)) {
+        int tm, tn;
+        tl.coords(tile, tm, tn);
+        const int mrows = min(P.M - tm * BM, BM);
+        const rsrc_t cr = make_rsrc(P.C + (int64_t)tm * BM * P.N, (uint32_t)(mrows * P.N * 2));
+        uint16_t* E = strips + wave * EPI;
+        const int ncol0 = tn * BN + wn * WTN;
+        const int row = lane & (EPI_ROWS - 1), part = (lane & 31) / EPI_ROWS;
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+#pragma unroll
+            for (int h = 0; h < 32 / EPI_ROWS; ++h) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (part == h) {
+#pragma unroll
+                    for (int i = 0; i < FN; ++i) {
+                        const int col = i * 32 + 4 * (lane >> 5);
+                        uint16_t* e = E + row * WTN + (col & 7);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            lds_st8(e + swz(row, (col >> 3) + q, EG) * 8,
+                                    pack4(acc[i][j][4 * q] * ref[j], acc[i][j][4 * q + 1] * ref[j],
+                                          acc[i][j][4 * q + 2] * ref[j], acc[i][j][4 * q + 3] * ref[j]));
+                    }
+                }
+                wave_lds_sync();
+                u32x4 v[EPI_PER_LANE];
+#pragma unroll
+                for (int p = 0; p < EPI_PER_LANE; ++p) {
+                    const int idx = p * 64 + lane;
+                    const int r = idx / EG, g = idx % EG;
+                    v[p] = lds_ld16(E + r * WTN + swz(r, g, EG) * 8);
+                }
+                wave_lds_sync();
+#pragma unroll
+                for (int p = 0; p < EPI_PER_LANE; ++p) {
+                    const int idx = p * 64 + lane;
+                    const int r = idx / EG, g = idx % EG;
+                    const uint32_t off =
+                        (uint32_t)(((wm * WTM + j * 32 + h * EPI_ROWS + r) * P.N + ncol0 + g * 8) * 2);
+                    buf_st16_nt(cr, v[p], off, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+                acc[i][j] = f32x16{};
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+            ref[j] = 0.0f;
+    };
+
+    // Prologue: stages 0 and 1 in flight.
+    Cursor lc;
+    cursor_at(0, lc);
+    issue(0, lc);
+    issue(1, lc);
+
+    int slot = 0;      // ring slot of the current stage
+    int ks = 0, tile = 0;
+
+    // Stage g: wait for its loads (issued two stages earlier; stage g+1's may
+    // stay in flight, and after the first stage of a tile other than the first
+    // so may the previous tile's stores); the barrier makes the slot visible to
+    // all waves and frees the slot of stage g-1, which stage g+2's loads refill.
+    while (true) {
+        if (ks == 0 && tile > 0)
+            vm_barrier<LOADS + STORES_PER_TILE>();
+        else
+            vm_barrier<LOADS>();
+        load_frags(slot);
+        const int after = slot == 0 ? 2 : slot - 1;
+        issue(after, lc);
+        const bool skip = sw_c == 0.0f;
+        const int e8 = skip ? 0 : 127;
+        float rho[FM], ref_next[FM];
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const float sig = sa_c[j] * sw_c;
+            const float r = ref[j] * __builtin_amdgcn_rcpf(sig);
+            rho[j] = skip ? 1.0f : (ref[j] == 0.0f ? 0.0f : r);
+            ref_next[j] = skip ? ref[j] : sig;
+        }
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[i][j][e] *= rho[j];
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[0][i], fa[0][j], acc[i][j], 0, 0, 0, e8,
+                                                                            0, e8);
+            }
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[1][i], fa[1][j], acc[i][j], 0, 0, 0, e8,
+                                                                            0, e8);
+        // Order: reads and loads first, then per block its 16 rescale
+        // multiplies ahead of its first MFMA (run under the previous block's
+        // MFMA), then the second k step.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * (FN + FM) + FM + 1, 0);
+#pragma unroll
+        for (int b = 0; b < FN * FM; ++b) {
+            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, FN * FM, 0);
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+            ref[j] = ref_next[j];
+        slot = slot == NSLOT - 1 ? 0 : slot + 1;
+        if (++ks == KT) {
+            epilogue(tile);
+            ks = 0;
+            if (++tile == tl.count)
+                break;
+        }
+    }
+    // The spare loads of the last stages may still be landing in LDS.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+}  // namespace
+
+hipError_t launch_product_fp8_ring(const DecompressArgs& a, int cus, hipStream_t s)
+{
+    Fp8GemmParams P;
+    P.A = static_cast<const uint8_t*>(a.q);
+    P.SA = a.q_scale;
+    P.W = static_cast<const uint8_t*>(a.W);
+    P.SW = a.W_scale;
+    P.C = static_cast<uint16_t*>(a.out);
+    P.M = a.M;
+    P.N = a.N;
+    P.K = a.K;
+    P.tiles_m = (a.M + BM - 1) / BM;
+    P.tiles_n = a.N / BN;
+    P.xcd_map = (P.tiles_n % 8 == 0 && cus % 8 == 0) ? 1 : 0;
+    const int tiles = P.tiles_m * P.tiles_n;
+    const int grid = P.xcd_map ? cus : (tiles < cus ? tiles : cus);
+    hipLaunchKernelGGL(gemm_fp8_ring, dim3(grid), dim3(NT), 0, s, P);
+    return hipGetLastError();
+}
+
+}  // namespace mla

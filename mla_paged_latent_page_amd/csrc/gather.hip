@@ -1,26 +1,55 @@
 // Paged gather of latent rows (page "generic_flare_mla_decompress_k_cache_ragged_paged",
 // summary and Args buffer_row_offsets_1d, cache_offsets_1d, k_latent_buffer):
 //   k_latent[r][0:D] = cache row of request b at position cache_offsets[b] + (r - row_offsets[b])
-// as a bit copy.  One wave per row: the row's request and page are resolved with
-// wave-uniform (scalar) loads, then the lanes copy the row in 16-byte pieces.
-// The copy is HBM-bound (it reads and writes D * elem bytes per row).
+// as a bit copy.  The copy is HBM-bound: it reads and writes D * elem bytes per row.
+//
+// Each wave copies ROWS consecutive rows.  Lanes 0..ROWS-1 resolve one row each
+// (request by binary search, then page and slot), the offsets are broadcast
+// with readlane, and then every lane issues its 16-byte loads for all ROWS rows
+// before the first store, so ROWS loads per lane are in flight at once.
 #include "launch.hpp"
 
 namespace mla {
 namespace {
 
+constexpr int ROWS = 8;  // rows per wave
+
 __global__ void __launch_bounds__(256) gather_rows_kernel(DecompressArgs a, int granules_per_row)
 {
     const int lane = threadIdx.x & 63;
-    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (r >= a.M)
+    const int r0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * ROWS;
+    if (r0 >= a.M)
         return;
-    const uint32_t b = find_request(a.bro, a.L.batch, (uint32_t)r);
-    const uint32_t p = a.co[b] + ((uint32_t)r - a.bro[b]);
-    const char* src = a.L.base + token_offset(a.L, b, p);
-    char* dst = static_cast<char*>(a.lat) + (int64_t)r * granules_per_row * 16;
-    for (int g = lane; g < granules_per_row; g += 64)
-        st16(dst + g * 16, ld16(src + g * 16));
+
+    // Lane i < ROWS resolves row r0 + i (rows past M get a harmless offset 0).
+    int64_t my_off = 0;
+    const int my_row = r0 + lane;
+    if (lane < ROWS && my_row < a.M) {
+        const uint32_t b = find_request(a.bro, a.L.batch, (uint32_t)my_row);
+        const uint32_t p = a.co[b] + ((uint32_t)my_row - a.bro[b]);
+        my_off = token_offset(a.L, b, p);
+    }
+    const uint32_t off_lo = (uint32_t)my_off, off_hi = (uint32_t)(my_off >> 32);
+    const char* src[ROWS];
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+        const uint64_t o = ((uint64_t)__builtin_amdgcn_readlane(off_hi, i) << 32) | __builtin_amdgcn_readlane(off_lo, i);
+        src[i] = a.L.base + o;
+    }
+    const int nrows = min(ROWS, a.M - r0);
+    const int64_t row_bytes = (int64_t)granules_per_row * 16;
+    char* dst = static_cast<char*>(a.lat) + (int64_t)r0 * row_bytes;
+    for (int g = lane; g < granules_per_row; g += 64) {
+        u32x4 v[ROWS];
+#pragma unroll
+        for (int i = 0; i < ROWS; ++i)
+            if (i < nrows)
+                v[i] = ld16(src[i] + g * 16);
+#pragma unroll
+        for (int i = 0; i < ROWS; ++i)
+            if (i < nrows)
+                st16(dst + i * row_bytes + g * 16, v[i]);
+    }
 }
 
 }  // namespace
@@ -28,7 +57,8 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(DecompressArgs a, int 
 hipError_t launch_gather_rows(const DecompressArgs& a, int elem_bytes, hipStream_t s)
 {
     const int gpr = a.D * elem_bytes / 16;
-    hipLaunchKernelGGL(gather_rows_kernel, dim3((a.M + 3) / 4), dim3(256), 0, s, a, gpr);
+    const int waves = (a.M + ROWS - 1) / ROWS;
+    hipLaunchKernelGGL(gather_rows_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, a, gpr);
     return hipGetLastError();
 }
 

@@ -39,5 +39,6 @@ hipError_t launch_decompress_bf16(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_decompress_f32(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_decompress_fp8(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_kv_matmul(const KvMatmulArgs& a, hipStream_t s);
+hipError_t launch_product_fp8_ring(const DecompressArgs& a, int cus, hipStream_t s);
 
 }  // namespace mla

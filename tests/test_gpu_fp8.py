@@ -87,3 +87,26 @@ def test_c3_fp8_full_size_sampled():
     rows = sample_rows(case)
     say(f"[gpu] c3: {len(rows)} sampled rows")
     _check(case, rows)
+
+
+def test_fp8_zero_negative_and_far_apart_scales():
+    """Weight-scale blocks that are zero, negative or 10^12 apart, and latent
+    blocks whose magnitudes differ by 2^40 within a row: each scale block must
+    enter the sum with its own factor, and a zero block must add nothing."""
+    case = W.small_decompress(13, batch=4, max_len=300, page_size=16, K=512, rope=64, N=512, fp8=True)
+    ws = case.weight_scale.astype(np.float64)
+    ws[0, 1] = 0.0
+    ws[1, :] = 0.0
+    ws[2, 0] = -ws[2, 0]
+    ws[3, 0] *= 1e6
+    ws[3, 3] *= 1e-6
+    case.weight_scale = ws.astype(np.float32)
+    c = case.cache
+    used = c.page_table[c.page_table != W.PAGE_NONE].astype(np.int64)
+    blk = elem_f64(c.pool[used, case.layer_idx, 0, :, 0, :512], "bf16")
+    blk[..., 128:256] *= 2.0 ** 20
+    blk[..., 384:512] *= 2.0 ** -20
+    c.pool[used, case.layer_idx, 0, :, 0, :512] = W.to_bf16_bits(blk.astype(np.float32))
+    res, _ = _check(case)
+    got = res["out"][:case.M].double().cpu().numpy()
+    assert np.all(got[:, 128:256] == 0.0), "a weight block with zero scales must give exact zeros"
