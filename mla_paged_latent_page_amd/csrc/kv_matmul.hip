@@ -246,6 +246,8 @@ hipError_t launch_kv_matmul(const KvMatmulArgs& a, hipStream_t s)
         const char* e = getenv("MLA_PAGED_KV_TILE");
         return e ? atoi(e) : 0;
     }();
+    if (cfg == 0 && a.Kd % 128 == 0 && a.HD % 256 == 0)
+        return launch_kv_matmul_ring(a, num_cus(), s);
     switch (cfg) {
     case 1: return launch_cfg<256, 256, 2, 2>(a, s);
     case 2: return launch_cfg<128, 256, 2, 2>(a, s);

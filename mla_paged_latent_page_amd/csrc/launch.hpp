@@ -40,5 +40,7 @@ hipError_t launch_decompress_f32(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_decompress_fp8(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_kv_matmul(const KvMatmulArgs& a, hipStream_t s);
 hipError_t launch_product_fp8_ring(const DecompressArgs& a, int cus, hipStream_t s);
+hipError_t launch_kv_matmul_ring(const KvMatmulArgs& a, int cus, hipStream_t s);
+int num_cus();
 
 }  // namespace mla

@@ -88,3 +88,12 @@ def test_c4_with_cached_prefix_sampled():
     case = W.c4_kv_matmul(start="random")
     rng = np.random.default_rng(1)
     _check(case, np.sort(rng.choice(case.T, 400, replace=False)))
+
+
+@pytest.mark.parametrize("hidden,heads,dim", [(192, 1, 128), (384, 4, 64), (1024, 2, 256)])
+def test_kv_other_shapes(hidden, heads, dim):
+    """Shapes off the 256-column / 128-deep tiling (hidden 192, HD 128) take the
+    general kernel; HD 256 and 512 with hidden 384 / 1024 the pipelined one."""
+    case = W.small_kv_matmul(7, batch=5, max_len=350, hidden_dim=hidden, num_kv_heads=heads, head_dim=dim,
+                             page_size=32, start="random")
+    _check(case)
