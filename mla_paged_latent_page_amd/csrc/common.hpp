@@ -158,6 +158,16 @@ __device__ inline void asm_ld4_lds(i32x4 srd, uint32_t lds, uint32_t voff, uint3
                  : "memory", "m0");
 }
 
+// 16 bytes per lane from a per-lane 64-bit address into LDS at lds + 16 * lane,
+// from inline assembly (same rules as asm_ld16_lds).
+__device__ inline void asm_gld16_lds(const void* src, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds), "v"(src)
+                 : "memory", "m0");
+}
+
 // Non-temporal store: output rows are written once and not read back.
 __device__ inline void buf_st16_nt(rsrc_t r, u32x4 v, uint32_t voff, uint32_t soff)
 {

@@ -4,10 +4,11 @@
 // from page "mla_prefill_decode_graph_fp8", Args w_k):
 //   k_buffer[r][n] = sum_{k<K} k_latent[r][k] * W[n][k]   (fp32 accumulate, bf16 RNE out)
 //
-// The call runs the paged gather (gather.hip) into k_latent_buffer, then a
-// persistent product kernel over k_latent_buffer: the LDS-ring kernel of
-// decompress_bf16_ring.hip when K is a multiple of 128, else the register-staged
-// kernel below.
+// Up to 256 rows (decode-sized calls) take the single fused kernel of
+// decompress_small.hip.  Otherwise the call runs the paged gather (gather.hip)
+// into k_latent_buffer, then a persistent product kernel over k_latent_buffer:
+// the LDS-ring kernel of decompress_bf16_ring.hip when K is a multiple of 128,
+// else the register-staged kernel below.
 //
 // Design of the register-staged product (one block of 4 waves per CU,
 // persistent over tiles):
@@ -244,6 +245,8 @@ int num_cus()
 // K a multiple of 128: the LDS-ring kernel; otherwise the register-staged one.
 hipError_t launch_product_bf16(const DecompressArgs& a, hipStream_t s)
 {
+    if (small_bf16_fits(a))
+        return launch_small_bf16(a, 0, s);
     const int cus = num_cus();
     if (a.K % 128 == 0)
         return launch_product_bf16_ring(a, cus, s);
@@ -254,6 +257,8 @@ hipError_t launch_product_bf16(const DecompressArgs& a, hipStream_t s)
 
 hipError_t launch_decompress_bf16(const DecompressArgs& a, hipStream_t s)
 {
+    if (small_bf16_fits(a))
+        return launch_small_bf16(a, 1, s);
     hipError_t e = launch_gather_rows(a, 2, s);
     if (e != hipSuccess)
         return e;

@@ -42,5 +42,7 @@ hipError_t launch_kv_matmul(const KvMatmulArgs& a, hipStream_t s);
 hipError_t launch_product_fp8_ring(const DecompressArgs& a, int cus, hipStream_t s);
 hipError_t launch_kv_matmul_ring(const KvMatmulArgs& a, int cus, hipStream_t s);
 int num_cus();
+bool small_bf16_fits(const DecompressArgs& a);
+hipError_t launch_small_bf16(const DecompressArgs& a, int gather, hipStream_t s);
 
 }  // namespace mla
