@@ -15,7 +15,8 @@ The JSON line also carries the other rows of the path, each timed the same way:
   c2_prefill   bf16, 4 x 16384 rows, copies starting mid-cache
   c3_fp8       fp8 block-scaled form on the same shapes (quantise pass + product)
   c4_kv_matmul write path, 128 lognormal requests, hidden 4096 -> 2 x 8 x 128
-  p64, p256    1 and 4 newest rows per request of the decode batch (weight-bound)
+  p64, p256    1 and 4 newest rows per request of the decode batch (weight-bound;
+               timed by HIP-graph replay over 32 weight copies, see probe_row)
 
 Timing: HIP events recorded on the stream the library launches on (torch's
 current stream), per launch and around the whole timed region, bracketed by
@@ -43,8 +44,9 @@ CSRC = "mla_paged_latent_page_amd/csrc/"
 KERNEL_SOURCES = {
     "gemm_bf16_ring": ("decompress_bf16_ring.hip", "bf16_tile_common.hpp", "decompress_bf16.hip"),
     "gather_rows_kernel": ("gather.hip",),
-    "gemm_fp8_kernel": ("decompress_fp8.hip",),
-    "kv_matmul_kernel": ("kv_matmul.hip",),
+    "gemm_fp8_ring": ("decompress_fp8_ring.hip", "decompress_fp8.hip", "bf16_tile_common.hpp"),
+    "kv_matmul_ring": ("kv_matmul_ring.hip", "kv_matmul.hip", "bf16_tile_common.hpp"),
+    "decompress_small_bf16": ("decompress_small.hip",),
 }
 
 
@@ -142,6 +144,57 @@ def probe_case(W, base, newest):
     bro[1:] = np.cumsum(np.full(len(lens), newest))
     return W.DecompressCase(f"p{newest * len(lens)}", base.cache, base.layer_idx, bro, offs.astype(np.uint32),
                             base.K, base.N, base.weight, base.weight_dtype)
+
+
+def probe_row(torch, mp, W, pc, warmup, copies=32, reps=20):
+    """Few-rows call timed without launch overhead: `copies` launches, each on
+    its own copy of the weight (32 x 16 MiB, so every launch reads its weight
+    from HBM, not from the last-level cache), captured once in a HIP graph and
+    replayed `reps` times between two events.  The graph's output is checked
+    against an eager call first."""
+    dc, t = W.device_decompress(pc)
+    M, D, N = pc.M, pc.D_c, pc.N
+    lat = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    cache = mp.PagedKVCache(dc.pool, dc.page_table, dc.cache_lengths)
+    weights = [t["weight"].clone() for _ in range(copies)]
+
+    def call(w):
+        mp.mla_decompress_k_paged(t["buffer_row_offsets"], t["cache_offsets"], M, w, cache, pc.layer_idx, lat, out)
+    call(weights[0])
+    torch.cuda.synchronize()
+    eager = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for w in weights[:3]:
+            call(w)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for w in weights:
+            call(w)
+    for _ in range(max(1, warmup)):
+        g.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out.view(torch.int16), eager.view(torch.int16)):
+        raise RuntimeError(f"{pc.name}: graph replay differs from the eager call")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * copies)
+    f, b = decompress_costs(pc)
+    gbs = b / (ms * 1e-3) / 1e9
+    del g
+    return {"rows": M, "us_per_call": round(ms * 1e3, 3), "tflops": round(f / (ms * 1e-3) / 1e12, 2),
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", traffic_from_profile("decompress_small_bf16", pc.name)),
+            "kernel": "decompress_small_bf16 (gather + product in one launch)",
+            "timing": f"HIP graph of {copies} launches on {copies} weight copies, replayed {reps} times"}
 
 
 def roofline(bound, achieved, peak, unit, traffic):
@@ -258,12 +311,10 @@ def main():
         steps = max(3, args.steps // 2)
         for probe_n in (1, 4):
             pc = probe_case(W, case, probe_n)
-            t = Timed(torch, decompress_runner(torch, mp, W, pc), steps * 4, args.warmup)
-            f, b = decompress_costs(pc)
-            gbs = b / (t.avg_launch_ms * 1e-3) / 1e9
-            rows[pc.name] = {"rows": pc.M, "ms": round(t.avg_launch_ms, 4),
-                             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None),
-                             "tflops": round(f / (t.avg_launch_ms * 1e-3) / 1e12, 2)}
+            rows[pc.name] = probe_row(torch, mp, W, pc, args.warmup)
+            r = rows[pc.name]
+            print(f"[bench] {pc.name}: {r['us_per_call']:.2f} us/call (graph replay), "
+                  f"{r['roofline']['achieved']:.0f} GB/s", file=sys.stderr, flush=True)
         del fn
         torch.cuda.empty_cache()
         for name, make, bound in (("c2_prefill", W.c2_prefill, "mfma"), ("c3_fp8", W.c3_fp8, "hbm")):
@@ -275,13 +326,14 @@ def main():
             entry = {"rows": c.M, "ms": round(t.avg_launch_ms, 4), "rows_per_s": round(c.M / (t.avg_launch_ms * 1e-3), 1),
                      "tflops": round(tf, 2), "hbm_gbs_algorithmic": round(gbs, 1)}
             if bound == "mfma":
-                entry["roofline"] = roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", None)
-                entry["note"] = "time per call: gather + product"
+                entry["roofline"] = roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                             traffic_from_profile("gemm_bf16_ring", name))
+                entry["note"] = "time per call: gather + product (gemm_bf16_ring); traffic: the product kernel"
             else:
                 entry["roofline"] = roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s",
-                                             traffic_from_profile("gemm_fp8_kernel", name))
+                                             traffic_from_profile("gemm_fp8_ring", name))
                 entry["fp8_mfma_frac"] = round(tf / PEAK_FP8_TFLOPS, 4)
-                entry["note"] = "time per call: quantise pass + fp8 product"
+                entry["note"] = "time per call: gather + quantise pass (gather_quant_fp8_kernel) + fp8 product (gemm_fp8_ring)"
             rows[name] = entry
             print(f"[bench] {name}: {t.avg_launch_ms:.3f} ms, {tf:.1f} TFLOP/s, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
             torch.cuda.empty_cache()
@@ -298,7 +350,8 @@ def main():
         rows["c4_kv_matmul"] = {"tokens": kc.T, "ms": round(t.avg_launch_ms, 4), "tflops": round(tf, 2),
                                 "hbm_gbs_algorithmic": round(b / (t.avg_launch_ms * 1e-3) / 1e9, 1),
                                 "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
-                                                     traffic_from_profile("kv_matmul_kernel", "c4_kv_matmul"))}
+                                                     traffic_from_profile("kv_matmul_ring", "c4_kv_matmul")),
+                                "kernel": "kv_matmul_ring"}
         print(f"[bench] c4_kv_matmul: {t.avg_launch_ms:.3f} ms, {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
         result["rows"] = rows
 
