@@ -20,18 +20,29 @@ struct GemmParams {
 
 // The tiles of one persistent block, in the order it processes them.
 // Blocks are dispatched to the 8 XCDs round-robin (block b runs on XCD b % 8).
-// With the XCD map, XCD x owns N-tiles [x*G, (x+1)*G) and walks the M-tiles:
-// its 1/8 of W stays in its own L2 while the activation rows stream past, and
-// the N-tiles of one M-tile, running side by side, share those rows in L2.
+// xcd_map 1 (weight-stationary): XCD x owns N-tiles [x*G, (x+1)*G) and walks
+// the M-tiles, so its 1/8 of W stays in its own L2 while the activation rows
+// stream past; the N-tiles of one M-tile, running side by side, share those
+// rows in L2.  Suits activations that are re-read cheaply (the decompress
+// rows, 1 KB each).
+// xcd_map 2 (activation-stationary): XCD x owns M-tiles x, x+8, x+16, ... and
+// runs all N-tiles of an M-tile side by side, so each activation tile is
+// fetched from HBM once and the whole weight, small enough for the last-level
+// cache, is re-read from there.  Suits long activation rows with few N-tiles
+// (the kv projection: 8 KB rows, 8 N-tiles).
+// xcd_map 0: plain row-major order.
 struct TileList {
-    int first, step, count, Gn, x, tiles_n;
-    bool xcd;
+    int first, step, count, Gn, x, tiles_n, mode;
     __device__ void coords(int i, int& tm, int& tn) const
     {
         const int u = first + i * step;
-        if (xcd) {
+        if (mode == 1) {
             tm = u / Gn;
             tn = x * Gn + (u - tm * Gn);
+        } else if (mode == 2) {
+            const int q = u / tiles_n;
+            tm = x + 8 * q;
+            tn = u - q * tiles_n;
         } else {
             tm = u / tiles_n;
             tn = u - tm * tiles_n;
@@ -45,14 +56,20 @@ __device__ inline TileList make_tiles(const PT& P)
 {
     TileList L;
     L.tiles_n = P.tiles_n;
-    L.xcd = P.xcd_map != 0;
+    L.mode = P.xcd_map;
     int total;
-    if (L.xcd) {
+    if (L.mode == 1) {
         L.x = blockIdx.x & 7;
         L.first = blockIdx.x >> 3;
         L.step = gridDim.x >> 3;
         L.Gn = P.tiles_n >> 3;
         total = P.tiles_m * L.Gn;
+    } else if (L.mode == 2) {
+        L.x = blockIdx.x & 7;
+        L.first = blockIdx.x >> 3;
+        L.step = gridDim.x >> 3;
+        L.Gn = 1;
+        total = (P.tiles_m > L.x ? (P.tiles_m - L.x + 7) / 8 : 0) * P.tiles_n;
     } else {
         L.x = 0;
         L.Gn = 1;

@@ -278,12 +278,8 @@ hipError_t launch_decompress_fp8(const DecompressArgs& a, hipStream_t s)
     case 1: return launch_gemm<256, 128, 4, 2>(a, s);
     case 2: return launch_gemm<128, 256, 2, 4>(a, s);
     case 3: return launch_gemm<128, 128, 2, 2>(a, s);
-    default: {
-        int dev = 0, cus = 256;
-        if (hipGetDevice(&dev) == hipSuccess)
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        return launch_product_fp8_ring(a, cus, s);
-    }
+    default:
+        return launch_product_fp8_ring(a, num_cus(), s);
     }
 }
 

@@ -8,7 +8,8 @@
 //
 // Same pipeline as the LDS-ring decompress product (decompress_bf16_ring.hip):
 // one 512-thread block per CU walks 256 x 256 output tiles in XCD-aware order
-// (8 waves of 128 x 64), and 64-wide K stages go from memory straight into two
+// (activation-stationary: each XCD runs all N-tiles of its M-tiles side by
+// side; 8 waves of 128 x 64), and 64-wide K stages go from memory straight into two
 // LDS slots (buffer loads with an LDS destination).  The difference is the
 // weight: it is [K][N] with N contiguous, while the MFMA operand wants 8
 // consecutive k values per lane.  Its stage tile is kept in LDS as it lies in
@@ -295,7 +296,15 @@ hipError_t launch_kv_matmul_ring(const KvMatmulArgs& a, int cus, hipStream_t s)
     P.a = a;
     P.tiles_m = (a.T + BM - 1) / BM;
     P.tiles_n = a.N / BN;
-    P.xcd_map = (P.tiles_n % 8 == 0 && cus % 8 == 0) ? 1 : 0;
+    // Hidden rows are 8 KB and T is large: keep each activation tile in one
+    // XCD's L2 and re-read the (small) weight from the last-level cache.
+    static const int order = [] {
+        const char* e = getenv("MLA_PAGED_KV_ORDER");
+        return e ? atoi(e) : 2;
+    }();
+    P.xcd_map = (cus % 8 == 0 && P.tiles_m >= 8) ? order : 0;
+    if (P.xcd_map == 1 && P.tiles_n % 8 != 0)
+        P.xcd_map = 0;
     const int tiles = P.tiles_m * P.tiles_n;
     const int grid = P.xcd_map ? cus : (tiles < cus ? tiles : cus);
     hipLaunchKernelGGL(kv_matmul_ring, dim3(grid), dim3(NT), 0, s, P);
