@@ -26,8 +26,11 @@
 //    then run with E8M0 operand scales 2^-127 each, so every product underflows
 //    to zero, and the accumulators keep their scale.
 //  * Epilogue as in the bf16 ring kernel (bf16 pairs into a per-wave LDS strip,
-//    read back as 16-byte row pieces, non-temporal stores), 8 rows at a time.
+//    read back as 16-byte row pieces, non-temporal stores), 32 rows at a time;
+//    the strips live in the ring slot the tile's last stage consumed.
 //    The product is bound by these stores: 2 bytes out per 1024 flop of fp8 work.
+#include <type_traits>
+
 #include "bf16_tile_common.hpp"
 
 namespace mla {
@@ -44,9 +47,10 @@ constexpr int CHUNK_ROWS = 1024 / ROWB;           // rows per 1 KB load chunk
 constexpr int A_BYTES = BM * ROWB, W_BYTES = BN * ROWB, SA_OFF = A_BYTES + W_BYTES, SW_OFF = SA_OFF + BM * 4;
 constexpr int SLOT_BYTES = SW_OFF + 256, NSLOT = 3;
 constexpr int CA = BM / CHUNK_ROWS / NW, CB = BN / CHUNK_ROWS / NW;
-constexpr int EPI_ROWS = 8, EPI = EPI_ROWS * WTN, EG = WTN / 8, EPI_PER_LANE = EPI_ROWS * EG / 64;
+constexpr int EPI_ROWS = 32, EPI = EPI_ROWS * WTN, EG = WTN / 8, EPI_PER_LANE = EPI_ROWS * EG / 64;
 constexpr int STORES_PER_TILE = (WTM / EPI_ROWS) * EPI_PER_LANE;
-static_assert(NSLOT * SLOT_BYTES + NW * EPI * 2 <= 163840, "LDS budget");
+static_assert(NSLOT * SLOT_BYTES <= 163840, "LDS budget");
+static_assert(NW * EPI * 2 <= SLOT_BYTES, "the strips fit in one ring slot");
 static_assert(CA * NW * CHUNK_ROWS == BM && CB * NW * CHUNK_ROWS == BN, "loader shape");
 static_assert(CA % 2 == 0 && CB % 2 == 0, "chunks alternate between the two swizzle phases");
 static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's columns sit inside one weight scale block");
@@ -86,7 +90,6 @@ __device__ inline i32x8 join(u32x4 lo, u32x4 hi)
 __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
 {
     __shared__ __attribute__((aligned(1024))) char ring[NSLOT * SLOT_BYTES];
-    __shared__ __attribute__((aligned(16))) uint16_t strips[NW * EPI];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -165,24 +168,25 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
     // This stage's fragments and scales.
     i32x8 fw[2][FN], fa[2][FM];
     float sa_c[FM], sw_c;
-    auto load_frags = [&](int sl) __attribute__((always_inline)) {
+    // The stage's scales (KK == 0) and the fragments of its k step KK.
+    auto load_frags = [&](int sl, auto kk_c) __attribute__((always_inline)) {
+        constexpr int kk = decltype(kk_c)::value;
         const char* s = ring + sl * SLOT_BYTES;
+        if constexpr (kk == 0) {
 #pragma unroll
-        for (int j = 0; j < FM; ++j)
-            sa_c[j] = *reinterpret_cast<const float*>(s + SA_OFF + (wm * WTM + j * 32 + (lane & 31)) * 4);
-        sw_c = *reinterpret_cast<const float*>(s + SW_OFF + lane * 4);
+            for (int j = 0; j < FM; ++j)
+                sa_c[j] = *reinterpret_cast<const float*>(s + SA_OFF + (wm * WTM + j * 32 + (lane & 31)) * 4);
+            sw_c = *reinterpret_cast<const float*>(s + SW_OFF + lane * 4);
+        }
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int i = 0; i < FN; ++i) {
+            const char* p = s + A_BYTES + (wn * WTN + i * 32) * ROWB;
+            fw[kk][i] = join(lds_ld16(p + fr_off[kk][0]), lds_ld16(p + fr_off[kk][1]));
+        }
 #pragma unroll
-            for (int i = 0; i < FN; ++i) {
-                const char* p = s + A_BYTES + (wn * WTN + i * 32) * ROWB;
-                fw[kk][i] = join(lds_ld16(p + fr_off[kk][0]), lds_ld16(p + fr_off[kk][1]));
-            }
-#pragma unroll
-            for (int j = 0; j < FM; ++j) {
-                const char* p = s + (wm * WTM + j * 32) * ROWB;
-                fa[kk][j] = join(lds_ld16(p + fr_off[kk][0]), lds_ld16(p + fr_off[kk][1]));
-            }
+        for (int j = 0; j < FM; ++j) {
+            const char* p = s + (wm * WTM + j * 32) * ROWB;
+            fa[kk][j] = join(lds_ld16(p + fr_off[kk][0]), lds_ld16(p + fr_off[kk][1]));
         }
     };
 
@@ -197,50 +201,54 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
     for (int j = 0; j < FM; ++j)
         ref[j] = 0.0f;
 
-    auto epilogue = [&](int tile) __attribute__((always_inline)) {
+    // Write the finished tile through per-wave strips of 32 rows x 64 columns
+    // in ring slot `sl`, which the tile's last stage has just consumed: every
+    // wave has read it once the block meets, and it is not refilled before the
+    // next stage's barrier.
+    auto epilogue = [&](int tile, int sl) __attribute__((always_inline)) {
         int tm, tn;
         tl.coords(tile, tm, tn);
         const int mrows = min(P.M - tm * BM, BM);
         const rsrc_t cr = make_rsrc(P.C + (int64_t)tm * BM * P.N, (uint32_t)(mrows * P.N * 2));
-        uint16_t* E = strips + wave * EPI;
+        uint16_t* E = reinterpret_cast<uint16_t*>(ring + sl * SLOT_BYTES) + wave * EPI;
         const int ncol0 = tn * BN + wn * WTN;
-        const int row = lane & (EPI_ROWS - 1), part = (lane & 31) / EPI_ROWS;
+        // The lane's addresses are recomputed per tile from an opaque copy of
+        // the lane id: hoisted out of the stage loop they would hold registers
+        // for the whole kernel.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int row = ln & 31;
+        lds_barrier();
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int h = 0; h < 32 / EPI_ROWS; ++h) {
-                __builtin_amdgcn_sched_barrier(0);
-                if (part == h) {
+            for (int i = 0; i < FN; ++i) {
+                const int col = i * 32 + 4 * (ln >> 5);
+                uint16_t* e = E + row * WTN + (col & 7);
 #pragma unroll
-                    for (int i = 0; i < FN; ++i) {
-                        const int col = i * 32 + 4 * (lane >> 5);
-                        uint16_t* e = E + row * WTN + (col & 7);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            lds_st8(e + swz(row, (col >> 3) + q, EG) * 8,
-                                    pack4(acc[i][j][4 * q] * ref[j], acc[i][j][4 * q + 1] * ref[j],
-                                          acc[i][j][4 * q + 2] * ref[j], acc[i][j][4 * q + 3] * ref[j]));
-                    }
-                }
-                wave_lds_sync();
-                u32x4 v[EPI_PER_LANE];
-#pragma unroll
-                for (int p = 0; p < EPI_PER_LANE; ++p) {
-                    const int idx = p * 64 + lane;
-                    const int r = idx / EG, g = idx % EG;
-                    v[p] = lds_ld16(E + r * WTN + swz(r, g, EG) * 8);
-                }
-                wave_lds_sync();
-#pragma unroll
-                for (int p = 0; p < EPI_PER_LANE; ++p) {
-                    const int idx = p * 64 + lane;
-                    const int r = idx / EG, g = idx % EG;
-                    const uint32_t off =
-                        (uint32_t)(((wm * WTM + j * 32 + h * EPI_ROWS + r) * P.N + ncol0 + g * 8) * 2);
-                    buf_st16_nt(cr, v[p], off, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                for (int q = 0; q < 4; ++q)
+                    lds_st8(e + swz(row, (col >> 3) + q, EG) * 8,
+                            pack4(acc[i][j][4 * q] * ref[j], acc[i][j][4 * q + 1] * ref[j],
+                                  acc[i][j][4 * q + 2] * ref[j], acc[i][j][4 * q + 3] * ref[j]));
             }
+            wave_lds_sync();
+            u32x4 v[EPI_PER_LANE];
+#pragma unroll
+            for (int p = 0; p < EPI_PER_LANE; ++p) {
+                const int idx = p * 64 + ln;
+                const int r = idx / EG, g = idx % EG;
+                v[p] = lds_ld16(E + r * WTN + swz(r, g, EG) * 8);
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int p = 0; p < EPI_PER_LANE; ++p) {
+                const int idx = p * 64 + ln;
+                const int r = idx / EG, g = idx % EG;
+                const uint32_t off = (uint32_t)(((wm * WTM + j * 32 + r) * P.N + ncol0 + g * 8) * 2);
+                buf_st16_nt(cr, v[p], off, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int i = 0; i < FN; ++i)
@@ -270,9 +278,10 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
             vm_barrier<LOADS + STORES_PER_TILE>();
         else
             vm_barrier<LOADS>();
-        load_frags(slot);
+        load_frags(slot, std::integral_constant<int, 0>{});
         const int after = slot == 0 ? 2 : slot - 1;
         issue(after, lc);
+        load_frags(slot, std::integral_constant<int, 1>{});
         const bool skip = sw_c == 0.0f;
         const int e8 = skip ? 0 : 127;
         float rho[FM], ref_next[FM];
@@ -299,22 +308,25 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
             for (int j = 0; j < FM; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[1][i], fa[1][j], acc[i][j], 0, 0, 0, e8,
                                                                             0, e8);
-        // Order: reads and loads first, then per block its 16 rescale
-        // multiplies ahead of its first MFMA (run under the previous block's
-        // MFMA), then the second k step.
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 * (FN + FM) + FM + 1, 0);
+        // Order: the scales and the first k step's fragments first, then per
+        // block its 16 rescale multiplies (run under the previous block's
+        // MFMA), its first MFMA and a share of the second k step's fragment
+        // reads, then the second k step.
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (FN + FM) + FM + 1, 0);
 #pragma unroll
         for (int b = 0; b < FN * FM; ++b) {
             __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (FN + FM) / (FN * FM), 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, FN * FM, 0);
 #pragma unroll
         for (int j = 0; j < FM; ++j)
             ref[j] = ref_next[j];
+        const int done = slot;
         slot = slot == NSLOT - 1 ? 0 : slot + 1;
         if (++ks == KT) {
-            epilogue(tile);
+            epilogue(tile, done);
             ks = 0;
             if (++tile == tl.count)
                 break;

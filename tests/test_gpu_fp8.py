@@ -110,3 +110,16 @@ def test_fp8_zero_negative_and_far_apart_scales():
     res, _ = _check(case)
     got = res["out"][:case.M].double().cpu().numpy()
     assert np.all(got[:, 128:256] == 0.0), "a weight block with zero scales must give exact zeros"
+
+
+@pytest.mark.parametrize("K,N,batch,max_len", [(512, 8192, 8, 700), (128, 16384, 6, 500), (384, 8192, 10, 700),
+                                               (1024, 16384, 6, 500)])
+def test_fp8_several_tiles_per_block(K, N, batch, max_len):
+    """More output tiles than compute units, so every block carries one tile's
+    results into the next tile's stages; K of 1, 3, 4 and 8 scale blocks covers
+    every way a tile's rows are spread over its stages."""
+    case = W.small_decompress(20 + K // 128, batch=batch, max_len=max_len, page_size=16, K=K, rope=64, N=N, fp8=True)
+    tiles = -(-case.M // 256) * (N // 128)
+    say(f"[gpu] fp8 K={K} M={case.M} N={N}: {tiles} tiles")
+    assert tiles > 256
+    _check(case)
