@@ -7,23 +7,27 @@
 //    4 waves of 128 x 128 (256 accumulators, one wave per SIMD) or 8 waves of
 //    128 x 64 (128 accumulators, two waves per SIMD, so one wave's LDS and
 //    memory stalls are covered by the other's MFMAs).
-//  * K advances in 32-wide stages through a ring of four LDS slots (4 x 32 KB).
-//    Operand tiles go from memory straight into LDS (buffer loads with an LDS
-//    destination, 16 bytes per lane, no VGPR staging), three stages ahead of the
-//    MFMAs, so a load has about three stage times to land; the stream of stages
-//    runs straight across tile boundaries.
-//  * Per stage: read the fragments of k step 1 and issue step 0's 16 MFMAs;
-//    wait for this thread's loads of the next stage and meet at the block
-//    barrier (the next stage is then complete in LDS and the oldest slot is
-//    free); issue the loads three stages ahead into the free slot, read the next
-//    stage's step-0 fragments, and issue step 1's 16 MFMAs over them.
+//  * K advances in 64-wide stages through two LDS slots of 64 KB (256 rows of
+//    128 bytes for each operand).  Operand tiles go from memory straight into
+//    LDS (buffer loads with an LDS destination, 16 bytes per lane, no VGPR
+//    staging) one stage ahead of the MFMAs; the stream of stages runs straight
+//    across tile boundaries.
+//  * Per stage: wait for this thread's loads of the stage and meet at the block
+//    barrier (the stage is then complete in LDS, and every wave is done with
+//    the other slot); issue the next stage's loads into the other slot; read the
+//    fragments of k steps 0 and 1, then run each k step's 8 MFMAs while the
+//    fragments of the step after it are read.  The loads are spread over the
+//    first MFMAs so the waves, released together, do not flood the queues.
 //  * Each ring slot is a separate LDS array, so the compiler's own waits for the
 //    LDS-bound loads stay exact; the waits before the barrier are explicit.
-//  * Rows of 64 bytes hold four 16-byte granules XOR-swizzled by (row / 4) % 4:
-//    a 1 KB load chunk covers 16 rows, and 16 lanes reading one granule column
-//    of 16 rows hit 16 different bank groups.
-//  * K is a multiple of 128, so every tile spans a whole number of ring turns
-//    and the ring slot of each stage is known at compile time.
+//  * Rows of 128 bytes hold eight 16-byte granules XOR-swizzled by (row / 2) % 8:
+//    a 1 KB load chunk covers 8 rows, and the MFMA operand reads of 16 lanes
+//    (16 rows, one logical granule column) touch each of the 64 LDS banks once.
+//  * K is a multiple of 128, so every tile spans an even number of stages and
+//    the slot of each stage is known at compile time.
+//  * Epilogue per wave through a private LDS strip of 32 rows x 64 columns:
+//    bf16 pairs in, 16-byte row pieces out, non-temporal stores; after a tile
+//    the first stage of the next one waits only for its loads, not the stores.
 #include <type_traits>
 
 #include "bf16_tile_common.hpp"
