@@ -10,16 +10,16 @@
 //  * K advances in 64-wide stages through two LDS slots of 64 KB (256 rows of
 //    128 bytes for each operand).  Operand tiles go from memory straight into
 //    LDS (buffer loads with an LDS destination, 16 bytes per lane, no VGPR
-//    staging) one stage ahead of the MFMAs; the stream of stages runs straight
-//    across tile boundaries.
-//  * Per stage: wait for this thread's loads of the stage and meet at the block
-//    barrier (the stage is then complete in LDS, and every wave is done with
-//    the other slot); issue the next stage's loads into the other slot; read the
-//    fragments of k steps 0 and 1, then run each k step's 8 MFMAs while the
-//    fragments of the step after it are read.  The loads are spread over the
-//    first MFMAs so the waves, released together, do not flood the queues.
-//  * Each ring slot is a separate LDS array, so the compiler's own waits for the
-//    LDS-bound loads stay exact; the waits before the barrier are explicit.
+//    staging); the stream of stages runs straight across tile boundaries.
+//  * Per stage, with its k step 0 fragments already in registers: k steps 0..2
+//    run while the fragments of the step after each are read; then the block
+//    meets (this thread's loads of the next stage have landed, and every wave
+//    has read all of the current slot), the loads two stages ahead go into the
+//    current slot, one per MFMA of k step 3, and the next stage's step-0
+//    fragments are read under those MFMAs.  The matrix pipe has work as soon as
+//    the barrier opens.
+//  * The loads are issued from inline assembly, so the compiler adds no waits
+//    of its own for them; the waits before the barrier are explicit.
 //  * Rows of 128 bytes hold eight 16-byte granules XOR-swizzled by (row / 2) % 8:
 //    a 1 KB load chunk covers 8 rows, and the MFMA operand reads of 16 lanes
 //    (16 rows, one logical granule column) touch each of the 64 LDS banks once.
@@ -81,7 +81,7 @@ __device__ inline void interleave()
 // Where the loader of the next stages stands.
 struct LoadCursor {
     int tile, ks;
-    rsrc_t ar, wr;
+    i32x4 ar, wr;   // operand tiles, as resources for the inline-assembly loads
 };
 
 template <int WAVES_M, int WAVES_N>
@@ -125,24 +125,28 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_bf16_ring(Gemm
         const int mrows = min(P.M - tm * BM, BM), nrows = min(P.N - tn * BN, BN);
         c.tile = tile;
         c.ks = 0;
-        c.ar = make_rsrc(P.A + (int64_t)tm * BM * P.lda, (uint32_t)(mrows * P.lda * 2));
-        c.wr = make_rsrc(P.W + (int64_t)tn * BN * P.K, (uint32_t)(nrows * P.K * 2));
+        c.ar = make_srd(P.A + (int64_t)tm * BM * P.lda, (uint32_t)(mrows * P.lda * 2));
+        c.wr = make_srd(P.W + (int64_t)tn * BN * P.K, (uint32_t)(nrows * P.K * 2));
     };
-    // Issue the loads of the cursor's stage into ring slot b and advance the
-    // cursor.  Past the last tile the last stage is loaded again (never read).
-    auto issue = [&](auto b, LoadCursor& c) __attribute__((always_inline)) {
-        char* s = slot(b);
+    // Load q (of LOADS) of the cursor's stage into ring slot b.  The loads are
+    // issued from inline assembly, so the compiler adds no waits of its own for
+    // them; every wait is explicit.  Past the last tile the last stage is
+    // loaded again (never read).
+    auto load_one = [&](auto b, const LoadCursor& c, int q) __attribute__((always_inline)) {
+        const uint32_t s = lds_addr(slot(b));
         const uint32_t kb = c.ks * BK * 2;
-#pragma unroll
-        for (int q = 0; q < CA; ++q) {
+        if (q < CA) {
             const int ch = wave * CA + q;
-            buf_ld16_lds(c.ar, s + ch * 1024, a_lane[q & 1], ch * a_chunk + kb);
+            asm_ld16_lds(c.ar, s + ch * 1024, a_lane[q & 1], ch * a_chunk + kb);
+        } else {
+            const int ch = wave * CB + (q - CA);
+            asm_ld16_lds(c.wr, s + A_BYTES + ch * 1024, w_lane[(q - CA) & 1], ch * w_chunk + kb);
         }
+    };
+    auto issue = [&](auto b, LoadCursor& c) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < CB; ++q) {
-            const int ch = wave * CB + q;
-            buf_ld16_lds(c.wr, s + A_BYTES + ch * 1024, w_lane[q & 1], ch * w_chunk + kb);
-        }
+        for (int q = 0; q < LOADS; ++q)
+            load_one(b, c, q);
         ++c.ks;
     };
     // Move a cursor that ran off its tile to the next tile (kept out of the
@@ -236,41 +240,57 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_bf16_ring(Gemm
     using first_t = std::integral_constant<bool, true>;
     using rest_t = std::integral_constant<bool, false>;
 
-    // Prologue: stage 0 in flight.
+    // Prologue: stage 0 landed and visible, stage 1 in flight, stage 0's first
+    // fragments read.
     LoadCursor lc;
     cursor_at(0, lc);
     issue(I0{}, lc);
     settle(lc);
+    vm_barrier<0>();
+    issue(I1{}, lc);
+    settle(lc);
+    load_frags(I0{}, 0, fa0, fb0);
 
-    // One stage in slot B.  At its start this thread's loads of the stage have
-    // landed (after the first stage of a tile other than the first, the
-    // previous tile's stores are still queued behind them and may stay in
-    // flight: `relaxed`); the barrier then makes the stage visible to all waves
-    // and frees the other slot (everyone is done with the previous stage), so
-    // the next stage's loads go there while this one is multiplied.  Fragments
-    // of k step kk+1 are read under step kk's MFMAs.
+    // One stage in slot B, its k step 0 fragments already in registers.  Steps
+    // 0..2 run while the fragments of the step after each are read; then the
+    // block meets: this thread's loads of the next stage have landed (after the
+    // first stage of a tile other than the first, the previous tile's stores
+    // are queued behind them and may stay in flight: `relaxed`), so the next
+    // stage is complete in LDS, and every wave has read all of slot B.  The
+    // loads two stages ahead go into slot B, the next stage's step-0 fragments
+    // are read, and step 3's MFMAs cover that read: the matrix pipe has work
+    // as soon as the barrier opens.
     auto stage = [&](auto b, auto first, auto relaxed) __attribute__((always_inline)) {
         constexpr int B = decltype(b)::value;
         using Bn = std::integral_constant<int, (B + 1) % NBUF>;
-        if constexpr (decltype(relaxed)::value)
-            vm_barrier<STORES_PER_TILE>();
-        else
-            vm_barrier<0>();
-        issue(Bn{}, lc);
-        load_frags(b, 0, fa0, fb0);
         load_frags(b, 1, fa1, fb1);
         mfmas(fa0, fb0, first);
-        interleave<FN * FM, FN + FM, LOADS / 2>();
+        interleave<FN * FM, FN + FM, 0>();
         __builtin_amdgcn_sched_barrier(0);
         load_frags(b, 2, fa0, fb0);
         mfmas(fa1, fb1, rest_t{});
-        interleave<FN * FM, FN + FM, LOADS - LOADS / 2>();
+        interleave<FN * FM, FN + FM, 0>();
         __builtin_amdgcn_sched_barrier(0);
         load_frags(b, 3, fa1, fb1);
         mfmas(fa0, fb0, rest_t{});
         interleave<FN * FM, FN + FM, 0>();
         __builtin_amdgcn_sched_barrier(0);
-        mfmas(fa1, fb1, rest_t{});
+        static_assert(LOADS <= FN * FM, "one load per step-3 MFMA");
+        if constexpr (decltype(relaxed)::value)
+            vm_barrier<STORES_PER_TILE>();
+        else
+            vm_barrier<0>();
+        load_frags(Bn{}, 0, fa0, fb0);
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[i], fb1[j], acc[i][j], 0, 0, 0);
+                const int q = i * FM + j;
+                if (q < LOADS)
+                    load_one(b, lc, q);
+            }
+        ++lc.ks;
         __builtin_amdgcn_sched_barrier(0);
         settle(lc);
     };
