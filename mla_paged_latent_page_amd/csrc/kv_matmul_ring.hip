@@ -96,7 +96,7 @@ __global__ void __launch_bounds__(NT, 1) kv_matmul_ring(KvRingParams P)
 
     struct Cursor {
         int tile, ks;
-        rsrc_t ar, wr;
+        i32x4 ar, wr;   // operand tiles, as resources for the inline-assembly loads
     };
     auto cursor_at = [&](int tile, Cursor& c) __attribute__((always_inline)) {
         int tm, tn;
@@ -104,21 +104,25 @@ __global__ void __launch_bounds__(NT, 1) kv_matmul_ring(KvRingParams P)
         const int mrows = min(a.T - tm * BM, BM);
         c.tile = tile;
         c.ks = 0;
-        c.ar = make_rsrc(a.H + (int64_t)tm * BM * a.Kd, (uint32_t)(mrows * a.Kd * 2));
-        c.wr = make_rsrc(a.W + (int64_t)tn * BN, (uint32_t)((int64_t)a.Kd * a.N * 2 - (int64_t)tn * BN * 2));
+        c.ar = make_srd(a.H + (int64_t)tm * BM * a.Kd, (uint32_t)(mrows * a.Kd * 2));
+        c.wr = make_srd(a.W + (int64_t)tn * BN, (uint32_t)((int64_t)a.Kd * a.N * 2 - (int64_t)tn * BN * 2));
+    };
+    // Load q (of LOADS) of the cursor's stage into ring slot b, from inline
+    // assembly: the compiler adds no waits of its own for these loads.
+    auto load_one = [&](auto b, const Cursor& c, int q) __attribute__((always_inline)) {
+        const uint32_t s = lds_addr(slot(b));
+        if (q < CA) {
+            const int ch = wave * CA + q;
+            asm_ld16_lds(c.ar, s + ch * 1024, a_lane[q & 1], ch * a_chunk + c.ks * BK * 2);
+        } else {
+            const int ch = wave * CB + (q - CA);
+            asm_ld16_lds(c.wr, s + A_BYTES + ch * 1024, w_lane[(q - CA) & 1], (c.ks * BK) * a.N * 2 + ch * w_chunk);
+        }
     };
     auto issue = [&](auto b, Cursor& c) __attribute__((always_inline)) {
-        char* s = slot(b);
 #pragma unroll
-        for (int q = 0; q < CA; ++q) {
-            const int ch = wave * CA + q;
-            buf_ld16_lds(c.ar, s + ch * 1024, a_lane[q & 1], ch * a_chunk + c.ks * BK * 2);
-        }
-#pragma unroll
-        for (int q = 0; q < CB; ++q) {
-            const int ch = wave * CB + q;
-            buf_ld16_lds(c.wr, s + A_BYTES + ch * 1024, w_lane[q & 1], (c.ks * BK) * a.N * 2 + ch * w_chunk);
-        }
+        for (int q = 0; q < LOADS; ++q)
+            load_one(b, c, q);
         ++c.ks;
     };
     auto settle = [&](Cursor& c) __attribute__((always_inline)) {
@@ -243,20 +247,26 @@ __global__ void __launch_bounds__(NT, 1) kv_matmul_ring(KvRingParams P)
     using first_t = std::integral_constant<bool, true>;
     using rest_t = std::integral_constant<bool, false>;
 
+    // Prologue: stage 0 landed and visible, stage 1 in flight, stage 0's first
+    // fragments read.
     Cursor lc;
     cursor_at(0, lc);
     issue(I0{}, lc);
     settle(lc);
+    vm_barrier<0>();
+    issue(I1{}, lc);
+    settle(lc);
+    load_frags(I0{}, 0, fw0, fb0);
 
-    // One stage in slot B (see decompress_bf16_ring.hip): wait for this thread's
-    // loads of the stage (and any stores still in flight), meet at the barrier,
-    // issue the next stage into the other slot, multiply this one.
+    // One stage in slot B, its k step 0 fragments already in registers (the
+    // order of decompress_bf16_ring.hip): k steps 0..2 run while the fragments
+    // of the step after each are read; the block meets once this thread's
+    // loads of the next stage (and any stores) are done; then the loads two
+    // stages ahead go into slot B, one per MFMA of k step 3, and the next
+    // stage's step-0 fragments are read under those MFMAs.
     auto stage = [&](auto b, auto first) __attribute__((always_inline)) {
         constexpr int B = decltype(b)::value;
         using Bn = std::integral_constant<int, (B + 1) % 2>;
-        vm_barrier<0>();
-        issue(Bn{}, lc);
-        load_frags(b, 0, fw0, fb0);
         load_frags(b, 1, fw1, fb1);
         mfmas(fw0, fb0, first);
         __builtin_amdgcn_sched_barrier(0);
@@ -266,7 +276,19 @@ __global__ void __launch_bounds__(NT, 1) kv_matmul_ring(KvRingParams P)
         load_frags(b, 3, fw1, fb1);
         mfmas(fw0, fb0, rest_t{});
         __builtin_amdgcn_sched_barrier(0);
-        mfmas(fw1, fb1, rest_t{});
+        vm_barrier<0>();
+        load_frags(Bn{}, 0, fw0, fb0);
+        static_assert(LOADS <= FN * FM, "one load per step-3 MFMA");
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw1[i], fb1[j], acc[i][j], 0, 0, 0);
+                const int q = i * FM + j;
+                if (q < LOADS)
+                    load_one(b, lc, q);
+            }
+        ++lc.ks;
         __builtin_amdgcn_sched_barrier(0);
         settle(lc);
     };
