@@ -209,6 +209,63 @@ mla_status_t mla_decompress_k_paged_fp8(const uint32_t* buffer_row_offsets,
                                         void* stream);
 
 /*
+ * Fused K and V decompression: one gather, two up-projections of the gathered
+ * rows (page "mla_prefill_decode_graph_fp8", Args w_k and w_uv: w_uv projects the
+ * latent values to V, shape [num_heads][v_head_dim][kv_latent_dim], i.e. an
+ * [N_v][K] matrix with N_v = num_heads*v_head_dim; the gather and the product
+ * are those of page "generic_flare_mla_decompress_k_cache_ragged_paged").
+ *
+ *   k_latent_buffer and k_buffer exactly as mla_decompress_k_paged(..., w_k, N_k, ...)
+ *   v_buffer[r][n] = sum_{k<K} k_latent_buffer[r][k] * w_v[n][k]   (n < N_v),
+ *   fp32 accumulation, rounded to the cache dtype (round to nearest even).
+ *
+ * Every element of k_buffer and v_buffer equals, bit for bit, what
+ * mla_decompress_k_paged returns with w_k or w_v alone.  Each latent row is read
+ * once from the cache; with BF16, K % 128 == 0 and N_k % 256 == 0 both products
+ * run in a single launch that reads each tile of gathered rows for both.
+ *
+ * w_v        [device] [N_v][K] in the cache dtype, 16-byte aligned
+ * N_v        BF16: N_v % 64 == 0; F32: N_v % 4 == 0
+ * v_buffer   [device] [>= M][N_v] cache dtype, written
+ * Other arguments, errors and validation order as in mla_decompress_k_paged
+ * (w_k, N_k play the roles of weight, N).
+ */
+mla_status_t mla_decompress_kv_paged(const uint32_t* buffer_row_offsets,
+                                     const uint32_t* cache_offsets,
+                                     int32_t buffer_length,
+                                     const void* w_k, int32_t N_k,
+                                     const void* w_v, int32_t N_v, int32_t K,
+                                     const mla_paged_cache_t* cache, uint32_t layer_idx,
+                                     void* k_latent_buffer, void* k_buffer, void* v_buffer,
+                                     void* stream);
+
+/*
+ * The fp8 block-scaled form of mla_decompress_kv_paged (page
+ * "mla_prefill_decode_graph_fp8": Args w_k, w_k_scale, w_uv, w_uv_scale; the
+ * quantisation of the gathered rows as in mla_decompress_k_paged_fp8, done once
+ * for both products, which run in a single launch).
+ *
+ *   v_buffer[r][n] = bf16( sum_kb s_a[r][kb] * w_v_scale[n / n_gran][kb]
+ *                                * sum_{k in block kb} codes[r][k] * w_v[n][k] )
+ *
+ * w_v_e4m3   [device] [N_v][K] e4m3fn codes, 16-byte aligned; N_v % 128 == 0
+ * w_v_scale  [device] float [N_v / n_gran][K / k_gran]
+ * v_buffer   [device] [>= M][N_v] bf16, written
+ * Other arguments (workspace included), errors and validation order as in
+ * mla_decompress_k_paged_fp8.
+ */
+mla_status_t mla_decompress_kv_paged_fp8(const uint32_t* buffer_row_offsets,
+                                         const uint32_t* cache_offsets,
+                                         int32_t buffer_length,
+                                         const void* w_k_e4m3, const float* w_k_scale, int32_t N_k,
+                                         const void* w_v_e4m3, const float* w_v_scale, int32_t N_v,
+                                         int32_t K, int32_t m_gran, int32_t n_gran, int32_t k_gran,
+                                         const mla_paged_cache_t* cache, uint32_t layer_idx,
+                                         void* k_latent_buffer, void* k_buffer, void* v_buffer,
+                                         void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
+/*
  * Project hidden states and write them into the paged K/V cache (page
  * "kv_matmul_ragged_paged", summary and Args).
  *

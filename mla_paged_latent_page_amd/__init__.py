@@ -31,7 +31,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL_POINTER", 2: "MLA_ERR_INVALID_SHAPE",
 EXPORTS = ("mla_paged_cache_default_strides", "mla_decompress_k_paged", "mla_gather_latent_paged",
            "mla_latent_matmul", "mla_decompress_k_paged_fp8_workspace_size", "mla_decompress_k_paged_fp8",
            "kv_matmul_paged", "mla_check_indices", "mla_status_string", "mla_last_hip_error",
-           "mla_abi_version")
+           "mla_abi_version", "mla_decompress_kv_paged", "mla_decompress_kv_paged_fp8")
 
 
 class MlaError(RuntimeError):
@@ -78,6 +78,12 @@ def lib():
             L.mla_decompress_k_paged_fp8.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                                      ctypes.POINTER(CacheDesc), u32, vp, vp, vp, sz, vp]
             L.mla_decompress_k_paged_fp8.restype = i32
+            L.mla_decompress_kv_paged.argtypes = [vp, vp, i32, vp, i32, vp, i32, i32, ctypes.POINTER(CacheDesc),
+                                                  u32, vp, vp, vp, vp]
+            L.mla_decompress_kv_paged.restype = i32
+            L.mla_decompress_kv_paged_fp8.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                                      ctypes.POINTER(CacheDesc), u32, vp, vp, vp, vp, sz, vp]
+            L.mla_decompress_kv_paged_fp8.restype = i32
             L.kv_matmul_paged.argtypes = [vp, vp, i32, i32, vp, ctypes.POINTER(CacheDesc), u32, vp]
             L.kv_matmul_paged.restype = i32
             L.mla_gather_latent_paged.argtypes = [vp, vp, i32, ctypes.POINTER(CacheDesc), u32, vp, vp]
@@ -256,6 +262,60 @@ def mla_decompress_k_paged_fp8(buffer_row_offsets, cache_offsets, buffer_length:
                                           workspace.data_ptr() if workspace is not None else None,
                                           ws_bytes, _stream(stream))
     _check(st, "mla_decompress_k_paged_fp8")
+
+
+def _weight_shape(w, name):
+    if w.dim() != 2 or not w.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [N, K] tensor")
+    return w.shape
+
+
+def mla_decompress_kv_paged(buffer_row_offsets, cache_offsets, buffer_length: int, w_k, w_v,
+                            cache: PagedKVCache, layer_idx: int, k_latent_buffer, k_buffer, v_buffer,
+                            stream=None) -> None:
+    """One gather, two up-projections: k_buffer = rows @ w_k.T, v_buffer = rows @ w_v.T."""
+    N_k, K = _weight_shape(w_k, "w_k")
+    N_v, K_v = _weight_shape(w_v, "w_v")
+    if K_v != K:
+        raise ValueError("w_k and w_v must have the same K")
+    desc = cache.descriptor()
+    _check_outputs(buffer_length, desc, N_k, k_latent_buffer, k_buffer)
+    if v_buffer.numel() < buffer_length * N_v or not v_buffer.is_contiguous():
+        raise ValueError(f"v_buffer must be contiguous and hold at least [{buffer_length}, {N_v}]")
+    st = lib().mla_decompress_kv_paged(_u32(buffer_row_offsets, "buffer_row_offsets"),
+                                       _u32(cache_offsets, "cache_offsets"), int(buffer_length),
+                                       w_k.data_ptr(), N_k, w_v.data_ptr(), N_v, K, ctypes.byref(desc),
+                                       int(layer_idx), k_latent_buffer.data_ptr(), k_buffer.data_ptr(),
+                                       v_buffer.data_ptr(), _stream(stream))
+    _check(st, "mla_decompress_kv_paged")
+
+
+def mla_decompress_kv_paged_fp8(buffer_row_offsets, cache_offsets, buffer_length: int, w_k_e4m3, w_k_scale,
+                                w_v_e4m3, w_v_scale, cache: PagedKVCache, layer_idx: int, k_latent_buffer,
+                                k_buffer, v_buffer, workspace, m_gran: int = 1, n_gran: int = 128,
+                                k_gran: int = 128, stream=None) -> None:
+    """The fp8 block-scaled fused form (one gather and quantisation, two products)."""
+    N_k, K = _weight_shape(w_k_e4m3, "w_k_e4m3")
+    N_v, K_v = _weight_shape(w_v_e4m3, "w_v_e4m3")
+    if K_v != K:
+        raise ValueError("w_k_e4m3 and w_v_e4m3 must have the same K")
+    desc = cache.descriptor()
+    _check_outputs(buffer_length, desc, N_k, k_latent_buffer, k_buffer)
+    if v_buffer.numel() < buffer_length * N_v or not v_buffer.is_contiguous():
+        raise ValueError(f"v_buffer must be contiguous and hold at least [{buffer_length}, {N_v}]")
+    for sc, n, nm in ((w_k_scale, N_k, "w_k_scale"), (w_v_scale, N_v, "w_v_scale")):
+        if sc.numel() < -(-n // n_gran) * -(-K // k_gran) or sc.element_size() != 4:
+            raise ValueError(f"{nm} must hold float32 [N/n_gran, K/k_gran]")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().mla_decompress_kv_paged_fp8(_u32(buffer_row_offsets, "buffer_row_offsets"),
+                                           _u32(cache_offsets, "cache_offsets"), int(buffer_length),
+                                           w_k_e4m3.data_ptr(), w_k_scale.data_ptr(), N_k,
+                                           w_v_e4m3.data_ptr(), w_v_scale.data_ptr(), N_v, K,
+                                           m_gran, n_gran, k_gran, ctypes.byref(desc), int(layer_idx),
+                                           k_latent_buffer.data_ptr(), k_buffer.data_ptr(), v_buffer.data_ptr(),
+                                           workspace.data_ptr() if workspace is not None else None,
+                                           ws_bytes, _stream(stream))
+    _check(st, "mla_decompress_kv_paged_fp8")
 
 
 def kv_matmul_paged(hidden_state, input_row_offsets, weight, cache: PagedKVCache, layer_idx: int,

@@ -110,59 +110,131 @@ MLA_API mla_status_t mla_paged_cache_default_strides(mla_paged_cache_t* c)
     return MLA_OK;
 }
 
+namespace {
+
+// A second projection of the same rows (the fused K and V form), or none.
+struct Second {
+    const void* w = nullptr;
+    const float* scale = nullptr;   // fp8 only
+    int32_t N = 0;
+    void* out = nullptr;
+    bool present = false;
+};
+
+// Validation of the bf16 / f32 decompress calls, in the documented order
+// (pointers, shapes, dtype, alignment, ranges); D receives the cache row width.
+mla_status_t check_decompress(const uint32_t* bro, const uint32_t* co, int32_t M, const void* weight, int32_t N,
+                              int32_t K, const mla_paged_cache_t* cache, uint32_t layer_idx, const void* lat,
+                              const void* out, const Second& v, int64_t& D)
+{
+    if (!cache)
+        return MLA_ERR_NULL_POINTER;
+    const bool work = M > 0;
+    if (work && (!bro || !co || !weight || !lat || !out || !cache->blocks || !cache->page_table))
+        return MLA_ERR_NULL_POINTER;
+    if (work && v.present && (!v.w || !v.out))
+        return MLA_ERR_NULL_POINTER;
+    if (M < 0 || N <= 0 || K <= 0 || (v.present && v.N <= 0))
+        return MLA_ERR_INVALID_SHAPE;
+    if (mla_status_t st = check_cache_shape(cache, 1))
+        return st;
+    D = (int64_t)cache->num_heads * cache->head_dim;
+    if (K > D)
+        return MLA_ERR_INVALID_SHAPE;
+    const int32_t N2 = v.present ? v.N : 64;
+    if (cache->dtype == MLA_DTYPE_BF16) {
+        if (K % 64 || N % 64 || N2 % 64 || (int64_t)N * K * 2 >= (int64_t(1) << 31) ||
+            (int64_t)N2 * K * 2 >= (int64_t(1) << 31))
+            return MLA_ERR_INVALID_SHAPE;
+    } else if (cache->dtype == MLA_DTYPE_F32) {
+        if (K % 4 || N % 4 || N2 % 4)
+            return MLA_ERR_INVALID_SHAPE;
+    } else {
+        return MLA_ERR_INVALID_DTYPE;
+    }
+    if (!aligned16(weight) || !aligned16(lat) || !aligned16(out) || !aligned16(v.w) || !aligned16(v.out))
+        return MLA_ERR_MISALIGNED;
+    if (mla_status_t st = check_cache_alignment(cache))
+        return st;
+    if (layer_idx >= cache->num_layers)
+        return MLA_ERR_OUT_OF_RANGE;
+    return MLA_OK;
+}
+
+mla::DecompressArgs decompress_args(const uint32_t* bro, const uint32_t* co, int32_t M, const void* weight,
+                                    int32_t N, int32_t K, const mla_paged_cache_t* cache, uint32_t layer_idx,
+                                    void* lat, void* out, int64_t D, const Second& v)
+{
+    mla::DecompressArgs a{};
+    a.bro = bro;
+    a.co = co;
+    a.L = layer_view(cache, layer_idx);
+    a.W = weight;
+    a.lat = lat;
+    a.out = out;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.D = (int)D;
+    if (v.present) {
+        a.W2 = v.w;
+        a.W2_scale = v.scale;
+        a.out2 = v.out;
+        a.N2 = v.N;
+    }
+    return a;
+}
+
+}  // namespace
+
 MLA_API mla_status_t mla_decompress_k_paged(const uint32_t* buffer_row_offsets,
                                             const uint32_t* cache_offsets, int32_t buffer_length,
                                             const void* weight, int32_t N, int32_t K,
                                             const mla_paged_cache_t* cache, uint32_t layer_idx,
                                             void* k_latent_buffer, void* k_buffer, void* stream)
 {
-    if (!cache)
-        return MLA_ERR_NULL_POINTER;
-    const bool work = buffer_length > 0;
-    if (work && (!buffer_row_offsets || !cache_offsets || !weight || !k_latent_buffer || !k_buffer ||
-                 !cache->blocks || !cache->page_table))
-        return MLA_ERR_NULL_POINTER;
-    if (buffer_length < 0 || N <= 0 || K <= 0)
-        return MLA_ERR_INVALID_SHAPE;
-    if (mla_status_t st = check_cache_shape(cache, 1))
+    int64_t D = 0;
+    const Second none;
+    if (mla_status_t st = check_decompress(buffer_row_offsets, cache_offsets, buffer_length, weight, N, K, cache,
+                                           layer_idx, k_latent_buffer, k_buffer, none, D))
         return st;
-    const int64_t D = (int64_t)cache->num_heads * cache->head_dim;
-    if (K > D)
-        return MLA_ERR_INVALID_SHAPE;
-    if (cache->dtype == MLA_DTYPE_BF16) {
-        if (K % 64 || N % 64 || (int64_t)N * K * 2 >= (int64_t(1) << 31))
-            return MLA_ERR_INVALID_SHAPE;
-    } else if (cache->dtype == MLA_DTYPE_F32) {
-        if (K % 4 || N % 4)
-            return MLA_ERR_INVALID_SHAPE;
-    } else {
-        return MLA_ERR_INVALID_DTYPE;
-    }
-    if (!aligned16(weight) || !aligned16(k_latent_buffer) || !aligned16(k_buffer))
-        return MLA_ERR_MISALIGNED;
-    if (mla_status_t st = check_cache_alignment(cache))
-        return st;
-    if (layer_idx >= cache->num_layers)
-        return MLA_ERR_OUT_OF_RANGE;
-    if (!work)
+    if (buffer_length == 0)
         return MLA_OK;
     if (mla_status_t st = check_device())
         return st;
-
-    mla::DecompressArgs a{};
-    a.bro = buffer_row_offsets;
-    a.co = cache_offsets;
-    a.L = layer_view(cache, layer_idx);
-    a.W = weight;
-    a.lat = k_latent_buffer;
-    a.out = k_buffer;
-    a.M = buffer_length;
-    a.N = N;
-    a.K = K;
-    a.D = (int)D;
+    const mla::DecompressArgs a = decompress_args(buffer_row_offsets, cache_offsets, buffer_length, weight, N, K,
+                                                  cache, layer_idx, k_latent_buffer, k_buffer, D, none);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = cache->dtype == MLA_DTYPE_BF16 ? mla::launch_decompress_bf16(a, s)
                                                         : mla::launch_decompress_f32(a, s);
+    return e == hipSuccess ? MLA_OK : hip_failed(e);
+}
+
+MLA_API mla_status_t mla_decompress_kv_paged(const uint32_t* buffer_row_offsets,
+                                             const uint32_t* cache_offsets, int32_t buffer_length,
+                                             const void* w_k, int32_t N_k, const void* w_v, int32_t N_v,
+                                             int32_t K, const mla_paged_cache_t* cache, uint32_t layer_idx,
+                                             void* k_latent_buffer, void* k_buffer, void* v_buffer,
+                                             void* stream)
+{
+    int64_t D = 0;
+    Second v;
+    v.w = w_v;
+    v.N = N_v;
+    v.out = v_buffer;
+    v.present = true;
+    if (mla_status_t st = check_decompress(buffer_row_offsets, cache_offsets, buffer_length, w_k, N_k, K, cache,
+                                           layer_idx, k_latent_buffer, k_buffer, v, D))
+        return st;
+    if (buffer_length == 0)
+        return MLA_OK;
+    if (mla_status_t st = check_device())
+        return st;
+    const mla::DecompressArgs a = decompress_args(buffer_row_offsets, cache_offsets, buffer_length, w_k, N_k, K,
+                                                  cache, layer_idx, k_latent_buffer, k_buffer, D, v);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = cache->dtype == MLA_DTYPE_BF16 ? mla::launch_decompress_kv_bf16(a, s)
+                                                        : mla::launch_decompress_kv_f32(a, s);
     return e == hipSuccess ? MLA_OK : hip_failed(e);
 }
 
@@ -253,6 +325,56 @@ MLA_API size_t mla_decompress_k_paged_fp8_workspace_size(int32_t buffer_length, 
     return align256(M * (size_t)K) + align256(M * (size_t)(K / k_gran) * sizeof(float));
 }
 
+namespace {
+
+// Validation of the fp8 decompress calls, in the documented order.
+mla_status_t check_decompress_fp8(const uint32_t* bro, const uint32_t* co, int32_t M, const void* w,
+                                  const float* w_scale, int32_t N, int32_t K, int32_t m_gran, int32_t n_gran,
+                                  int32_t k_gran, const mla_paged_cache_t* cache, uint32_t layer_idx,
+                                  const void* lat, const void* out, const void* workspace, size_t workspace_bytes,
+                                  const Second& v, int64_t& D)
+{
+    if (!cache)
+        return MLA_ERR_NULL_POINTER;
+    const bool work = M > 0;
+    if (work && (!bro || !co || !w || !w_scale || !lat || !out || !workspace || !cache->blocks ||
+                 !cache->page_table))
+        return MLA_ERR_NULL_POINTER;
+    if (work && v.present && (!v.w || !v.scale || !v.out))
+        return MLA_ERR_NULL_POINTER;
+    const int32_t N2 = v.present ? v.N : 128;
+    if (M < 0 || N <= 0 || K <= 0 || N2 <= 0 || m_gran != 1 || n_gran != 128 || k_gran != 128 || N % 128 ||
+        N2 % 128 || K % 128 || (int64_t)N * K >= (int64_t(1) << 31) || (int64_t)N2 * K >= (int64_t(1) << 31))
+        return MLA_ERR_INVALID_SHAPE;
+    if (mla_status_t st = check_cache_shape(cache, 1))
+        return st;
+    D = (int64_t)cache->num_heads * cache->head_dim;
+    if (K > D)
+        return MLA_ERR_INVALID_SHAPE;
+    if (cache->dtype != MLA_DTYPE_BF16)
+        return MLA_ERR_INVALID_DTYPE;
+    if (!aligned16(w) || !aligned16(lat) || !aligned16(out) || !aligned16(v.w) || !aligned16(v.out) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) || (reinterpret_cast<uintptr_t>(w_scale) & 3u) ||
+        (reinterpret_cast<uintptr_t>(v.scale) & 3u))
+        return MLA_ERR_MISALIGNED;
+    if (mla_status_t st = check_cache_alignment(cache))
+        return st;
+    if (layer_idx >= cache->num_layers)
+        return MLA_ERR_OUT_OF_RANGE;
+    if (work && workspace_bytes < mla_decompress_k_paged_fp8_workspace_size(M, K, k_gran))
+        return MLA_ERR_WORKSPACE;
+    return MLA_OK;
+}
+
+void set_fp8_workspace(mla::DecompressArgs& a, const float* w_scale, void* workspace)
+{
+    a.W_scale = w_scale;
+    a.q = workspace;
+    a.q_scale = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)a.M * (size_t)a.K));
+}
+
+}  // namespace
+
 MLA_API mla_status_t mla_decompress_k_paged_fp8(const uint32_t* buffer_row_offsets,
                                                 const uint32_t* cache_offsets, int32_t buffer_length,
                                                 const void* weight_e4m3, const float* weight_scale,
@@ -261,53 +383,51 @@ MLA_API mla_status_t mla_decompress_k_paged_fp8(const uint32_t* buffer_row_offse
                                                 uint32_t layer_idx, void* k_latent_buffer, void* k_buffer,
                                                 void* workspace, size_t workspace_bytes, void* stream)
 {
-    if (!cache)
-        return MLA_ERR_NULL_POINTER;
-    const bool work = buffer_length > 0;
-    if (work && (!buffer_row_offsets || !cache_offsets || !weight_e4m3 || !weight_scale ||
-                 !k_latent_buffer || !k_buffer || !workspace || !cache->blocks || !cache->page_table))
-        return MLA_ERR_NULL_POINTER;
-    if (buffer_length < 0 || N <= 0 || K <= 0 || m_gran != 1 || n_gran != 128 || k_gran != 128 ||
-        N % 128 || K % 128 || (int64_t)N * K >= (int64_t(1) << 31))
-        return MLA_ERR_INVALID_SHAPE;
-    if (mla_status_t st = check_cache_shape(cache, 1))
+    int64_t D = 0;
+    const Second none;
+    if (mla_status_t st = check_decompress_fp8(buffer_row_offsets, cache_offsets, buffer_length, weight_e4m3,
+                                               weight_scale, N, K, m_gran, n_gran, k_gran, cache, layer_idx,
+                                               k_latent_buffer, k_buffer, workspace, workspace_bytes, none, D))
         return st;
-    const int64_t D = (int64_t)cache->num_heads * cache->head_dim;
-    if (K > D)
-        return MLA_ERR_INVALID_SHAPE;
-    if (cache->dtype != MLA_DTYPE_BF16)
-        return MLA_ERR_INVALID_DTYPE;
-    if (!aligned16(weight_e4m3) || !aligned16(k_latent_buffer) || !aligned16(k_buffer) ||
-        (reinterpret_cast<uintptr_t>(workspace) & 255u) || (reinterpret_cast<uintptr_t>(weight_scale) & 3u))
-        return MLA_ERR_MISALIGNED;
-    if (mla_status_t st = check_cache_alignment(cache))
-        return st;
-    if (layer_idx >= cache->num_layers)
-        return MLA_ERR_OUT_OF_RANGE;
-    const size_t need = mla_decompress_k_paged_fp8_workspace_size(buffer_length, K, k_gran);
-    if (work && workspace_bytes < need)
-        return MLA_ERR_WORKSPACE;
-    if (!work)
+    if (buffer_length == 0)
         return MLA_OK;
     if (mla_status_t st = check_device())
         return st;
-
-    mla::DecompressArgs a{};
-    a.bro = buffer_row_offsets;
-    a.co = cache_offsets;
-    a.L = layer_view(cache, layer_idx);
-    a.W = weight_e4m3;
-    a.W_scale = weight_scale;
-    a.lat = k_latent_buffer;
-    a.out = k_buffer;
-    a.q = workspace;
-    a.q_scale = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                         align256((size_t)buffer_length * (size_t)K));
-    a.M = buffer_length;
-    a.N = N;
-    a.K = K;
-    a.D = (int)D;
+    mla::DecompressArgs a = decompress_args(buffer_row_offsets, cache_offsets, buffer_length, weight_e4m3, N, K,
+                                            cache, layer_idx, k_latent_buffer, k_buffer, D, none);
+    set_fp8_workspace(a, weight_scale, workspace);
     const hipError_t e = mla::launch_decompress_fp8(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MLA_OK : hip_failed(e);
+}
+
+MLA_API mla_status_t mla_decompress_kv_paged_fp8(const uint32_t* buffer_row_offsets,
+                                                 const uint32_t* cache_offsets, int32_t buffer_length,
+                                                 const void* w_k_e4m3, const float* w_k_scale, int32_t N_k,
+                                                 const void* w_v_e4m3, const float* w_v_scale, int32_t N_v,
+                                                 int32_t K, int32_t m_gran, int32_t n_gran, int32_t k_gran,
+                                                 const mla_paged_cache_t* cache, uint32_t layer_idx,
+                                                 void* k_latent_buffer, void* k_buffer, void* v_buffer,
+                                                 void* workspace, size_t workspace_bytes, void* stream)
+{
+    int64_t D = 0;
+    Second v;
+    v.w = w_v_e4m3;
+    v.scale = w_v_scale;
+    v.N = N_v;
+    v.out = v_buffer;
+    v.present = true;
+    if (mla_status_t st = check_decompress_fp8(buffer_row_offsets, cache_offsets, buffer_length, w_k_e4m3,
+                                               w_k_scale, N_k, K, m_gran, n_gran, k_gran, cache, layer_idx,
+                                               k_latent_buffer, k_buffer, workspace, workspace_bytes, v, D))
+        return st;
+    if (buffer_length == 0)
+        return MLA_OK;
+    if (mla_status_t st = check_device())
+        return st;
+    mla::DecompressArgs a = decompress_args(buffer_row_offsets, cache_offsets, buffer_length, w_k_e4m3, N_k, K,
+                                            cache, layer_idx, k_latent_buffer, k_buffer, D, v);
+    set_fp8_workspace(a, w_k_scale, workspace);
+    const hipError_t e = mla::launch_decompress_kv_fp8(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MLA_OK : hip_failed(e);
 }
 

@@ -16,7 +16,27 @@ struct GemmParams {
     int M, N, K;
     int tiles_m, tiles_n;
     int xcd_map;
+    // Second projection (fused K and V): N-tiles tiles_n1 .. tiles_n - 1 take
+    // their weight rows from W2 [N2][K] and write C2 [M][N2].  tiles_n1 ==
+    // tiles_n when there is none.
+    const uint16_t* W2;
+    uint16_t* C2;
+    int N2, tiles_n1;
 };
+
+// The projection an N-tile belongs to: its weight, output, width and its
+// tile index within that projection.
+struct Segment {
+    const uint16_t* W;
+    uint16_t* C;
+    int N, tn;
+};
+__device__ inline Segment segment_of(const GemmParams& P, int tn)
+{
+    if (tn < P.tiles_n1)
+        return Segment{P.W, P.C, P.N, tn};
+    return Segment{P.W2, P.C2, P.N2, tn - P.tiles_n1};
+}
 
 // The tiles of one persistent block, in the order it processes them.
 // Blocks are dispatched to the 8 XCDs round-robin (block b runs on XCD b % 8).
@@ -134,6 +154,12 @@ inline GemmParams make_gemm_params(const DecompressArgs& a, int BM, int BN, int 
     P.K = a.K;
     P.tiles_m = (a.M + BM - 1) / BM;
     P.tiles_n = (a.N + BN - 1) / BN;
+    P.tiles_n1 = P.tiles_n;
+    P.W2 = static_cast<const uint16_t*>(a.W2);
+    P.C2 = static_cast<uint16_t*>(a.out2);
+    P.N2 = a.N2;
+    if (a.N2 > 0)   // the first projection's width is then a multiple of BN
+        P.tiles_n += (a.N2 + BN - 1) / BN;
     P.xcd_map = (P.tiles_n % 8 == 0 && cus % 8 == 0) ? 1 : 0;
     return P;
 }

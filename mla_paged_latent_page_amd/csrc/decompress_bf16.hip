@@ -265,4 +265,26 @@ hipError_t launch_decompress_bf16(const DecompressArgs& a, hipStream_t s)
     return launch_product_bf16(a, s);
 }
 
+// Fused K and V: the rows are gathered once.  With K a multiple of 128 and the
+// first projection a whole number of 256-column tiles, both projections run in
+// one product launch whose N-tiles span W and then W2 (each activation tile is
+// then read from L2 for both); otherwise the two products are launched in turn.
+// Few rows: the single-launch few-rows kernel gathers with the first projection
+// and the second reads the gathered rows back.
+hipError_t launch_decompress_kv_bf16(const DecompressArgs& a, hipStream_t s)
+{
+    const DecompressArgs k = first_projection(a), v = second_projection(a);
+    if (small_bf16_fits(k) && small_bf16_fits(v)) {
+        hipError_t e = launch_small_bf16(k, 1, s);
+        return e != hipSuccess ? e : launch_small_bf16(v, 0, s);
+    }
+    hipError_t e = launch_gather_rows(a, 2, s);
+    if (e != hipSuccess)
+        return e;
+    if (a.K % 128 == 0 && a.N % kRingTileN == 0)
+        return launch_product_bf16_ring(a, num_cus(), s);
+    e = launch_product_bf16(k, s);
+    return e != hipSuccess ? e : launch_product_bf16(v, s);
+}
+
 }  // namespace mla

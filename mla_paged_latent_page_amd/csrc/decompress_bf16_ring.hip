@@ -36,6 +36,7 @@ namespace mla {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 64, NBUF = 2;
+static_assert(BN == kRingTileN, "tile width the launchers assume");
 constexpr int ROWB = BK * 2;                  // bytes per tile row in a stage
 constexpr int CHUNK_ROWS = 1024 / ROWB;       // rows covered by one 1 KB load chunk
 constexpr int A_BYTES = BM * ROWB, SLOT_BYTES = (BM + BN) * ROWB;
@@ -122,11 +123,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_bf16_ring(Gemm
     auto cursor_at = [&](int tile, LoadCursor& c) __attribute__((always_inline)) {
         int tm, tn;
         tl.coords(tile, tm, tn);
-        const int mrows = min(P.M - tm * BM, BM), nrows = min(P.N - tn * BN, BN);
+        const Segment sg = segment_of(P, tn);
+        const int mrows = min(P.M - tm * BM, BM), nrows = min(sg.N - sg.tn * BN, BN);
         c.tile = tile;
         c.ks = 0;
         c.ar = make_srd(P.A + (int64_t)tm * BM * P.lda, (uint32_t)(mrows * P.lda * 2));
-        c.wr = make_srd(P.W + (int64_t)tn * BN * P.K, (uint32_t)(nrows * P.K * 2));
+        c.wr = make_srd(sg.W + (int64_t)sg.tn * BN * P.K, (uint32_t)(nrows * P.K * 2));
     };
     // Load q (of LOADS) of the cursor's stage into ring slot b.  The loads are
     // issued from inline assembly, so the compiler adds no waits of its own for
@@ -198,9 +200,10 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_bf16_ring(Gemm
         int tm, tn;
         tl.coords(tile, tm, tn);
         const int mrows = min(P.M - tm * BM, BM);
-        const rsrc_t cr = make_rsrc(P.C + (int64_t)tm * BM * P.N, (uint32_t)(mrows * P.N * 2));
+        const Segment sg = segment_of(P, tn);
+        const rsrc_t cr = make_rsrc(sg.C + (int64_t)tm * BM * sg.N, (uint32_t)(mrows * sg.N * 2));
         uint16_t* E = strips + wave * EPI;
-        const int ncol0 = tn * BN + wn * WTN;
+        const int ncol0 = sg.tn * BN + wn * WTN;
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
             __builtin_amdgcn_sched_barrier(0);
@@ -228,7 +231,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_bf16_ring(Gemm
                 const int idx = p * 64 + lane;
                 const int r = idx / EG, g = idx % EG;
                 const int n = ncol0 + g * 8;
-                const uint32_t off = n < P.N ? (uint32_t)(((wm * WTM + j * 32 + r) * P.N + n) * 2) : kOutOfRange;
+                const uint32_t off = n < sg.N ? (uint32_t)(((wm * WTM + j * 32 + r) * sg.N + n) * 2) : kOutOfRange;
                 buf_st16_nt(cr, v[p], off, 0);
             }
             __builtin_amdgcn_sched_barrier(0);

@@ -54,4 +54,14 @@ hipError_t launch_decompress_f32(const DecompressArgs& a, hipStream_t s)
     return launch_product_f32(a, s);
 }
 
+// Fused K and V (f32): one gather, then the two products.
+hipError_t launch_decompress_kv_f32(const DecompressArgs& a, hipStream_t s)
+{
+    hipError_t e = launch_gather_rows(a, 4, s);
+    if (e != hipSuccess)
+        return e;
+    e = launch_product_f32(first_projection(a), s);
+    return e != hipSuccess ? e : launch_product_f32(second_projection(a), s);
+}
+
 }  // namespace mla

@@ -279,8 +279,19 @@ hipError_t launch_decompress_fp8(const DecompressArgs& a, hipStream_t s)
     case 2: return launch_gemm<128, 256, 2, 4>(a, s);
     case 3: return launch_gemm<128, 128, 2, 2>(a, s);
     default:
-        return launch_product_fp8_ring(a, num_cus(), s);
+        return launch_product_fp8_ring(first_projection(a), num_cus(), s);
     }
+}
+
+// Fused K and V (fp8): one gather and quantisation pass, then one product
+// launch over both projections' N-tiles.
+hipError_t launch_decompress_kv_fp8(const DecompressArgs& a, hipStream_t s)
+{
+    hipLaunchKernelGGL(gather_quant_fp8_kernel, dim3((a.M + 3) / 4), dim3(256), 0, s, first_projection(a));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    return launch_product_fp8_ring(a, num_cus(), s);
 }
 
 }  // namespace mla

@@ -67,11 +67,31 @@ struct Fp8GemmParams {
     int M, N, K;
     int tiles_m, tiles_n;
     int xcd_map;
+    // Second projection (fused K and V): N-tiles tiles_n1 .. tiles_n - 1 use
+    // W2 [N2][K] with scales SW2 and write C2 [M][N2].
+    const uint8_t* W2;
+    const float* SW2;
+    uint16_t* C2;
+    int N2, tiles_n1;
 };
 
+// The projection an N-tile belongs to, and the tile's index within it.
+struct Fp8Segment {
+    const uint8_t* W;
+    const float* SW;
+    uint16_t* C;
+    int N, tn;
+};
+__device__ inline Fp8Segment segment_of(const Fp8GemmParams& P, int tn)
+{
+    if (tn < P.tiles_n1)
+        return Fp8Segment{P.W, P.SW, P.C, P.N, tn};
+    return Fp8Segment{P.W2, P.SW2, P.C2, P.N2, tn - P.tiles_n1};
+}
+
 struct Cursor {
-    int tile, ks, tn, row0;
-    i32x4 ar, wr;   // operand tiles, as resources for the inline-assembly loads
+    int tile, ks, tn, row0;     // tn: the tile's index within its projection
+    i32x4 ar, wr, swr;   // operand tiles and weight scales, as resources for the inline-assembly loads
 };
 // Every load of the main loop is issued from inline assembly into LDS, so the
 // compiler sees no vector-memory loads there and inserts no waits of its own:
@@ -108,7 +128,6 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
     const uint32_t k_lane[2] = {(uint32_t)(lrow * P.K + lg_even * 16), (uint32_t)(lrow * P.K + lg_odd * 16)};
     const uint32_t chunk = (uint32_t)(CHUNK_ROWS * P.K);
     const i32x4 sar = make_srd(P.SA, (uint32_t)((int64_t)P.M * KT * 4));
-    const i32x4 swr = make_srd(P.SW, (uint32_t)((P.N / 128) * KT * 4));
     const uint32_t ring_lds = lds_addr(ring);
 
     auto cursor_at = [&](int tile, Cursor& c) __attribute__((always_inline)) {
@@ -117,10 +136,12 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
         const int mrows = min(P.M - tm * BM, BM);
         c.tile = tile;
         c.ks = 0;
-        c.tn = tn;
+        const Fp8Segment sg = segment_of(P, tn);
+        c.tn = sg.tn;
         c.row0 = tm * BM;
         c.ar = make_srd(P.A + (int64_t)tm * BM * P.K, (uint32_t)(mrows * P.K));
-        c.wr = make_srd(P.W + (int64_t)tn * BN * P.K, (uint32_t)(BN * P.K));
+        c.wr = make_srd(sg.W + (int64_t)sg.tn * BN * P.K, (uint32_t)(BN * P.K));
+        c.swr = make_srd(sg.SW, (uint32_t)((sg.N / 128) * KT * 4));
     };
     // The cursor's stage into ring slot `sl`: operand tiles, the activation
     // scales of the tile's rows (0 past M; waves 0..3 take 64 rows each) and
@@ -145,7 +166,7 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
             asm_ld4_lds(sar, s + SA_OFF + wave * 256, (uint32_t)((c.row0 + wave * 64 + lane) * KT) * 4,
                         (uint32_t)c.ks * 4);
         else
-            asm_ld4_lds(swr, s + SW_OFF, 0u, (uint32_t)(c.tn * KT + c.ks) * 4);
+            asm_ld4_lds(c.swr, s + SW_OFF, 0u, (uint32_t)(c.tn * KT + c.ks) * 4);
         if (++c.ks == KT) {
             if (c.tile + 1 < tl.count)
                 cursor_at(c.tile + 1, c);
@@ -209,9 +230,10 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
         int tm, tn;
         tl.coords(tile, tm, tn);
         const int mrows = min(P.M - tm * BM, BM);
-        const rsrc_t cr = make_rsrc(P.C + (int64_t)tm * BM * P.N, (uint32_t)(mrows * P.N * 2));
+        const Fp8Segment sg = segment_of(P, tn);
+        const rsrc_t cr = make_rsrc(sg.C + (int64_t)tm * BM * sg.N, (uint32_t)(mrows * sg.N * 2));
         uint16_t* E = reinterpret_cast<uint16_t*>(ring + sl * SLOT_BYTES) + wave * EPI;
-        const int ncol0 = tn * BN + wn * WTN;
+        const int ncol0 = sg.tn * BN + wn * WTN;
         // The lane's addresses are recomputed per tile from an opaque copy of
         // the lane id: hoisted out of the stage loop they would hold registers
         // for the whole kernel.
@@ -245,7 +267,7 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
             for (int p = 0; p < EPI_PER_LANE; ++p) {
                 const int idx = p * 64 + ln;
                 const int r = idx / EG, g = idx % EG;
-                const uint32_t off = (uint32_t)(((wm * WTM + j * 32 + r) * P.N + ncol0 + g * 8) * 2);
+                const uint32_t off = (uint32_t)(((wm * WTM + j * 32 + r) * sg.N + ncol0 + g * 8) * 2);
                 buf_st16_nt(cr, v[p], off, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -351,6 +373,12 @@ hipError_t launch_product_fp8_ring(const DecompressArgs& a, int cus, hipStream_t
     P.K = a.K;
     P.tiles_m = (a.M + BM - 1) / BM;
     P.tiles_n = a.N / BN;
+    P.tiles_n1 = P.tiles_n;
+    P.W2 = static_cast<const uint8_t*>(a.W2);
+    P.SW2 = a.W2_scale;
+    P.C2 = static_cast<uint16_t*>(a.out2);
+    P.N2 = a.N2;
+    P.tiles_n += a.N2 / BN;
     P.xcd_map = (P.tiles_n % 8 == 0 && cus % 8 == 0) ? 1 : 0;
     const int tiles = P.tiles_m * P.tiles_n;
     const int grid = P.xcd_map ? cus : (tiles < cus ? tiles : cus);

@@ -21,6 +21,12 @@ struct DecompressArgs {
     void* q;               // fp8 only: activation codes [M][K]
     float* q_scale;        // fp8 only: activation scales [M][K/128]
     int M, N, K, D;        // D = elements per cache token row = row stride of lat
+    // Optional second projection of the same rows (the fused K and V form):
+    // out2[M][N2] = rows x W2^T, with W2 [N2][K] (and W2_scale for fp8).  N2 == 0: none.
+    const void* W2;
+    const float* W2_scale;
+    void* out2;
+    int N2;
 };
 
 struct KvMatmulArgs {
@@ -38,9 +44,37 @@ hipError_t launch_product_f32(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_decompress_bf16(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_decompress_f32(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_decompress_fp8(const DecompressArgs& a, hipStream_t s);
+// Fused K and V forms: one gather (and quantisation), both projections.
+hipError_t launch_decompress_kv_bf16(const DecompressArgs& a, hipStream_t s);
+hipError_t launch_decompress_kv_f32(const DecompressArgs& a, hipStream_t s);
+hipError_t launch_decompress_kv_fp8(const DecompressArgs& a, hipStream_t s);
+// The same arguments with the second projection moved into the first slot.
+inline DecompressArgs second_projection(const DecompressArgs& a)
+{
+    DecompressArgs b = a;
+    b.W = a.W2;
+    b.W_scale = a.W2_scale;
+    b.out = a.out2;
+    b.N = a.N2;
+    b.W2 = nullptr;
+    b.W2_scale = nullptr;
+    b.out2 = nullptr;
+    b.N2 = 0;
+    return b;
+}
+inline DecompressArgs first_projection(const DecompressArgs& a)
+{
+    DecompressArgs b = a;
+    b.W2 = nullptr;
+    b.W2_scale = nullptr;
+    b.out2 = nullptr;
+    b.N2 = 0;
+    return b;
+}
 hipError_t launch_kv_matmul(const KvMatmulArgs& a, hipStream_t s);
 hipError_t launch_product_fp8_ring(const DecompressArgs& a, int cus, hipStream_t s);
 hipError_t launch_kv_matmul_ring(const KvMatmulArgs& a, int cus, hipStream_t s);
+constexpr int kRingTileN = 256;   // N-tile width of the bf16 ring kernel
 int num_cus();
 bool small_bf16_fits(const DecompressArgs& a);
 hipError_t launch_small_bf16(const DecompressArgs& a, int gather, hipStream_t s);

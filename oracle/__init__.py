@@ -229,6 +229,25 @@ def decompress_k_fp8(case, rows=None):
     return lat, q, s, out
 
 
+def decompress_kv(case_k, case_v, rows=None):
+    """(k_latent bits, k_buffer rows, v_buffer rows), binary64 products.
+
+    The fused K and V form (page "mla_prefill_decode_graph_fp8", Args w_k and
+    w_uv: w_uv projects the latent values to V): one gather, then the first K
+    columns of each gathered row times W_k^T and times W_uv^T.  ``case_v`` is
+    ``case_k`` with the weight replaced by W_uv (same cache, offsets and K)."""
+    assert case_v.cache is case_k.cache and case_v.K == case_k.K
+    lat = gather(case_k)
+    if case_k.weight_dtype == "e4m3":
+        q, s = quantize_e4m3_rows(lat, case_k.K, case_k.k_gran)
+        k = fp8_matmul_nt(q, s, case_k.weight_q, case_k.weight_scale, case_k.n_gran, case_k.k_gran, rows)
+        v = fp8_matmul_nt(q, s, case_v.weight_q, case_v.weight_scale, case_v.n_gran, case_v.k_gran, rows)
+    else:
+        k = matmul_nt(lat, case_k.cache.dtype, case_k.weight, case_k.weight_dtype, case_k.K, rows)
+        v = matmul_nt(lat, case_v.cache.dtype, case_v.weight, case_v.weight_dtype, case_v.K, rows)
+    return lat, k, v
+
+
 def kv_destinations(case) -> np.ndarray:
     """int64 [T, 2]: element offsets into the pool of each token's K and V rows."""
     c = case.cache

@@ -58,6 +58,39 @@ def run_decompress(case, extra_rows=0, fp8=None):
     return res
 
 
+def run_decompress_kv(case, case_v, extra_rows=0):
+    """Run the fused K and V op (mla_decompress_kv_paged[_fp8]) on a case and
+    its second projection; outputs over-allocated by extra_rows poisoned rows."""
+    fp8 = case.weight_dtype == "e4m3"
+    dc, t = W.device_decompress(case)
+    _, tv = W.device_decompress(case_v)
+    M, D = case.M, case.D_c
+    dt = torch.float32 if case.cache.dtype == "f32" else torch.bfloat16
+    lat = torch.empty((M + extra_rows, D), dtype=dt, device="cuda")
+    kout = torch.empty((M + extra_rows, case.N), dtype=dt, device="cuda")
+    vout = torch.empty((M + extra_rows, case_v.N), dtype=dt, device="cuda")
+    for x in (lat, kout, vout):
+        if dt == torch.bfloat16:
+            x.view(torch.int16).fill_(POISON_OUT)
+        else:
+            x.fill_(float("nan"))
+    cache = mp.PagedKVCache(dc.pool, dc.page_table, dc.cache_lengths)
+    say(f"[gpu] {case.name} fused K+V: M={M} N_k={case.N} N_v={case_v.N} K={case.K} fp8={fp8}")
+    res = {"lat": lat, "k": kout, "v": vout, "pool": dc.pool}
+    if fp8:
+        ws_bytes = mp.mla_decompress_k_paged_fp8_workspace_size(M, case.K)
+        ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        mp.mla_decompress_kv_paged_fp8(t["buffer_row_offsets"], t["cache_offsets"], M, t["weight_q"],
+                                       t["weight_scale"], tv["weight_q"], tv["weight_scale"], cache,
+                                       case.layer_idx, lat, kout, vout, ws)
+        res["ws"] = ws
+    else:
+        mp.mla_decompress_kv_paged(t["buffer_row_offsets"], t["cache_offsets"], M, t["weight"], tv["weight"],
+                                   cache, case.layer_idx, lat, kout, vout)
+    torch.cuda.synchronize()
+    return res
+
+
 def workspace_views(ws, M, K):
     """(codes uint8 [M, K], scales float32 [M, K/128]) inside an fp8 workspace."""
     a = ws.cpu().numpy()

@@ -209,3 +209,58 @@ def test_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mp, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         mp.lib()
+
+
+def decompress_kv(lib, d, M=100, Nk=512, Nv=512, K=512, layer=1, **ptrs):
+    p = dict(bro=FAKE, co=FAKE, wk=FAKE, wv=FAKE, lat=FAKE, kout=FAKE, vout=FAKE)
+    p.update(ptrs)
+    return lib.mla_decompress_kv_paged(p["bro"], p["co"], M, p["wk"], Nk, p["wv"], Nv, K,
+                                       ctypes.byref(d) if d is not None else None, layer, p["lat"], p["kout"],
+                                       p["vout"], None)
+
+
+def test_decompress_kv_error_paths(lib):
+    """The fused K and V call checks its second weight and output like the first,
+    in the documented order (pointers, shapes, dtype, alignment, ranges)."""
+    d = cache_desc()
+    assert decompress_kv(lib, None) == NULLP
+    for k in ("bro", "co", "wk", "wv", "lat", "kout", "vout"):
+        assert decompress_kv(lib, d, **{k: None}) == NULLP
+    assert decompress_kv(lib, d, wv=None, Nv=100) == NULLP          # pointers come before shapes
+    assert decompress_kv(lib, d, Nv=0) == SHAPE
+    assert decompress_kv(lib, d, Nv=100) == SHAPE                    # bf16 needs N_v % 64
+    assert decompress_kv(lib, d, Nk=100) == SHAPE
+    assert decompress_kv(lib, d, K=1024) == SHAPE
+    assert decompress_kv(lib, cache_desc(dtype=2)) == DTYPE
+    assert decompress_kv(lib, d, wv=FAKE + 8) == MISAL
+    assert decompress_kv(lib, d, vout=FAKE + 4) == MISAL
+    assert decompress_kv(lib, d, vout=FAKE + 4, Nv=100) == SHAPE     # shapes come before alignment
+    assert decompress_kv(lib, d, layer=2) == RANGE
+    assert decompress_kv(lib, d, M=0, bro=None, co=None, wk=None, wv=None, lat=None, kout=None, vout=None) == OK
+    assert decompress_kv(lib, d) == DEV
+    assert decompress_kv(lib, cache_desc(dtype=0, head_dim=80, page_size=16), Nk=128, Nv=68, K=64) == DEV
+
+
+def fp8_kv(lib, d, M=100, Nk=512, Nv=512, K=512, grans=(1, 128, 128), ws=None, ws_bytes=None, layer=1, **ptrs):
+    p = dict(bro=FAKE, co=FAKE, wk=FAKE, sk=FAKE, wv=FAKE, sv=FAKE, lat=FAKE, kout=FAKE, vout=FAKE)
+    p.update(ptrs)
+    need = lib.mla_decompress_k_paged_fp8_workspace_size(max(M, 0), K, 128)
+    return lib.mla_decompress_kv_paged_fp8(p["bro"], p["co"], M, p["wk"], p["sk"], Nk, p["wv"], p["sv"], Nv, K,
+                                           *grans, ctypes.byref(d), layer, p["lat"], p["kout"], p["vout"],
+                                           FAKE if ws is None else ws, need if ws_bytes is None else ws_bytes, None)
+
+
+def test_decompress_kv_fp8_error_paths(lib):
+    d = cache_desc()
+    for k in ("bro", "co", "wk", "sk", "wv", "sv", "lat", "kout", "vout"):
+        assert fp8_kv(lib, d, **{k: None}) == NULLP
+    assert fp8_kv(lib, d, ws=0) == NULLP
+    assert fp8_kv(lib, d, Nv=192) == SHAPE                           # N_v % 128
+    assert fp8_kv(lib, d, grans=(1, 128, 64)) == SHAPE
+    assert fp8_kv(lib, cache_desc(dtype=0, head_dim=576)) == DTYPE
+    assert fp8_kv(lib, d, wv=FAKE + 8) == MISAL
+    assert fp8_kv(lib, d, sv=FAKE + 2) == MISAL
+    assert fp8_kv(lib, d, layer=5) == RANGE
+    assert fp8_kv(lib, d, ws_bytes=1000) == WS
+    assert fp8_kv(lib, d, M=0, ws_bytes=0) == OK
+    assert fp8_kv(lib, d) == DEV

@@ -223,6 +223,22 @@ def decompress_case(name, *, seed, cache_lengths, cache_offsets, page_size,
     return case
 
 
+def with_second_projection(case: DecompressCase, *, seed, N, w_std=0.02) -> DecompressCase:
+    """``case`` with its weight replaced by another projection of the same rows
+    (W_uv for the fused K and V form): same cache, offsets and K, a new [N, K]
+    weight drawn like the first (bf16/f32 N(0, w_std); e4m3 payload N(0,1) with
+    128x128 scales U[0.015, 0.025])."""
+    rng = np.random.default_rng(seed)
+    v = dataclasses.replace(case, name=case.name + "_v", N=N, weight=None, weight_q=None, weight_scale=None)
+    if case.weight_dtype == "e4m3":
+        v.weight_q = to_e4m3_bits(rng.standard_normal((N, case.K), dtype=np.float32))
+        v.weight_scale = rng.uniform(0.015, 0.025, size=(-(-N // 128), -(-case.K // 128))).astype(np.float32)
+    else:
+        w = rng.standard_normal((N, case.K), dtype=np.float32) * np.float32(w_std)
+        v.weight = to_bf16_bits(w) if case.weight_dtype == "bf16" else w.view(np.uint32).copy()
+    return v
+
+
 # --------------------------------------------------------------------------
 # write-path cases (projection + scatter into K/V pages)
 # --------------------------------------------------------------------------
