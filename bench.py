@@ -24,6 +24,7 @@ torch.cuda.synchronize().  The CPU baseline times the oracle on the host cores
 on a bounded sample of the same workload and is a reported baseline only.
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -120,6 +121,27 @@ def decompress_runner(torch, mp, W, case):
             mp.mla_decompress_k_paged(t["buffer_row_offsets"], t["cache_offsets"], M, t["weight"], cache,
                                       case.layer_idx, lat, out)
     return fn
+
+
+def kv_runner(torch, mp, W, case, case_v):
+    """One fused K and V call (mla_decompress_kv_paged) on a case and its W_uv."""
+    dc, t = W.device_decompress(case)
+    _, tv = W.device_decompress(case_v)
+    M, D = case.M, case.D_c
+    lat = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
+    kout = torch.empty((M, case.N), dtype=torch.bfloat16, device="cuda")
+    vout = torch.empty((M, case_v.N), dtype=torch.bfloat16, device="cuda")
+    cache = mp.PagedKVCache(dc.pool, dc.page_table, dc.cache_lengths)
+
+    def fused():
+        mp.mla_decompress_kv_paged(t["buffer_row_offsets"], t["cache_offsets"], M, t["weight"], tv["weight"],
+                                   cache, case.layer_idx, lat, kout, vout)
+
+    def separate():
+        mp.mla_decompress_k_paged(t["buffer_row_offsets"], t["cache_offsets"], M, t["weight"], cache,
+                                  case.layer_idx, lat, kout)
+        mp.mla_latent_matmul(lat, M, tv["weight"], vout)
+    return fused, separate
 
 
 def decompress_costs(case):
@@ -337,6 +359,42 @@ def main():
             rows[name] = entry
             print(f"[bench] {name}: {t.avg_launch_ms:.3f} ms, {tf:.1f} TFLOP/s, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
             torch.cuda.empty_cache()
+        # fused K and V on the prefill batch (W_uv drawn like W_k), against the
+        # same work as a K call followed by a V product on the gathered rows
+        c = W.c2_prefill()
+        cv = W.with_second_projection(c, seed=1002, N=c.N)
+        fused, separate = kv_runner(torch, mp, W, c, cv)
+        t = Timed(torch, fused, steps, args.warmup)
+        t2 = Timed(torch, separate, steps, args.warmup)
+        f = 2.0 * c.M * (c.N + cv.N) * c.K
+        b = c.M * (2 * c.D_c * 2 + (c.N + cv.N) * 2) + (c.N + cv.N) * c.K * 2
+        tf = f / (t.avg_launch_ms * 1e-3) / 1e12
+        rows["c2_fused_kv"] = {"rows": c.M, "ms": round(t.avg_launch_ms, 4),
+                               "separate_calls_ms": round(t2.avg_launch_ms, 4), "tflops": round(tf, 2),
+                               "hbm_gbs_algorithmic": round(b / (t.avg_launch_ms * 1e-3) / 1e9, 1),
+                               "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                                    traffic_from_profile("gemm_bf16_ring", "c2_fused_kv")),
+                               "note": "one gather + one gemm_bf16_ring launch over the N-tiles of W_k, then "
+                                       "those of W_uv [16384, 512] (each XCD keeps one projection's share of "
+                                       "the weight in L2 at a time); separate_calls_ms: mla_decompress_k_paged "
+                                       "then mla_latent_matmul with W_uv"}
+        print(f"[bench] c2_fused_kv: {t.avg_launch_ms:.3f} ms ({tf:.1f} TFLOP/s); separate calls "
+              f"{t2.avg_launch_ms:.3f} ms", file=sys.stderr, flush=True)
+        del fused, separate
+        torch.cuda.empty_cache()
+        # one GPU's share of W_k under 8-way tensor parallelism over heads: N = 2048
+        ct = dataclasses.replace(c, name="c2_tp8_share", N=2048, weight=np.ascontiguousarray(c.weight[:2048]))
+        t = Timed(torch, decompress_runner(torch, mp, W, ct), steps, args.warmup)
+        f, b = decompress_costs(ct)
+        tf = f / (t.avg_launch_ms * 1e-3) / 1e12
+        rows["c2_tp8_share"] = {"rows": ct.M, "N": 2048, "ms": round(t.avg_launch_ms, 4), "tflops": round(tf, 2),
+                                "hbm_gbs_algorithmic": round(b / (t.avg_launch_ms * 1e-3) / 1e9, 1),
+                                "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                                     traffic_from_profile("gemm_bf16_ring", "c2_tp8_share")),
+                                "note": "the prefill batch against the first 16 heads of W_k (N = 2048), "
+                                        "one GPU's share at 8-way tensor parallelism over heads"}
+        print(f"[bench] c2_tp8_share: {t.avg_launch_ms:.3f} ms, {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
         kc = W.c4_kv_matmul()
         dc, tt = W.device_kv(kc)
         cache = mp.PagedKVCache(dc.pool, dc.page_table, dc.cache_lengths)

@@ -50,15 +50,24 @@ __device__ inline Segment segment_of(const GemmParams& P, int tn)
 // fetched from HBM once and the whole weight, small enough for the last-level
 // cache, is re-read from there.  Suits long activation rows with few N-tiles
 // (the kv projection: 8 KB rows, 8 N-tiles).
+// xcd_map 3 (two projections, weight-stationary in two passes): XCD x walks the
+// M-tiles over its eighth of the first projection's N-tiles, then over its
+// eighth of the second's, so only one projection's eighth of the weight has to
+// stay in its L2 at a time (both together would fill it).
 // xcd_map 0: plain row-major order.
 struct TileList {
     int first, step, count, Gn, x, tiles_n, mode;
+    int G2, tiles_n1, pass1;   // xcd_map 3 only
     __device__ void coords(int i, int& tm, int& tn) const
     {
         const int u = first + i * step;
-        if (mode == 1) {
+        if (mode == 1 || (mode == 3 && u < pass1)) {
             tm = u / Gn;
             tn = x * Gn + (u - tm * Gn);
+        } else if (mode == 3) {
+            const int v = u - pass1;
+            tm = v / G2;
+            tn = tiles_n1 + x * G2 + (v - tm * G2);
         } else if (mode == 2) {
             const int q = u / tiles_n;
             tm = x + 8 * q;
@@ -70,6 +79,11 @@ struct TileList {
     }
 };
 
+// N-tiles of the first projection (all of them unless the block has two).
+template <class PT>
+__device__ inline int first_projection_tiles(const PT& P) { return P.tiles_n; }
+__device__ inline int first_projection_tiles(const GemmParams& P) { return P.tiles_n1; }
+
 // PT: any parameter block with tiles_m, tiles_n and xcd_map.
 template <class PT>
 __device__ inline TileList make_tiles(const PT& P)
@@ -77,8 +91,19 @@ __device__ inline TileList make_tiles(const PT& P)
     TileList L;
     L.tiles_n = P.tiles_n;
     L.mode = P.xcd_map;
+    L.G2 = 0;
+    L.tiles_n1 = first_projection_tiles(P);
+    L.pass1 = 0;
     int total;
-    if (L.mode == 1) {
+    if (L.mode == 3) {
+        L.x = blockIdx.x & 7;
+        L.first = blockIdx.x >> 3;
+        L.step = gridDim.x >> 3;
+        L.Gn = L.tiles_n1 >> 3;
+        L.G2 = (P.tiles_n - L.tiles_n1) >> 3;
+        L.pass1 = P.tiles_m * L.Gn;
+        total = L.pass1 + P.tiles_m * L.G2;
+    } else if (L.mode == 1) {
         L.x = blockIdx.x & 7;
         L.first = blockIdx.x >> 3;
         L.step = gridDim.x >> 3;
@@ -158,9 +183,12 @@ inline GemmParams make_gemm_params(const DecompressArgs& a, int BM, int BN, int 
     P.W2 = static_cast<const uint16_t*>(a.W2);
     P.C2 = static_cast<uint16_t*>(a.out2);
     P.N2 = a.N2;
-    if (a.N2 > 0)   // the first projection's width is then a multiple of BN
+    if (a.N2 > 0) {   // the first projection's width is then a multiple of BN
         P.tiles_n += (a.N2 + BN - 1) / BN;
-    P.xcd_map = (P.tiles_n % 8 == 0 && cus % 8 == 0) ? 1 : 0;
+        P.xcd_map = (P.tiles_n1 % 8 == 0 && (P.tiles_n - P.tiles_n1) % 8 == 0 && cus % 8 == 0) ? 3 : 0;
+    } else {
+        P.xcd_map = (P.tiles_n % 8 == 0 && cus % 8 == 0) ? 1 : 0;
+    }
     return P;
 }
 

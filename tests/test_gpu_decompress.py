@@ -116,3 +116,12 @@ def test_c1_decode_full_size_sampled():
 @pytest.mark.slow
 def test_c2_prefill_full_size_sampled():
     _check_sampled(W.c2_prefill())
+
+
+@pytest.mark.slow
+def test_c2_tensor_parallel_share_sampled():
+    """One GPU's share of W_k under 8-way tensor parallelism over heads (the
+    first 16 heads: N = 2048) on the full prefill batch, as the bench times it."""
+    import dataclasses
+    c = W.c2_prefill()
+    _check_sampled(dataclasses.replace(c, name="c2_tp8_share", N=2048, weight=np.ascontiguousarray(c.weight[:2048])))
