@@ -148,3 +148,28 @@ def test_fp8_scales_are_indexed_by_row_block_and_column_block():
     assert np.all(out[:, :128] == 0) and np.all(out[:, 256:] == 0)
     ref = vals[:, 256:384].sum(axis=1) * 0.5
     np.testing.assert_allclose(out[:, 128:256], np.repeat(ref[:, None], 128, 1), rtol=1e-12)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_fused_kv_is_the_two_products_of_one_gather(fp8):
+    """The V product of the fused form is the same definition with W_uv: a
+    selection W_uv picks latent columns exactly (bf16), and each output equals
+    the single-projection oracle on its own weight."""
+    case = W.small_decompress(7, batch=3, max_len=60, page_size=16, K=256, rope=64, N=128, fp8=fp8)
+    case_v = W.with_second_projection(case, seed=8, N=256)
+    lat, k, v = oracle.decompress_kv(case, case_v)
+    if fp8:
+        _, _, _, k1 = oracle.decompress_k_fp8(case)
+        _, _, _, v1 = oracle.decompress_k_fp8(case_v)
+    else:
+        _, k1 = oracle.decompress_k(case)
+        _, v1 = oracle.decompress_k(case_v)
+        # W_uv row n = e_{(3n) mod K}: v[:, n] is latent column (3n) mod K, exactly
+        sel = np.zeros((256, case.K), np.float32)
+        sel[np.arange(256), (3 * np.arange(256)) % case.K] = 1.0
+        case_s = W.with_second_projection(case, seed=9, N=256)
+        case_s.weight = W.to_bf16_bits(sel)
+        _, _, vs = oracle.decompress_kv(case, case_s)
+        assert np.array_equal(vs, oracle.bf16_decode(lat)[:, (3 * np.arange(256)) % case.K].astype(np.float64))
+    assert np.array_equal(k, k1) and np.array_equal(v, v1)
+    assert v.shape == (case.M, 256)
