@@ -7,14 +7,14 @@
 // 16 MiB at N = 16384) once from HBM, so the whole weight must be in flight at
 // once and the call must be one launch.  One block of 4 waves per 64 weight
 // rows (256 blocks at N = 16384, one per CU):
-//  * the rows' cache addresses are resolved first (one thread per request: its
-//    offsets, then the page-table entries of its rows), gathering form only;
-//  * then the block's 64 x 512 weight tile (64 KB) and the rows' first 512
-//    columns, 64 columns (128 bytes) per chunk, go straight into LDS (loads with
-//    an LDS destination: the weight as a buffer, the rows by per-lane
-//    addresses, 8 rows of 128 bytes per load).  All weight loads and as many row
-//    chunks as fit (all 8 for 64 rows, 3 for 256) are in flight together; the
-//    rest follow as chunks are consumed;
+//  * waves 1..3 put the block's 64 x 512 weight tile (64 KB) in flight first,
+//    while wave 0 resolves the rows' cache addresses (one lane per request:
+//    its offsets, then the page-table entries of its rows; gathering form);
+//  * then the rows' first 512 columns, 64 columns (128 bytes) per chunk, go
+//    straight into LDS (loads with an LDS destination: the weight as a buffer,
+//    the rows by per-lane addresses, 8 rows of 128 bytes per load).  As many
+//    row chunks as fit (all 8 for 64 rows, 3 for 256) are in flight together;
+//    the rest follow as chunks are consumed;
 //  * v_mfma_f32_32x32x16_bf16 with the weight as the row operand: wave w owns
 //    weight rows 32 (w % 2) .. +32 and the 32-row blocks w/2, w/2 + 2, ... of
 //    the M rows; outputs go straight to k_buffer (4 consecutive columns per
@@ -73,32 +73,37 @@ __global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a
     const int n0 = blockIdx.x * SBN;
     const int M = a.M;
 
-    // 1. Row addresses: the first columns of row r start at rowaddr[r]; rows
-    //    M .. ROWS-1 repeat row M-1 (loaded, never stored).
-    if (gather) {
-        for (uint32_t b = tid; b < a.L.batch; b += SNT) {
+    // 1. The weight tile does not depend on the rows: waves 1..3 put all of it
+    //    in flight first (row c is one 1 KB load; lane l fills physical granule
+    //    l, which holds logical granule l ^ (c % 16)), while wave 0 resolves the
+    //    rows.  Wave 0 issues none of these loads, so the waits the compiler
+    //    puts on its index loads do not wait for the weight.
+    const uint32_t wt_lds = lds_addr(wt), at_lds = lds_addr(at);
+    if (wave > 0) {
+        const i32x4 wr = make_srd(a.W, (uint32_t)((int64_t)a.N * SK * 2));
+        for (int c = wave - 1; c < SBN; c += 3)
+            asm_ld16_lds(wr, wt_lds + c * 1024, (uint32_t)((lane ^ (c & 15)) * 16), (uint32_t)((n0 + c) * SK * 2));
+    }
+
+    // 2. Row addresses (wave 0): the first columns of row r start at
+    //    rowaddr[r]; rows M .. ROWS-1 repeat row M-1 (loaded, never stored).
+    if (wave > 0) {
+    } else if (gather) {
+        for (uint32_t b = lane; b < a.L.batch; b += 64) {
             const uint32_t lo = a.bro[b], hi0 = a.bro[b + 1], c0 = a.co[b];
             const uint32_t hi = hi0 < (uint32_t)M ? hi0 : (uint32_t)M;
             for (uint32_t r = lo; r < hi; ++r)
                 rowaddr[r] = (uint64_t)(a.L.base + token_offset(a.L, b, c0 + (r - lo)));
         }
     } else {
-        for (int r = tid; r < M; r += SNT)
+        for (int r = lane; r < M; r += 64)
             rowaddr[r] = (uint64_t)(static_cast<const char*>(a.lat) + (int64_t)r * a.D * 2);
     }
-    __syncthreads();
+    lds_barrier();
     if (tid >= M && tid < C::ROWS)
         rowaddr[tid] = rowaddr[M - 1];
-    __syncthreads();
+    lds_barrier();
 
-    // 2. Weight tile: row c is one 1 KB load; lane l fills physical granule l,
-    //    which holds logical granule l ^ (c % 16).
-    const uint32_t wt_lds = lds_addr(wt), at_lds = lds_addr(at);
-    {
-        const i32x4 wr = make_srd(a.W, (uint32_t)((int64_t)a.N * SK * 2));
-        for (int c = wave * (SBN / 4); c < (wave + 1) * (SBN / 4); ++c)
-            asm_ld16_lds(wr, wt_lds + c * 1024, (uint32_t)((lane ^ (c & 15)) * 16), (uint32_t)((n0 + c) * SK * 2));
-    }
     // Row chunks: chunk q holds columns 64 q .. 64 q + 63 of every row, rows of
     // 128 bytes (8 granules XOR-swizzled by (row / 2) % 8).  A load covers 8
     // rows: lane l takes row 8 i + l / 8, physical granule l % 8.
@@ -109,7 +114,7 @@ __global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a
         const int r = (wave * LPC + i) * 8 + lrow;
         src_row[i] = reinterpret_cast<const char*>(rowaddr[r]) + (lpos ^ ((r >> 1) & 7)) * 16;
     }
-    __syncthreads();
+    lds_barrier();
     auto issue_chunk = [&](int q, int slot) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < LPC; ++i) {
