@@ -84,6 +84,8 @@ def _load():
         lib.or_kv_destinations.argtypes = [_i64, _i64, _i64, _i64, _u32, _u32, _u32, _p, _u32,
                                            _u32, _p, _p, _u32, _p]
         lib.or_kv_destinations.restype = _int
+        lib.or_latent_rows.argtypes = [_p, _i64, _i64, _i64, _p, ctypes.c_double, _p, _i64, _p, _p]
+        lib.or_latent_rows.restype = _int
         _lib = lib
         return lib
 
@@ -263,6 +265,31 @@ def kv_destinations(case) -> np.ndarray:
     if rc != 0:
         raise OracleError(f"kv destination precondition failed ({rc})")
     return dst
+
+
+def latent_write(case):
+    """(row values binary64 [T, D_c], element offsets int64 [T] of each token's
+    cache row): the latent write path (page "mla_prefill_decode_graph_fp8", Args
+    kv_input_fn, kv_norm_gamma, epsilon, freqs_cis, input_row_offsets): the
+    RMS-normalised latent part and the rotated rope part of each new token, and
+    where its row goes (the token placement of the write path, kv half 0)."""
+    T, D = case.x.shape
+    K, R = case.K, D - case.K
+    iro = np.asarray(case.input_row_offsets, np.int64)
+    cl = np.asarray(case.cache.cache_lengths, np.int64)
+    pos = np.empty(T, np.int64)
+    for b in range(len(iro) - 1):
+        pos[iro[b]:iro[b + 1]] = cl[b] + np.arange(iro[b + 1] - iro[b])
+    x = np.ascontiguousarray(case.x, np.uint16)
+    gamma = np.ascontiguousarray(case.gamma, np.float32)
+    freqs = np.ascontiguousarray(case.freqs, np.float32)
+    out = np.empty((T, D), np.float64)
+    if T:
+        rc = _load().or_latent_rows(_ptr(x), T, K, R, _ptr(gamma), float(case.eps), _ptr(freqs),
+                                    freqs.shape[0], _ptr(pos), _ptr(out))
+        if rc != 0:
+            raise OracleError(f"latent write precondition failed ({rc})")
+    return out, kv_destinations(case)[:, 0]
 
 
 def kv_matmul(case, rows=None):

@@ -345,3 +345,43 @@ int or_kv_destinations(int64_t stride_page, int64_t stride_layer, int64_t stride
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Latent write path ("mla_prefill_decode_graph_fp8", Args kv_input_fn,
+ * kv_norm_gamma, epsilon, freqs_cis).
+ *
+ * Row t of X (bf16, K latent then R rope columns) for position pos[t]:
+ *   out[t][k]      = gamma[k] * x[k] / sqrt(sum_{k<K} x[k]^2 / K + eps)     k < K
+ *   out[t][K+2j]   = x[K+2j] * c - x[K+2j+1] * s
+ *   out[t][K+2j+1] = x[K+2j] * s + x[K+2j+1] * c,  c = freqs[pos][2j], s = freqs[pos][2j+1]
+ * in binary64 (the caller rounds).  Returns 0, or -6 for a position at or past
+ * max_seq.
+ * ---------------------------------------------------------------------- */
+int or_latent_rows(const uint16_t* X, int64_t T, int64_t K, int64_t R, const float* gamma, double eps,
+                   const float* freqs, int64_t max_seq, const int64_t* pos, double* out)
+{
+    const int64_t D = K + R;
+    for (int64_t t = 0; t < T; ++t)
+        if (R > 0 && (pos[t] < 0 || pos[t] >= max_seq))
+            return -6;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t* x = X + t * D;
+        double* y = out + t * D;
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = bf16_to_float(x[k]);
+            ss += v * v;
+        }
+        double rms = sqrt(ss / (double)K + eps);
+        for (int64_t k = 0; k < K; ++k)
+            y[k] = (double)gamma[k] * (double)bf16_to_float(x[k]) / rms;
+        for (int64_t j = 0; 2 * j < R; ++j) {
+            double x0 = bf16_to_float(x[K + 2 * j]), x1 = bf16_to_float(x[K + 2 * j + 1]);
+            double c = freqs[pos[t] * R + 2 * j], s = freqs[pos[t] * R + 2 * j + 1];
+            y[K + 2 * j] = x0 * c - x1 * s;
+            y[K + 2 * j + 1] = x0 * s + x1 * c;
+        }
+    }
+    return 0;
+}

@@ -12,7 +12,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "mla_oracle.c")
 PINS = ["tests/test_oracle_codecs.py", "tests/test_oracle_gather.py",
-        "tests/test_oracle_products.py", "tests/test_oracle_kv.py"]
+        "tests/test_oracle_products.py", "tests/test_oracle_kv.py", "tests/test_oracle_latent_write.py"]
 
 MUTANTS = {
     "slot_uses_page_index": ("(p % P->page_size) * P->stride_token", "(p / P->page_size) * P->stride_token"),
@@ -34,6 +34,13 @@ MUTANTS = {
     "kv_position_not_relative": ("(int64_t)cache_lengths[b] + (t - (int64_t)input_row_offsets[b])",
                                  "(int64_t)cache_lengths[b] + t"),
     "nn_weight_transposed": ("bf16_to_float(W[k * ldw + n])", "bf16_to_float(W[n * ldw + k])"),
+    "rms_eps_dropped": ("sqrt(ss / (double)K + eps)", "sqrt(ss / (double)K)"),
+    "rms_mean_over_row": ("sqrt(ss / (double)K + eps)", "sqrt(ss / (double)D + eps)"),
+    "rope_sign": ("y[K + 2 * j] = x0 * c - x1 * s;", "y[K + 2 * j] = x0 * c + x1 * s;"),
+    "rope_pair_swapped": ("double c = freqs[pos[t] * R + 2 * j], s = freqs[pos[t] * R + 2 * j + 1];",
+                          "double s = freqs[pos[t] * R + 2 * j], c = freqs[pos[t] * R + 2 * j + 1];"),
+    "rope_row_of_token": ("double c = freqs[pos[t] * R + 2 * j], s = freqs[pos[t] * R + 2 * j + 1];",
+                          "double c = freqs[t * R + 2 * j], s = freqs[t * R + 2 * j + 1];"),
 }
 
 

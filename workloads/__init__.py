@@ -286,6 +286,66 @@ def kv_matmul_case(name, *, seed, seq_lens, start_lengths, hidden_dim, num_kv_he
 
 
 # --------------------------------------------------------------------------
+# latent write-path cases (RMSNorm + RoPE + scatter into the MLA pages)
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class LatentWriteCase:
+    name: str
+    cache: PagedCache               # num_kv == 1, bf16; cache_lengths = start positions
+    layer_idx: int
+    x: np.ndarray                   # uint16 bf16 bits [T, D_c]: latent K then rope R columns
+    input_row_offsets: np.ndarray   # uint32 [B+1]
+    gamma: np.ndarray               # float32 [K]
+    eps: float
+    freqs: np.ndarray               # float32 [max_seq_len, R]: (cos, sin) per rope pair
+    K: int
+
+    @property
+    def T(self) -> int: return int(self.input_row_offsets[-1])
+
+
+def rope_table(max_seq_len, R, base=10000.0):
+    """float32 [max_seq_len, R]: (cos, sin) of position p times base^(-2j/R) for
+    rope pair j, interleaved."""
+    j = np.arange(R // 2, dtype=np.float64)
+    ang = np.arange(max_seq_len, dtype=np.float64)[:, None] * base ** (-2.0 * j / R)[None, :]
+    out = np.empty((max_seq_len, R), np.float32)
+    out[:, 0::2] = np.cos(ang)
+    out[:, 1::2] = np.sin(ang)
+    return out
+
+
+def latent_write_case(name, *, seed, seq_lens, start_lengths, page_size, K=512, R=64, num_layers=2,
+                      layer_idx=1, eps=1e-6, max_seq_len=None) -> LatentWriteCase:
+    """New tokens (latent N(0,1), rope N(0,1), bf16) appended after each request's
+    cached ones in an MLA cache of rows K + R; RMSNorm weights U[0.5, 1.5]."""
+    rng = np.random.default_rng(seed)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    start_lengths = np.asarray(start_lengths, dtype=np.int64)
+    cache = make_paged_cache(rng, cache_lengths=start_lengths, page_size=page_size, num_heads=1,
+                             head_dim=K + R, dtype="bf16", num_kv=1, num_layers=num_layers,
+                             layer_idx=layer_idx, extra_tokens=seq_lens)
+    T = int(seq_lens.sum())
+    iro = np.zeros(len(seq_lens) + 1, dtype=np.uint32)
+    iro[1:] = np.cumsum(seq_lens)
+    x = to_bf16_bits(rng.standard_normal((T, K + R), dtype=np.float32))
+    gamma = rng.uniform(0.5, 1.5, size=K).astype(np.float32)
+    if max_seq_len is None:
+        max_seq_len = int((start_lengths + seq_lens).max()) + 1
+    return LatentWriteCase(name, cache, layer_idx, x, iro, gamma, float(eps), rope_table(max_seq_len, R), K)
+
+
+def c5_latent_write(seed=5) -> LatentWriteCase:
+    """The write-path batch shape of the kv projection (128 requests, lengths
+    lognormal(ln 512, 1) clipped to [1, 8192], fresh requests) writing 576-wide
+    latent rows (512 + 64 rope), page_size 128."""
+    rng = np.random.default_rng(seed + 1000)
+    lens = lognormal_lengths(rng, 128, 512, 1.0, 8192)
+    return latent_write_case("c5_latent_write", seed=seed, seq_lens=lens, start_lengths=np.zeros(128, np.int64),
+                             page_size=128)
+
+
+# --------------------------------------------------------------------------
 # the named workloads
 # --------------------------------------------------------------------------
 def c0_tiny(seed=0) -> DecompressCase:
@@ -407,6 +467,15 @@ def device_decompress(case: DecompressCase, device="cuda"):
         t["weight_scale"] = torch.from_numpy(case.weight_scale).to(device)
     else:
         t["weight"] = _bits_to_torch(case.weight, device)
+    return dc, t
+
+
+def device_latent_write(case: LatentWriteCase, device="cuda"):
+    dc = device_cache(case.cache, device)
+    t = {"x": _bits_to_torch(case.x, device),
+         "input_row_offsets": _u32_to_torch(case.input_row_offsets, device),
+         "gamma": torch.from_numpy(case.gamma).to(device),
+         "freqs": torch.from_numpy(case.freqs).to(device)}
     return dc, t
 
 
