@@ -15,6 +15,10 @@ The JSON line also carries the other rows of the path, each timed the same way:
   c2_prefill   bf16, 4 x 16384 rows, copies starting mid-cache
   c3_fp8       fp8 block-scaled form on the same shapes (quantise pass + product)
   c4_kv_matmul write path, 128 lognormal requests, hidden 4096 -> 2 x 8 x 128
+  c2_fused_kv  K and V decompression in one call, against two separate calls
+  c2_tp8_share one GPU's share of W_k when 8 GPUs split the heads (N = 2048)
+  c5_latent_write  RMSNorm + rope rotation + scatter of 88994 new tokens'
+               rows into the MLA pages (HBM-bound)
   p64, p256    1 and 4 newest rows per request of the decode batch (weight-bound;
                timed by HIP-graph replay over 32 weight copies, see probe_row)
 
@@ -48,6 +52,7 @@ KERNEL_SOURCES = {
     "gemm_fp8_ring": ("decompress_fp8_ring.hip", "decompress_fp8.hip", "bf16_tile_common.hpp"),
     "kv_matmul_ring": ("kv_matmul_ring.hip", "kv_matmul.hip", "bf16_tile_common.hpp"),
     "decompress_small_bf16": ("decompress_small.hip",),
+    "latent_write_kernel": ("latent_write.hip",),
 }
 
 
@@ -411,6 +416,27 @@ def main():
                                                      traffic_from_profile("kv_matmul_ring", "c4_kv_matmul")),
                                 "kernel": "kv_matmul_ring"}
         print(f"[bench] c4_kv_matmul: {t.avg_launch_ms:.3f} ms, {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        del dc, tt, cache
+        torch.cuda.empty_cache()
+        # the latent write path (RMSNorm + rope rotation + scatter into the MLA pages)
+        lc = W.c5_latent_write()
+        ldc, lt = W.device_latent_write(lc)
+        lcache = mp.PagedKVCache(ldc.pool, ldc.page_table, ldc.cache_lengths)
+
+        def lw_fn():
+            mp.mla_write_latent_paged(lt["x"], lt["input_row_offsets"], lt["gamma"], lc.eps, lt["freqs"], lc.K,
+                                      lcache, lc.layer_idx)
+        t = Timed(torch, lw_fn, steps, args.warmup)
+        D = lc.x.shape[1]
+        b = lc.T * (D * 2 * 2 + (D - lc.K) * 4) + lc.K * 4
+        gbs = b / (t.avg_launch_ms * 1e-3) / 1e9
+        rows["c5_latent_write"] = {"tokens": lc.T, "ms": round(t.avg_launch_ms, 4), "hbm_gbs_algorithmic": round(gbs, 1),
+                                   "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s",
+                                                        traffic_from_profile("latent_write_kernel", "c5_latent_write")),
+                                   "kernel": "latent_write_kernel",
+                                   "note": "per token: read the 1152-byte row and its 256-byte rope table row, "
+                                           "write the 1152-byte cache row"}
+        print(f"[bench] c5_latent_write: {t.avg_launch_ms:.4f} ms, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
         result["rows"] = rows
 
     if args.cpu_seconds > 0:

@@ -266,6 +266,40 @@ mla_status_t mla_decompress_kv_paged_fp8(const uint32_t* buffer_row_offsets,
                                          void* stream);
 
 /*
+ * The latent write path: new tokens' latent rows, normalised and rotated, into
+ * the MLA cache pages this library's decompress calls read (page
+ * "mla_prefill_decode_graph_fp8", Args kv_input_fn (the latent values,
+ * [tot_seq_len, cache_head_dim] with cache_head_dim = kv_lora_rank +
+ * qk_rope_head_dim), kv_norm_gamma [kv_lora_rank], epsilon, freqs_cis
+ * [max_seq_len, qk_rope_head_dim], input_row_offsets, kv_collection, layer_idx).
+ *
+ *   Token t of request b (input_row_offsets[b] <= t < input_row_offsets[b+1]) is
+ *   written at position p = cache_lengths[b] + (t - input_row_offsets[b]):
+ *     row[k]       = bf16( gamma[k] * x[k] / sqrt(mean_{k<K} x[k]^2 + epsilon) ),  k < K
+ *     row[K+2j]    = bf16( x[K+2j] * c - x[K+2j+1] * s )
+ *     row[K+2j+1]  = bf16( x[K+2j] * s + x[K+2j+1] * c ),  (c, s) = freqs_cis[p][2j], [2j+1]
+ *   with x = kv_input[t], fp32 arithmetic, round to nearest even; stored as the
+ *   cache row of (page_table[b][p / page_size], slot p % page_size) in layer
+ *   layer_idx.  Other cache bytes are not touched; cache_lengths is not updated.
+ *
+ * kv_input         [device] bf16 [total_tokens][D_c], D_c = num_heads*head_dim = K + R
+ * input_row_offsets [device] uint32 [batch_size+1], [0] = 0, nondecreasing
+ * total_tokens     [host] input_row_offsets[batch_size]
+ * kv_norm_gamma    [device] float [K], 16-byte aligned
+ * epsilon          >= 0
+ * freqs_cis        [device] float [max_seq_len][R], (cos, sin) of each rope pair;
+ *                  may be NULL when R == 0; positions must be < max_seq_len
+ * K                kv_lora_rank: K % 8 == 0, K <= 512; R = D_c - K: R % 8 == 0, R <= 512
+ * cache            [host] num_kv == 1, BF16, cache_lengths set; pages are WRITTEN
+ * Errors and validation order as for the other calls (pointers, shapes, dtype,
+ * alignment, ranges, device).
+ */
+mla_status_t mla_write_latent_paged(const void* kv_input, const uint32_t* input_row_offsets,
+                                    int32_t total_tokens, const float* kv_norm_gamma, float epsilon,
+                                    const float* freqs_cis, int32_t max_seq_len, int32_t K,
+                                    const mla_paged_cache_t* cache, uint32_t layer_idx, void* stream);
+
+/*
  * Project hidden states and write them into the paged K/V cache (page
  * "kv_matmul_ragged_paged", summary and Args).
  *

@@ -31,7 +31,8 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_NULL_POINTER", 2: "MLA_ERR_INVALID_SHAPE",
 EXPORTS = ("mla_paged_cache_default_strides", "mla_decompress_k_paged", "mla_gather_latent_paged",
            "mla_latent_matmul", "mla_decompress_k_paged_fp8_workspace_size", "mla_decompress_k_paged_fp8",
            "kv_matmul_paged", "mla_check_indices", "mla_status_string", "mla_last_hip_error",
-           "mla_abi_version", "mla_decompress_kv_paged", "mla_decompress_kv_paged_fp8")
+           "mla_abi_version", "mla_decompress_kv_paged", "mla_decompress_kv_paged_fp8",
+           "mla_write_latent_paged")
 
 
 class MlaError(RuntimeError):
@@ -84,6 +85,9 @@ def lib():
             L.mla_decompress_kv_paged_fp8.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                                       ctypes.POINTER(CacheDesc), u32, vp, vp, vp, vp, sz, vp]
             L.mla_decompress_kv_paged_fp8.restype = i32
+            L.mla_write_latent_paged.argtypes = [vp, vp, i32, vp, ctypes.c_float, vp, i32, i32,
+                                                 ctypes.POINTER(CacheDesc), u32, vp]
+            L.mla_write_latent_paged.restype = i32
             L.kv_matmul_paged.argtypes = [vp, vp, i32, i32, vp, ctypes.POINTER(CacheDesc), u32, vp]
             L.kv_matmul_paged.restype = i32
             L.mla_gather_latent_paged.argtypes = [vp, vp, i32, ctypes.POINTER(CacheDesc), u32, vp, vp]
@@ -316,6 +320,24 @@ def mla_decompress_kv_paged_fp8(buffer_row_offsets, cache_offsets, buffer_length
                                            workspace.data_ptr() if workspace is not None else None,
                                            ws_bytes, _stream(stream))
     _check(st, "mla_decompress_kv_paged_fp8")
+
+
+def mla_write_latent_paged(kv_input, input_row_offsets, kv_norm_gamma, epsilon: float, freqs_cis, K: int,
+                           cache: PagedKVCache, layer_idx: int, stream=None) -> None:
+    """Append new tokens' rows (RMSNorm of the first K columns with kv_norm_gamma,
+    the rest rotated by freqs_cis at each token's position) into the cache pages."""
+    if kv_input.dim() != 2 or not kv_input.is_contiguous():
+        raise ValueError("kv_input must be a contiguous [T, D_c] tensor")
+    T = kv_input.shape[0]
+    desc = cache.descriptor()
+    if kv_input.shape[1] != desc.num_heads * desc.head_dim:
+        raise ValueError("kv_input rows must be as wide as the cache rows")
+    max_seq = freqs_cis.shape[0] if freqs_cis is not None else 0
+    st = lib().mla_write_latent_paged(kv_input.data_ptr(), _u32(input_row_offsets, "input_row_offsets"), T,
+                                      kv_norm_gamma.data_ptr(), float(epsilon),
+                                      freqs_cis.data_ptr() if freqs_cis is not None else None, int(max_seq),
+                                      int(K), ctypes.byref(desc), int(layer_idx), _stream(stream))
+    _check(st, "mla_write_latent_paged")
 
 
 def kv_matmul_paged(hidden_state, input_row_offsets, weight, cache: PagedKVCache, layer_idx: int,

@@ -431,6 +431,54 @@ MLA_API mla_status_t mla_decompress_kv_paged_fp8(const uint32_t* buffer_row_offs
     return e == hipSuccess ? MLA_OK : hip_failed(e);
 }
 
+MLA_API mla_status_t mla_write_latent_paged(const void* kv_input, const uint32_t* input_row_offsets,
+                                            int32_t total_tokens, const float* kv_norm_gamma, float epsilon,
+                                            const float* freqs_cis, int32_t max_seq_len, int32_t K,
+                                            const mla_paged_cache_t* cache, uint32_t layer_idx, void* stream)
+{
+    if (!cache)
+        return MLA_ERR_NULL_POINTER;
+    const bool work = total_tokens > 0;
+    const int64_t D = (int64_t)cache->num_heads * cache->head_dim;
+    const int64_t R = D - K;   // rope columns after the K latent ones
+    if (work && (!kv_input || !input_row_offsets || !kv_norm_gamma || !cache->blocks || !cache->page_table ||
+                 !cache->cache_lengths || (R > 0 && !freqs_cis)))
+        return MLA_ERR_NULL_POINTER;
+    if (total_tokens < 0 || K <= 0 || K % 8 || K > 512 || R < 0 || R % 8 || R > 512 || (R > 0 && max_seq_len <= 0) ||
+        !(epsilon >= 0.0f))
+        return MLA_ERR_INVALID_SHAPE;
+    if (mla_status_t st = check_cache_shape(cache, 1))
+        return st;
+    if (cache->dtype != MLA_DTYPE_BF16)
+        return MLA_ERR_INVALID_DTYPE;
+    if (!aligned16(kv_input) || !aligned16(kv_norm_gamma) || !aligned16(freqs_cis))
+        return MLA_ERR_MISALIGNED;
+    if (mla_status_t st = check_cache_alignment(cache))
+        return st;
+    if (layer_idx >= cache->num_layers)
+        return MLA_ERR_OUT_OF_RANGE;
+    if (!work)
+        return MLA_OK;
+    if (mla_status_t st = check_device())
+        return st;
+
+    mla::LatentWriteArgs a{};
+    a.X = static_cast<const uint16_t*>(kv_input);
+    a.iro = input_row_offsets;
+    a.cache_len = cache->cache_lengths;
+    a.gamma = kv_norm_gamma;
+    a.freqs = freqs_cis;
+    a.eps = epsilon;
+    a.L = layer_view(cache, layer_idx);
+    a.T = total_tokens;
+    a.K = K;
+    a.R = (int)R;
+    a.D = (int)D;
+    a.max_seq = R > 0 ? max_seq_len : 1;
+    const hipError_t e = mla::launch_latent_write(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MLA_OK : hip_failed(e);
+}
+
 MLA_API mla_status_t kv_matmul_paged(const void* hidden_state, const uint32_t* input_row_offsets,
                                      int32_t total_tokens, int32_t hidden_dim, const void* weight,
                                      const mla_paged_cache_t* cache, uint32_t layer_idx, void* stream)

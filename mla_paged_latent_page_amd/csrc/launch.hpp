@@ -38,7 +38,19 @@ struct KvMatmulArgs {
     int T, Kd, N, HD;          // N = 2*HD
 };
 
+struct LatentWriteArgs {
+    const uint16_t* X;         // new tokens' rows, bf16 [T][D] (latent K, then rope R)
+    const uint32_t* iro;       // input_row_offsets [batch+1]
+    const uint32_t* cache_len; // [batch] positions already cached
+    const float* gamma;        // RMSNorm weights [K]
+    const float* freqs;        // [max_seq][R]: (cos, sin) pairs per position
+    float eps;
+    PagedLayer L;              // layer view of the latent pool
+    int T, K, R, D, max_seq;
+};
+
 hipError_t launch_gather_rows(const DecompressArgs& a, int elem_bytes, hipStream_t s);
+hipError_t launch_latent_write(const LatentWriteArgs& a, hipStream_t s);
 hipError_t launch_product_bf16(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_product_f32(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_decompress_bf16(const DecompressArgs& a, hipStream_t s);

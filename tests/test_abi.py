@@ -264,3 +264,31 @@ def test_decompress_kv_fp8_error_paths(lib):
     assert fp8_kv(lib, d, ws_bytes=1000) == WS
     assert fp8_kv(lib, d, M=0, ws_bytes=0) == OK
     assert fp8_kv(lib, d) == DEV
+
+
+def write_latent(lib, d, T=50, K=512, max_seq=4096, eps=1e-6, layer=1, **ptrs):
+    p = dict(x=FAKE, iro=FAKE, g=FAKE, f=FAKE)
+    p.update(ptrs)
+    return lib.mla_write_latent_paged(p["x"], p["iro"], T, p["g"], eps, p["f"], max_seq, K,
+                                      ctypes.byref(d) if d is not None else None, layer, None)
+
+
+def test_write_latent_error_paths(lib):
+    d = cache_desc(with_lengths=True)
+    assert write_latent(lib, None) == NULLP
+    for k in ("x", "iro", "g", "f"):
+        assert write_latent(lib, d, **{k: None}) == NULLP
+    assert write_latent(lib, cache_desc()) == NULLP                   # no cache_lengths
+    assert write_latent(lib, cache_desc(head_dim=512, with_lengths=True), f=None) == DEV   # no rope part: no freqs needed
+    assert write_latent(lib, d, T=-1) == SHAPE
+    assert write_latent(lib, d, K=500) == SHAPE                       # K % 8
+    assert write_latent(lib, d, K=1024) == SHAPE                      # K > 512 and R < 0
+    assert write_latent(lib, d, max_seq=0) == SHAPE
+    assert write_latent(lib, d, eps=-1.0) == SHAPE
+    assert write_latent(lib, cache_desc(num_kv=2, with_lengths=True)) == SHAPE
+    assert write_latent(lib, cache_desc(dtype=0, with_lengths=True)) == DTYPE
+    assert write_latent(lib, d, x=FAKE + 8) == MISAL
+    assert write_latent(lib, d, g=FAKE + 4) == MISAL
+    assert write_latent(lib, d, layer=2) == RANGE
+    assert write_latent(lib, d, T=0, x=None, iro=None, g=None, f=None) == OK
+    assert write_latent(lib, d) == DEV
