@@ -145,6 +145,32 @@ def gather(case, *, check_lengths: bool = True) -> np.ndarray:
     return out
 
 
+def gather_scales(case, *, check_lengths: bool = True) -> np.ndarray:
+    """The scales that go with the gathered rows of an e4m3 cache, float32
+    [M, blocks per row]: the same copy as ``gather`` (same requests, positions,
+    pages and slots) applied to the cache's scale pool, whose token rows hold one
+    fp32 scale per ``scale_gran`` columns (page "generic_flare_mla_decompress_k_cache_ragged_paged",
+    the collection's ``scale_dtype_`` and ``quantization_granularity_``)."""
+    c = case.cache
+    if c.scales is None:
+        raise OracleError("the cache has no scales")
+    sp, sl, skv, st = c.scale_strides()
+    M, nb = case.M, c.scale_blocks
+    out = np.empty((M, nb), dtype=np.float32)
+    pt = np.ascontiguousarray(c.page_table, np.uint32)
+    cl = np.ascontiguousarray(c.cache_lengths, np.uint32)
+    bro = np.ascontiguousarray(case.buffer_row_offsets, np.uint32)
+    co = np.ascontiguousarray(case.cache_offsets, np.uint32)
+    sc = np.ascontiguousarray(c.scales)
+    rc = _load().or_gather(_ptr(sc), 4, sp, sl, st, c.num_pages, c.num_layers,
+                           c.page_size, _ptr(pt), c.max_pages_per_seq, case.batch,
+                           _ptr(cl) if check_lengths else None, _ptr(bro), _ptr(co), M,
+                           case.layer_idx, nb, _ptr(out) if out.size else None)
+    if rc != 0:
+        raise OracleError(f"scale gather precondition failed ({rc})")
+    return out
+
+
 # ---------------------------------------------------------------------------
 # products
 # ---------------------------------------------------------------------------
@@ -229,6 +255,26 @@ def decompress_k_fp8(case, rows=None):
     q, s = quantize_e4m3_rows(lat, case.K, case.k_gran)
     out = fp8_matmul_nt(q, s, case.weight_q, case.weight_scale, case.n_gran, case.k_gran, rows)
     return lat, q, s, out
+
+
+def decompress_k_fp8_cache(case, rows=None):
+    """(k_latent codes uint8 [M, D_c], their scales float32 [M, blocks per row],
+    k_buffer rows binary64) for an e4m3 cache and an e4m3 W_k.
+
+    The gathered codes and scales are bit copies of the cache's; the product is
+    the block-scaled one of the fp8 form (page "mla_prefill_decode_graph_fp8",
+    Parameters m/n/k_scale_granularity, Args w_k, w_k_scale) on the first K
+    columns, with the cache's own per-128-column scales as the activation scales:
+    no quantisation step, the cache is already quantised."""
+    c = case.cache
+    if c.dtype != "e4m3" or c.scale_gran != case.k_gran:
+        raise OracleError("an e4m3 cache with one scale per k_gran columns is required")
+    codes = gather(case)
+    scales = gather_scales(case)
+    kb = -(-case.K // case.k_gran)
+    out = fp8_matmul_nt(codes[:, :case.K], scales[:, :kb], case.weight_q, case.weight_scale,
+                        case.n_gran, case.k_gran, rows)
+    return codes, scales, out
 
 
 def decompress_kv(case_k, case_v, rows=None):

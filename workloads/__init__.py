@@ -31,6 +31,7 @@ import torch
 PAGE_NONE = 0xFFFFFFFF
 POISON_BF16 = np.uint16(0x7FC1)       # a quiet NaN in bfloat16
 POISON_F32_BITS = np.uint32(0x7FC00001)  # a quiet NaN in binary32
+POISON_E4M3 = np.uint8(0x7F)          # NaN in e4m3fn
 
 
 # --------------------------------------------------------------------------
@@ -55,14 +56,19 @@ def to_e4m3_bits(x: np.ndarray) -> np.ndarray:
 class PagedCache:
     """A paged KV pool plus the page table of one batch of requests.
 
-    ``pool`` holds raw element bits: uint16 for bf16, uint32 for f32.
-    Shape ``[num_pages, num_layers, num_kv, page_size, num_heads, head_dim]``.
+    ``pool`` holds raw element bits: uint16 for bf16, uint32 for f32, uint8
+    codes for e4m3.  Shape ``[num_pages, num_layers, num_kv, page_size,
+    num_heads, head_dim]``.  An e4m3 pool comes with ``scales``, float32
+    ``[num_pages, num_layers, num_kv, page_size, ceil(row / scale_gran)]``:
+    element j of a token's scales covers row columns [j*scale_gran, (j+1)*scale_gran).
     """
     pool: np.ndarray
-    dtype: str                   # "bf16" | "f32"
+    dtype: str                   # "bf16" | "f32" | "e4m3"
     page_table: np.ndarray       # uint32 [batch, max_pages_per_seq]
     cache_lengths: np.ndarray    # uint32 [batch] tokens already cached per request
     used_pages: int
+    scales: Optional[np.ndarray] = None
+    scale_gran: int = 128
 
     @property
     def num_pages(self) -> int: return self.pool.shape[0]
@@ -90,6 +96,14 @@ class PagedCache:
     @property
     def elem_bytes(self) -> int: return self.pool.itemsize
 
+    def scale_strides(self):
+        """Element strides (page, layer, kv, token) of the scale pool."""
+        s = self.scales.strides
+        return s[0] // 4, s[1] // 4, s[2] // 4, s[3] // 4
+
+    @property
+    def scale_blocks(self) -> int: return self.scales.shape[4]
+
 
 def _allocate_pages(rng, pages_needed, spare_frac):
     used = int(sum(pages_needed))
@@ -108,7 +122,7 @@ def _allocate_pages(rng, pages_needed, spare_frac):
 def make_paged_cache(rng, *, cache_lengths, page_size, num_heads, head_dim,
                      dtype="bf16", num_kv=1, num_layers=2, layer_idx=1,
                      value_std=1.0, spare_frac=0.1, fill="normal",
-                     extra_tokens=None) -> PagedCache:
+                     extra_tokens=None, scale_gran=128) -> PagedCache:
     """Build a poisoned pool whose referenced pages hold N(0, value_std) values.
 
     ``extra_tokens[b]`` reserves room for tokens to be appended after the cached
@@ -116,6 +130,13 @@ def make_paged_cache(rng, *, cache_lengths, page_size, num_heads, head_dim,
     ``fill="tag"`` (f32 only) writes into every element the tag
     ``page<<20 | layer<<19 | kv<<18 | slot<<10 | col`` as raw binary32 bits, so a
     gathered element names where it came from.
+
+    ``dtype="e4m3"``: codes e4m3fn(clip(100 * N(0, 1), -448, 448)) with one fp32
+    scale U[0.008, 0.012] per ``scale_gran`` columns of each token row (so the
+    stored values are about N(0, 1)); poison is code 0x7F and scale NaN.  With
+    ``fill="tag"`` the scale of block j of (page, layer, kv, slot) is the exact
+    float ``page*65536 + layer*32768 + kv*16384 + slot*64 + j`` and code c of
+    column i is ``(i + 3*slot + 5*page) % 126`` (a finite positive code).
     """
     cache_lengths = np.asarray(cache_lengths, dtype=np.int64)
     extra = np.zeros_like(cache_lengths) if extra_tokens is None else np.asarray(extra_tokens, np.int64)
@@ -128,6 +149,8 @@ def make_paged_cache(rng, *, cache_lengths, page_size, num_heads, head_dim,
         pool = np.full(shape, POISON_BF16, dtype=np.uint16)
     elif dtype == "f32":
         pool = np.full(shape, POISON_F32_BITS, dtype=np.uint32)
+    elif dtype == "e4m3":
+        return _make_e4m3_cache(rng, shape, table, cache_lengths, pages_needed, used, layer_idx, fill, scale_gran)
     else:
         raise ValueError(dtype)
 
@@ -159,6 +182,40 @@ def make_paged_cache(rng, *, cache_lengths, page_size, num_heads, head_dim,
             pool[ids[p // page_size], layer_idx, :, p % page_size] = (
                 POISON_BF16 if dtype == "bf16" else POISON_F32_BITS)
     return PagedCache(pool, dtype, table, cache_lengths.astype(np.uint32), used)
+
+
+def _make_e4m3_cache(rng, shape, table, cache_lengths, pages_needed, used, layer_idx, fill, gran):
+    num_pages, num_layers, num_kv, page_size, num_heads, head_dim = shape
+    row = num_heads * head_dim
+    nblk = -(-row // gran)
+    pool = np.full(shape, POISON_E4M3, dtype=np.uint8)
+    sbits = np.full((num_pages, num_layers, num_kv, page_size, nblk), POISON_F32_BITS, dtype=np.uint32)
+    scales = sbits.view(np.float32)
+    if fill == "tag":
+        assert num_pages <= 256 and page_size <= 256 and nblk <= 64
+        pg = np.arange(num_pages)[:, None, None, None, None]
+        ly = np.arange(num_layers)[None, :, None, None, None]
+        kv = np.arange(num_kv)[None, None, :, None, None]
+        sl = np.arange(page_size)[None, None, None, :, None]
+        j = np.arange(nblk)[None, None, None, None, :]
+        scales[...] = (pg * 65536 + ly * 32768 + kv * 16384 + sl * 64 + j).astype(np.float32)
+        col = np.arange(row)[None, None, None, None, :]
+        codes = (col + 3 * sl + 5 * pg) % 126 + 0 * ly + 0 * kv
+        pool[...] = codes.astype(np.uint8).reshape(shape)
+        return PagedCache(pool, "e4m3", table, cache_lengths.astype(np.uint32), used, scales, gran)
+    for b, n in enumerate(pages_needed):
+        if n == 0:
+            continue
+        ids = table[b, :n].astype(np.int64)
+        vals = np.clip(rng.standard_normal((n, num_kv, page_size, row), dtype=np.float32) * np.float32(100.0),
+                       -448.0, 448.0)
+        pool[ids, layer_idx] = to_e4m3_bits(vals).reshape(n, num_kv, page_size, num_heads, head_dim)
+        scales[ids, layer_idx] = rng.uniform(0.008, 0.012, size=(n, num_kv, page_size, nblk)).astype(np.float32)
+        tail = int(cache_lengths[b])
+        for p in range(tail, n * page_size):
+            pool[ids[p // page_size], layer_idx, :, p % page_size] = POISON_E4M3
+            sbits[ids[p // page_size], layer_idx, :, p % page_size] = POISON_F32_BITS
+    return PagedCache(pool, "e4m3", table, cache_lengths.astype(np.uint32), used, scales, gran)
 
 
 # --------------------------------------------------------------------------
@@ -211,7 +268,7 @@ def decompress_case(name, *, seed, cache_lengths, cache_offsets, page_size,
     case = DecompressCase(name, cache, layer_idx, bro, cache_offsets.astype(np.uint32),
                           kv_lora_rank, N, None, dtype)
     if fp8:
-        assert dtype == "bf16"
+        assert dtype in ("bf16", "e4m3")
         payload = rng.standard_normal((N, kv_lora_rank), dtype=np.float32)
         case.weight_q = to_e4m3_bits(payload)
         nb, kb = -(-N // 128), -(-kv_lora_rank // 128)
@@ -381,6 +438,16 @@ def c3_fp8(seed=3) -> DecompressCase:
     return c2_prefill(seed=seed, fp8=True, name="c3_fp8")
 
 
+def c6_fp8_cache(seed=6) -> DecompressCase:
+    """The 64K-row prefill shapes read from an e4m3 cache (codes with one fp32
+    scale per 128 columns of each 576-wide row, values about N(0, 1)) with an
+    e4m3fn W_k (payload N(0,1), 128x128 scales U[0.015, 0.025])."""
+    rng = np.random.default_rng(seed + 1000)
+    offs = rng.integers(0, 8192, size=4, endpoint=True)
+    return decompress_case("c6_fp8_cache", seed=seed, cache_lengths=offs + 16384, cache_offsets=offs,
+                           page_size=128, kv_lora_rank=512, rope_dim=64, N=16384, dtype="e4m3", fp8=True)
+
+
 def c4_kv_matmul(seed=4, start="zero") -> KvMatmulCase:
     """128 requests of lognormal lengths (median 512, sigma 1, clipped to
     [1, 8192]); hidden [T, 4096] bf16 N(0,1); W [4096, 2*8*128] bf16 N(0,0.02);
@@ -450,11 +517,15 @@ class DeviceCache:
     pool: "torch.Tensor"
     page_table: "torch.Tensor"
     cache_lengths: "torch.Tensor"
+    scales: Optional["torch.Tensor"] = None
 
 
 def device_cache(cache: PagedCache, device="cuda") -> DeviceCache:
+    sc = None
+    if cache.scales is not None:
+        sc = torch.from_numpy(np.ascontiguousarray(cache.scales)).to(device)
     return DeviceCache(_bits_to_torch(cache.pool, device), _u32_to_torch(cache.page_table, device),
-                       _u32_to_torch(cache.cache_lengths, device))
+                       _u32_to_torch(cache.cache_lengths, device), sc)
 
 
 def device_decompress(case: DecompressCase, device="cuda"):
