@@ -14,6 +14,7 @@ gather step is timed the same way through mla_gather_latent_paged.
 The JSON line also carries the other rows of the path, each timed the same way:
   c2_prefill   bf16, 4 x 16384 rows, copies starting mid-cache
   c3_fp8       fp8 block-scaled form on the same shapes (quantise pass + product)
+  c6_fp8_cache the same shapes read from an e4m3 cache with per-128-column scales
   c4_kv_matmul write path, 128 lognormal requests, hidden 4096 -> 2 x 8 x 128
   c2_fused_kv  K and V decompression in one call, against two separate calls
   c2_tp8_share one GPU's share of W_k when 8 GPUs split the heads (N = 2048)
@@ -364,6 +365,34 @@ def main():
             rows[name] = entry
             print(f"[bench] {name}: {t.avg_launch_ms:.3f} ms, {tf:.1f} TFLOP/s, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
             torch.cuda.empty_cache()
+        # the prefill batch read from an e4m3 cache with per-128-column scales
+        c = W.c6_fp8_cache()
+        dc, tt = W.device_decompress(c)
+        nblk = c.cache.scale_blocks
+        f8lat = torch.empty((c.M, c.D_c), dtype=torch.uint8, device="cuda")
+        f8sc = torch.empty((c.M, nblk), dtype=torch.float32, device="cuda")
+        f8out = torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda")
+        f8cache = mp.PagedKVCache(dc.pool, dc.page_table, dc.cache_lengths, scales=dc.scales)
+
+        def f8_fn():
+            mp.mla_decompress_k_paged_fp8_cache(tt["buffer_row_offsets"], tt["cache_offsets"], c.M, tt["weight_q"],
+                                                tt["weight_scale"], f8cache, c.layer_idx, f8lat, f8sc, f8out)
+        t = Timed(torch, f8_fn, steps, args.warmup)
+        f = 2.0 * c.M * c.N * c.K
+        b = c.M * (2 * (c.D_c + nblk * 4) + c.N * 2) + c.N * c.K + c.weight_scale.nbytes
+        tf = f / (t.avg_launch_ms * 1e-3) / 1e12
+        gbs = b / (t.avg_launch_ms * 1e-3) / 1e9
+        rows["c6_fp8_cache"] = {"rows": c.M, "ms": round(t.avg_launch_ms, 4),
+                                "rows_per_s": round(c.M / (t.avg_launch_ms * 1e-3), 1), "tflops": round(tf, 2),
+                                "hbm_gbs_algorithmic": round(gbs, 1), "fp8_mfma_frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                                "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s",
+                                                     traffic_from_profile("gemm_fp8_ring", "c6_fp8_cache")),
+                                "note": "time per call: gather of e4m3 rows and their scales (gather_rows_kernel) "
+                                        "+ fp8 product on them (gemm_fp8_ring); no quantisation pass"}
+        print(f"[bench] c6_fp8_cache: {t.avg_launch_ms:.3f} ms, {tf:.1f} TFLOP/s, {gbs:.0f} GB/s", file=sys.stderr,
+              flush=True)
+        del f8_fn, f8lat, f8sc, f8out, f8cache, dc, tt
+        torch.cuda.empty_cache()
         # fused K and V on the prefill batch (W_uv drawn like W_k), against the
         # same work as a K call followed by a V product on the gathered rows
         c = W.c2_prefill()

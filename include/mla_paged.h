@@ -75,7 +75,8 @@ typedef enum {
  */
 typedef struct {
     void* blocks;                   /* [device] pool base; 16-byte aligned */
-    int32_t dtype;                  /* mla_dtype_t of the pool: F32 or BF16 */
+    int32_t dtype;                  /* mla_dtype_t of the pool: F32 or BF16 (F8E4M3FN with
+                                       scales, mla_decompress_k_paged_fp8_cache only) */
     uint32_t num_layers;
     uint32_t num_pages;
     uint32_t page_size;             /* tokens per page, >= 1 */
@@ -97,6 +98,25 @@ typedef struct {
 /* [host] Fill the four strides for a contiguous pool laid out
  * [page][layer][kv][slot][head][dim].  Returns MLA_ERR_NULL_POINTER or MLA_OK. */
 mla_status_t mla_paged_cache_default_strides(mla_paged_cache_t* cache);
+
+/*
+ * The scales of an fp8 (F8E4M3FN) pool (the collection's scale_dtype_ = fp32 and
+ * quantization_granularity_ of page "generic_flare_mla_decompress_k_cache_ragged_paged",
+ * signature): every token row of num_heads*head_dim codes has
+ * nblk = ceil(num_heads*head_dim / granularity) fp32 scales; scale j multiplies the
+ * codes of columns [j*granularity, (j+1)*granularity).  The scales of (page, layer,
+ * kv, slot) start at
+ *   scales + page*stride_page + layer*stride_layer + kv*stride_kv + slot*stride_token
+ * (strides in floats) and are contiguous.  The same page table addresses both pools.
+ */
+typedef struct {
+    const float* scales;            /* [device] scale pool; 4-byte aligned */
+    uint32_t granularity;           /* columns per scale; supported: 128 */
+    int64_t stride_page;            /* floats */
+    int64_t stride_layer;
+    int64_t stride_kv;
+    int64_t stride_token;           /* >= nblk */
+} mla_cache_scales_t;
 
 /*
  * Gather each request's latent rows from the paged cache, then up-project them
@@ -264,6 +284,44 @@ mla_status_t mla_decompress_kv_paged_fp8(const uint32_t* buffer_row_offsets,
                                          void* k_latent_buffer, void* k_buffer, void* v_buffer,
                                          void* workspace, size_t workspace_bytes,
                                          void* stream);
+
+/*
+ * The decompress call on an fp8 paged cache (page
+ * "generic_flare_mla_decompress_k_cache_ragged_paged", summary and Args, with a
+ * collection whose scale_dtype_ / quantization_granularity_ are fp32 / 128; the
+ * weight and its block scales as page "mla_prefill_decode_graph_fp8", Args w_k,
+ * w_k_scale, granularities 1 x 128 x 128).
+ *
+ *   For request b, i < rows_b, r = buffer_row_offsets[b] + i, p = cache_offsets[b] + i:
+ *     k_latent_buffer[r][0:D_c]  = e4m3 codes of token p of request b (a bit copy)
+ *     k_latent_scales[r][0:nblk] = that token's fp32 scales (a bit copy)
+ *     k_buffer[r][n] = bf16( sum_kb k_latent_scales[r][kb] * weight_scale[n/128][kb]
+ *                              * sum_{k in block kb} k_latent_buffer[r][k] * weight[n][k] )
+ *   over the K/128 blocks of the first K columns, fp32 accumulation, round to
+ *   nearest even.  The cache is already quantised: no quantisation step, no workspace.
+ *
+ * weight_e4m3      [device] [N][K] e4m3fn codes, 16-byte aligned
+ * weight_scale     [device] float [N/128][K/128], 4-byte aligned
+ * N, K             N % 128 == 0, K % 128 == 0, K <= D_c
+ * cache            [host] dtype F8E4M3FN, num_kv == 1, D_c % 16 == 0, byte strides
+ *                  multiples of 16
+ * cache_scales     [host] granularity 128, stride_token >= nblk = ceil(D_c / 128)
+ * k_latent_buffer  [device] uint8 [>= M][D_c], 16-byte aligned, written
+ * k_latent_scales  [device] float [>= M][nblk], 4-byte aligned, written
+ * k_buffer         [device] bf16 [>= M][N], 16-byte aligned, written
+ * M * D_c < 2^31.  Other arguments, errors and validation order as in
+ * mla_decompress_k_paged.
+ */
+mla_status_t mla_decompress_k_paged_fp8_cache(const uint32_t* buffer_row_offsets,
+                                              const uint32_t* cache_offsets,
+                                              int32_t buffer_length,
+                                              const void* weight_e4m3, const float* weight_scale,
+                                              int32_t N, int32_t K,
+                                              const mla_paged_cache_t* cache,
+                                              const mla_cache_scales_t* cache_scales,
+                                              uint32_t layer_idx,
+                                              void* k_latent_buffer, float* k_latent_scales,
+                                              void* k_buffer, void* stream);
 
 /*
  * The latent write path: new tokens' latent rows, normalised and rotated, into

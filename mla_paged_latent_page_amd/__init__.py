@@ -8,6 +8,9 @@ There is no fallback: if the library has not been built, every call raises.
 Entry points (same names as the C ABI):
   mla_decompress_k_paged       gather latent rows from a paged cache, up-project them
   mla_decompress_k_paged_fp8   the fp8 block-scaled form (1x128 activation, 128x128 weight scales)
+  mla_decompress_kv_paged(_fp8)  one gather, K and V up-projections
+  mla_decompress_k_paged_fp8_cache  the fp8 form on an e4m3 cache with per-128-column scales
+  mla_write_latent_paged       RMSNorm + rope rotation of new tokens' rows into the cache pages
   kv_matmul_paged              project hidden states and write them into K/V cache pages
   mla_gather_latent_paged      the gather step alone
   mla_latent_matmul            the up-projection step alone (rows already gathered)
@@ -32,7 +35,7 @@ EXPORTS = ("mla_paged_cache_default_strides", "mla_decompress_k_paged", "mla_gat
            "mla_latent_matmul", "mla_decompress_k_paged_fp8_workspace_size", "mla_decompress_k_paged_fp8",
            "kv_matmul_paged", "mla_check_indices", "mla_status_string", "mla_last_hip_error",
            "mla_abi_version", "mla_decompress_kv_paged", "mla_decompress_kv_paged_fp8",
-           "mla_write_latent_paged")
+           "mla_write_latent_paged", "mla_decompress_k_paged_fp8_cache")
 
 
 class MlaError(RuntimeError):
@@ -52,6 +55,15 @@ class CacheDesc(ctypes.Structure):
         ("stride_kv", ctypes.c_int64), ("stride_token", ctypes.c_int64),
         ("page_table", ctypes.c_void_p), ("batch_size", ctypes.c_uint32),
         ("max_pages_per_seq", ctypes.c_uint32), ("cache_lengths", ctypes.c_void_p),
+    ]
+
+
+class ScalesDesc(ctypes.Structure):
+    """Mirror of ``mla_cache_scales_t``."""
+    _fields_ = [
+        ("scales", ctypes.c_void_p), ("granularity", ctypes.c_uint32),
+        ("stride_page", ctypes.c_int64), ("stride_layer", ctypes.c_int64),
+        ("stride_kv", ctypes.c_int64), ("stride_token", ctypes.c_int64),
     ]
 
 
@@ -88,6 +100,9 @@ def lib():
             L.mla_write_latent_paged.argtypes = [vp, vp, i32, vp, ctypes.c_float, vp, i32, i32,
                                                  ctypes.POINTER(CacheDesc), u32, vp]
             L.mla_write_latent_paged.restype = i32
+            L.mla_decompress_k_paged_fp8_cache.argtypes = [vp, vp, i32, vp, vp, i32, i32, ctypes.POINTER(CacheDesc),
+                                                           ctypes.POINTER(ScalesDesc), u32, vp, vp, vp, vp]
+            L.mla_decompress_k_paged_fp8_cache.restype = i32
             L.kv_matmul_paged.argtypes = [vp, vp, i32, i32, vp, ctypes.POINTER(CacheDesc), u32, vp]
             L.kv_matmul_paged.restype = i32
             L.mla_gather_latent_paged.argtypes = [vp, vp, i32, ctypes.POINTER(CacheDesc), u32, vp, vp]
@@ -113,13 +128,18 @@ class PagedKVCache:
     """A paged pool as torch tensors.
 
     pool          [num_pages, num_layers, num_kv, page_size, num_heads, head_dim]
-                  (float32 or bfloat16; may be a strided view with contiguous token rows)
+                  (float32, bfloat16, or uint8 / float8_e4m3fn codes; may be a strided
+                  view with contiguous token rows)
     page_table    int32/uint32 [batch, max_pages_per_seq] page ids (raw 32-bit values)
     cache_lengths int32/uint32 [batch] or None
+    scales        fp8 pools only: float32 [num_pages, num_layers, num_kv, page_size, nblk],
+                  one scale per scale_granularity columns of a token row
     """
     pool: "object"
     page_table: "object"
     cache_lengths: Optional["object"] = None
+    scales: Optional["object"] = None
+    scale_granularity: int = 128
 
     def descriptor(self) -> CacheDesc:
         import torch
@@ -128,7 +148,8 @@ class PagedKVCache:
             raise ValueError("pool must be [pages, layers, kv, page_size, heads, head_dim]")
         if p.stride(5) != 1 or p.stride(4) != p.shape[5]:
             raise ValueError("token rows of the pool must be contiguous")
-        dt = {torch.float32: MLA_DTYPE_F32, torch.bfloat16: MLA_DTYPE_BF16}.get(p.dtype, -1)
+        dt = {torch.float32: MLA_DTYPE_F32, torch.bfloat16: MLA_DTYPE_BF16, torch.uint8: MLA_DTYPE_F8E4M3FN,
+              torch.float8_e4m3fn: MLA_DTYPE_F8E4M3FN}.get(p.dtype, -1)
         d = CacheDesc()
         d.blocks = p.data_ptr()
         d.dtype = dt
@@ -144,6 +165,21 @@ class PagedKVCache:
             if not cl.is_contiguous() or cl.element_size() != 4 or cl.numel() != pt.shape[0]:
                 raise ValueError("cache_lengths must be a contiguous 32-bit [batch] tensor")
             d.cache_lengths = cl.data_ptr()
+        return d
+
+    def scales_descriptor(self) -> ScalesDesc:
+        import torch
+        sc = self.scales
+        if sc is None:
+            raise ValueError("this cache has no scale pool")
+        if sc.dim() != 5 or sc.dtype != torch.float32 or sc.stride(4) != 1:
+            raise ValueError("scales must be float32 [pages, layers, kv, page_size, nblk] with contiguous rows")
+        if tuple(sc.shape[:4]) != tuple(self.pool.shape[:4]):
+            raise ValueError("scales must have the pool's pages, layers, kv halves and slots")
+        d = ScalesDesc()
+        d.scales = sc.data_ptr()
+        d.granularity = int(self.scale_granularity)
+        d.stride_page, d.stride_layer, d.stride_kv, d.stride_token = sc.stride(0), sc.stride(1), sc.stride(2), sc.stride(3)
         return d
 
 
@@ -320,6 +356,34 @@ def mla_decompress_kv_paged_fp8(buffer_row_offsets, cache_offsets, buffer_length
                                            workspace.data_ptr() if workspace is not None else None,
                                            ws_bytes, _stream(stream))
     _check(st, "mla_decompress_kv_paged_fp8")
+
+
+def mla_decompress_k_paged_fp8_cache(buffer_row_offsets, cache_offsets, buffer_length: int, w_k_e4m3, w_k_scale,
+                                     cache: PagedKVCache, layer_idx: int, k_latent_buffer, k_latent_scales, k_buffer,
+                                     stream=None) -> None:
+    """Gather e4m3 rows and their scales from an fp8 cache (bit copies into
+    k_latent_buffer / k_latent_scales), then k_buffer = block-scaled rows @ w_k.T."""
+    N, K = _weight_shape(w_k_e4m3, "w_k_e4m3")
+    desc = cache.descriptor()
+    sdesc = cache.scales_descriptor()
+    D = desc.num_heads * desc.head_dim
+    nblk = -(-D // 128)
+    if k_latent_buffer.numel() * k_latent_buffer.element_size() < buffer_length * D or \
+            not k_latent_buffer.is_contiguous() or k_latent_buffer.element_size() != 1:
+        raise ValueError(f"k_latent_buffer must be a contiguous 1-byte tensor of at least [{buffer_length}, {D}]")
+    if k_latent_scales.numel() < buffer_length * nblk or not k_latent_scales.is_contiguous() or \
+            k_latent_scales.element_size() != 4:
+        raise ValueError(f"k_latent_scales must be a contiguous float32 tensor of at least [{buffer_length}, {nblk}]")
+    if k_buffer.numel() < buffer_length * N or not k_buffer.is_contiguous():
+        raise ValueError(f"k_buffer must be contiguous and hold at least [{buffer_length}, {N}]")
+    if w_k_scale.numel() < -(-N // 128) * -(-K // 128) or w_k_scale.element_size() != 4:
+        raise ValueError("w_k_scale must hold float32 [N/128, K/128]")
+    st = lib().mla_decompress_k_paged_fp8_cache(_u32(buffer_row_offsets, "buffer_row_offsets"),
+                                                _u32(cache_offsets, "cache_offsets"), int(buffer_length),
+                                                w_k_e4m3.data_ptr(), w_k_scale.data_ptr(), N, K, ctypes.byref(desc),
+                                                ctypes.byref(sdesc), int(layer_idx), k_latent_buffer.data_ptr(),
+                                                k_latent_scales.data_ptr(), k_buffer.data_ptr(), _stream(stream))
+    _check(st, "mla_decompress_k_paged_fp8_cache")
 
 
 def mla_write_latent_paged(kv_input, input_row_offsets, kv_norm_gamma, epsilon: float, freqs_cis, K: int,

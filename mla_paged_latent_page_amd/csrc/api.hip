@@ -431,6 +431,61 @@ MLA_API mla_status_t mla_decompress_kv_paged_fp8(const uint32_t* buffer_row_offs
     return e == hipSuccess ? MLA_OK : hip_failed(e);
 }
 
+MLA_API mla_status_t mla_decompress_k_paged_fp8_cache(const uint32_t* buffer_row_offsets,
+                                                      const uint32_t* cache_offsets, int32_t buffer_length,
+                                                      const void* weight_e4m3, const float* weight_scale,
+                                                      int32_t N, int32_t K, const mla_paged_cache_t* cache,
+                                                      const mla_cache_scales_t* cache_scales, uint32_t layer_idx,
+                                                      void* k_latent_buffer, float* k_latent_scales,
+                                                      void* k_buffer, void* stream)
+{
+    if (!cache || !cache_scales)
+        return MLA_ERR_NULL_POINTER;
+    const int32_t M = buffer_length;
+    const bool work = M > 0;
+    if (work && (!buffer_row_offsets || !cache_offsets || !weight_e4m3 || !weight_scale || !k_latent_buffer ||
+                 !k_latent_scales || !k_buffer || !cache->blocks || !cache->page_table || !cache_scales->scales))
+        return MLA_ERR_NULL_POINTER;
+    if (M < 0 || N <= 0 || K <= 0 || N % 128 || K % 128 || (int64_t)N * K >= (int64_t(1) << 31) ||
+        cache_scales->granularity != 128)
+        return MLA_ERR_INVALID_SHAPE;
+    if (mla_status_t st = check_cache_shape(cache, 1))
+        return st;
+    const int64_t D = (int64_t)cache->num_heads * cache->head_dim;
+    const int64_t nblk = (D + 127) / 128;
+    if (K > D || (int64_t)M * D >= (int64_t(1) << 31) || cache_scales->stride_token < nblk ||
+        cache_scales->stride_page <= 0 || cache_scales->stride_layer < 0 || cache_scales->stride_kv < 0)
+        return MLA_ERR_INVALID_SHAPE;
+    if (cache->dtype != MLA_DTYPE_F8E4M3FN)
+        return MLA_ERR_INVALID_DTYPE;
+    if (!aligned16(weight_e4m3) || !aligned16(k_latent_buffer) || !aligned16(k_buffer) ||
+        (reinterpret_cast<uintptr_t>(weight_scale) & 3u) || (reinterpret_cast<uintptr_t>(k_latent_scales) & 3u) ||
+        (reinterpret_cast<uintptr_t>(cache_scales->scales) & 3u))
+        return MLA_ERR_MISALIGNED;
+    if (mla_status_t st = check_cache_alignment(cache))
+        return st;
+    if (layer_idx >= cache->num_layers)
+        return MLA_ERR_OUT_OF_RANGE;
+    if (!work)
+        return MLA_OK;
+    if (mla_status_t st = check_device())
+        return st;
+
+    const Second none;
+    mla::DecompressArgs a = decompress_args(buffer_row_offsets, cache_offsets, M, weight_e4m3, N, K, cache,
+                                            layer_idx, k_latent_buffer, k_buffer, D, none);
+    a.W_scale = weight_scale;
+    a.Ls = a.L;
+    a.Ls.base = reinterpret_cast<const char*>(cache_scales->scales + (int64_t)layer_idx * cache_scales->stride_layer);
+    a.Ls.stride_page = cache_scales->stride_page * 4;
+    a.Ls.stride_token = cache_scales->stride_token * 4;
+    a.Ls.stride_kv = cache_scales->stride_kv * 4;
+    a.lat_scale = k_latent_scales;
+    a.nblk = (int)nblk;
+    const hipError_t e = mla::launch_decompress_fp8_cache(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MLA_OK : hip_failed(e);
+}
+
 MLA_API mla_status_t mla_write_latent_paged(const void* kv_input, const uint32_t* input_row_offsets,
                                             int32_t total_tokens, const float* kv_norm_gamma, float epsilon,
                                             const float* freqs_cis, int32_t max_seq_len, int32_t K,

@@ -283,6 +283,23 @@ hipError_t launch_decompress_fp8(const DecompressArgs& a, hipStream_t s)
     }
 }
 
+// fp8 cache: the gather copies each row's codes and scales bit for bit into
+// k_latent_buffer and k_latent_scales, and the product reads them from there
+// (row strides D bytes and nblk floats): the cache is already quantised, so
+// there is no quantisation pass.
+hipError_t launch_decompress_fp8_cache(const DecompressArgs& a, hipStream_t s)
+{
+    const hipError_t e = launch_gather_rows(a, 1, s);
+    if (e != hipSuccess)
+        return e;
+    DecompressArgs p = first_projection(a);
+    p.q = a.lat;
+    p.q_scale = a.lat_scale;
+    p.q_ld = a.D;
+    p.qs_ld = a.nblk;
+    return launch_product_fp8_ring(p, num_cus(), s);
+}
+
 // Fused K and V (fp8): one gather and quantisation pass, then one product
 // launch over both projections' N-tiles.
 hipError_t launch_decompress_kv_fp8(const DecompressArgs& a, hipStream_t s)

@@ -59,12 +59,13 @@ static_assert(SLOT_BYTES % 256 == 0 && BM / 64 < NW, "slot layout");
 constexpr int LOADS = CA + CB + 1;  // loads per wave per stage
 
 struct Fp8GemmParams {
-    const uint8_t* A;     // [M][K] activation codes
-    const float* SA;      // [M][K/128] activation scales
+    const uint8_t* A;     // [M][lda] activation codes (the first K of each row used)
+    const float* SA;      // [M][sas] activation scales (the first K/128 used)
     const uint8_t* W;     // [N][K] weight codes
     const float* SW;      // [N/128][K/128] weight scales
     uint16_t* C;          // [M][N] bf16
     int M, N, K;
+    int lda, sas;         // row strides of A (bytes) and SA (floats)
     int tiles_m, tiles_n;
     int xcd_map;
     // Second projection (fused K and V): N-tiles tiles_n1 .. tiles_n - 1 use
@@ -127,7 +128,9 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
     const int lg_even = (lane & 7) ^ ((lrow >> 1) & 7), lg_odd = (lane & 7) ^ (((lrow >> 1) + 4) & 7);
     const uint32_t k_lane[2] = {(uint32_t)(lrow * P.K + lg_even * 16), (uint32_t)(lrow * P.K + lg_odd * 16)};
     const uint32_t chunk = (uint32_t)(CHUNK_ROWS * P.K);
-    const i32x4 sar = make_srd(P.SA, (uint32_t)((int64_t)P.M * KT * 4));
+    const uint32_t a_lane[2] = {(uint32_t)(lrow * P.lda + lg_even * 16), (uint32_t)(lrow * P.lda + lg_odd * 16)};
+    const uint32_t a_chunk = (uint32_t)(CHUNK_ROWS * P.lda);
+    const i32x4 sar = make_srd(P.SA, (uint32_t)((int64_t)P.M * P.sas * 4));
     const uint32_t ring_lds = lds_addr(ring);
 
     auto cursor_at = [&](int tile, Cursor& c) __attribute__((always_inline)) {
@@ -139,7 +142,7 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
         const Fp8Segment sg = segment_of(P, tn);
         c.tn = sg.tn;
         c.row0 = tm * BM;
-        c.ar = make_srd(P.A + (int64_t)tm * BM * P.K, (uint32_t)(mrows * P.K));
+        c.ar = make_srd(P.A + (int64_t)tm * BM * P.lda, (uint32_t)(mrows * P.lda));
         c.wr = make_srd(sg.W + (int64_t)sg.tn * BN * P.K, (uint32_t)(BN * P.K));
         c.swr = make_srd(sg.SW, (uint32_t)((sg.N / 128) * KT * 4));
     };
@@ -153,7 +156,7 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
 #pragma unroll
         for (int q = 0; q < CA; ++q) {
             const int ch = wave * CA + q;
-            asm_ld16_lds(c.ar, s + ch * 1024, k_lane[q & 1], ch * chunk + kb);
+            asm_ld16_lds(c.ar, s + ch * 1024, a_lane[q & 1], ch * a_chunk + kb);
         }
 #pragma unroll
         for (int q = 0; q < CB; ++q) {
@@ -163,7 +166,7 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
         // Every wave issues the same number of loads (the weight-scale copies
         // of waves 4..7 are identical), so one vmcnt value fits all waves.
         if (wave < BM / 64)
-            asm_ld4_lds(sar, s + SA_OFF + wave * 256, (uint32_t)((c.row0 + wave * 64 + lane) * KT) * 4,
+            asm_ld4_lds(sar, s + SA_OFF + wave * 256, (uint32_t)((c.row0 + wave * 64 + lane) * P.sas) * 4,
                         (uint32_t)c.ks * 4);
         else
             asm_ld4_lds(c.swr, s + SW_OFF, 0u, (uint32_t)(c.tn * KT + c.ks) * 4);
@@ -371,6 +374,8 @@ hipError_t launch_product_fp8_ring(const DecompressArgs& a, int cus, hipStream_t
     P.M = a.M;
     P.N = a.N;
     P.K = a.K;
+    P.lda = a.q_ld ? a.q_ld : a.K;
+    P.sas = a.qs_ld ? a.qs_ld : a.K / 128;
     P.tiles_m = (a.M + BM - 1) / BM;
     P.tiles_n = a.N / BN;
     P.tiles_n1 = P.tiles_n;

@@ -2,6 +2,9 @@
 // summary and Args buffer_row_offsets_1d, cache_offsets_1d, k_latent_buffer):
 //   k_latent[r][0:D] = cache row of request b at position cache_offsets[b] + (r - row_offsets[b])
 // as a bit copy.  The copy is HBM-bound: it reads and writes D * elem bytes per row.
+// With an fp8 cache the row's fp32 scales (one per 128 columns, the collection's
+// scale_dtype_ and quantization_granularity_) are copied the same way from the
+// scale pool into k_latent_scales[r][0:nblk].
 //
 // Each wave copies ROWS consecutive rows.  Lanes 0..ROWS-1 resolve one row each
 // (request by binary search, then page and slot), the offsets are broadcast
@@ -22,12 +25,14 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(DecompressArgs a, int 
         return;
 
     // Lane i < ROWS resolves row r0 + i (rows past M get a harmless offset 0).
-    int64_t my_off = 0;
+    int64_t my_off = 0, my_soff = 0;
     const int my_row = r0 + lane;
     if (lane < ROWS && my_row < a.M) {
         const uint32_t b = find_request(a.bro, a.L.batch, (uint32_t)my_row);
         const uint32_t p = a.co[b] + ((uint32_t)my_row - a.bro[b]);
         my_off = token_offset(a.L, b, p);
+        if (a.lat_scale)
+            my_soff = token_offset(a.Ls, b, p);
     }
     const uint32_t off_lo = (uint32_t)my_off, off_hi = (uint32_t)(my_off >> 32);
     const char* src[ROWS];
@@ -37,6 +42,20 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(DecompressArgs a, int 
         src[i] = a.L.base + o;
     }
     const int nrows = min(ROWS, a.M - r0);
+    if (a.lat_scale) {
+        // Scales: element idx = i * nblk + j of the wave's ROWS x nblk block is
+        // scale j of row r0 + i, whose offset lane i resolved.
+        const uint32_t s_lo = (uint32_t)my_soff, s_hi = (uint32_t)(my_soff >> 32);
+        for (int base = 0; base < ROWS * a.nblk; base += 64) {
+            const int idx = base + lane;
+            const int i = min(idx / a.nblk, ROWS - 1);
+            const uint64_t o = ((uint64_t)(uint32_t)__shfl((int)s_hi, i, 64) << 32) | (uint32_t)__shfl((int)s_lo, i, 64);
+            if (idx < nrows * a.nblk) {
+                const int j = idx - i * a.nblk;
+                a.lat_scale[(int64_t)r0 * a.nblk + idx] = *reinterpret_cast<const float*>(a.Ls.base + o + j * 4);
+            }
+        }
+    }
     const int64_t row_bytes = (int64_t)granules_per_row * 16;
     char* dst = static_cast<char*>(a.lat) + (int64_t)r0 * row_bytes;
     for (int g = lane; g < granules_per_row; g += 64) {

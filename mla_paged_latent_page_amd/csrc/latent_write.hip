@@ -12,16 +12,21 @@
 // computed in fp32 and stored, rounded to bf16, as the cache row of position p.
 //
 // HBM-bound: per token one 1152-byte row in, 256 bytes of freqs_cis, one row
-// out.  One wave per token: lane l holds latent values 8l .. 8l+7 (one
-// 16-byte load), the wave's sum of squares is a butterfly over the 64 lanes,
-// and lanes 0 .. R/8-1 hold the rope part (4 pairs each) with their 4 (cos,
-// sin) pairs of the position's freqs_cis row.
+// out.  A wave owns 2 consecutive tokens: it puts both input rows in flight
+// first (lane l holds latent values 8l .. 8l+7 of each, one 16-byte load; lanes
+// 0 .. R/8-1 also hold 4 rope pairs), then finds the tokens' requests with one
+// round of loads: lane j reads input_row_offsets[j], [j + 64], [j + 128] and
+// [j + 192] (256 entries per pass), and the request of token t is the number
+// of entries <= t, minus one, counted by ballots.  Then come the dependent
+// loads of both tokens (cache length, page table, freqs_cis row), and only
+// after them the stores.
 #include "launch.hpp"
 
 namespace mla {
 namespace {
 
 constexpr int WRITE_WAVES = 4;
+constexpr int TOKENS_PER_WAVE = 2;
 
 __device__ inline float wave_sum(float v)
 {
@@ -33,57 +38,107 @@ __device__ inline float wave_sum(float v)
 
 __global__ void __launch_bounds__(64 * WRITE_WAVES) latent_write_kernel(LatentWriteArgs a)
 {
+    constexpr int TW = TOKENS_PER_WAVE;
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * WRITE_WAVES + (threadIdx.x >> 6);
-    if (t >= a.T)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int t0 = (blockIdx.x * WRITE_WAVES + wave) * TW;
+    if (t0 >= a.T)
         return;
-    const uint32_t b = find_request(a.iro, a.L.batch, (uint32_t)t);
-    const uint32_t p = a.cache_len[b] + ((uint32_t)t - a.iro[b]);
-    const uint32_t pf = p < (uint32_t)a.max_seq ? p : (uint32_t)a.max_seq - 1;   // freqs row, clamped
-    char* dst = const_cast<char*>(a.L.base) + token_offset(a.L, b, p);
-    const char* src = reinterpret_cast<const char*>(a.X) + (int64_t)t * a.D * 2;
+    const bool lat = lane * 8 < a.K;   // K <= 512: at most 64 lanes
+    const bool rot = lane * 8 < a.R;   // R <= 512
 
-    // Latent part: K / 8 lanes hold 8 values each (K <= 512).
-    const bool lat = lane * 8 < a.K;
-    u32x4 xv = lat ? ld16(src + lane * 16) : u32x4{0u, 0u, 0u, 0u};
-    float x[8];
+    // Input rows of the wave's tokens (a tail wave re-reads its last token).
+    u32x4 xv[TW], rv[TW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        x[2 * i] = bf16_lo(xv[i]);
-        x[2 * i + 1] = bf16_hi(xv[i]);
-    }
-    float ss = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        ss += x[i] * x[i];
-    ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)a.K + a.eps);
-    if (lat) {
-        const float* g = a.gamma + lane * 8;
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(g), g1 = *reinterpret_cast<const f32x4*>(g + 4);
-        const float gg[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
-        u32x4 y;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            y[i] = pack_bf16x2(gg[2 * i] * (x[2 * i] * inv), gg[2 * i + 1] * (x[2 * i + 1] * inv));
-        st16(dst + lane * 16, y);
+    for (int k = 0; k < TW; ++k) {
+        const int t = min(t0 + k, a.T - 1);
+        const char* src = reinterpret_cast<const char*>(a.X) + (int64_t)t * a.D * 2;
+        xv[k] = lat ? ld16(src + lane * 16) : u32x4{0u, 0u, 0u, 0u};
+        rv[k] = rot ? ld16(src + a.K * 2 + lane * 16) : u32x4{0u, 0u, 0u, 0u};
     }
 
-    // Rope part: R / 8 lanes hold 4 pairs each, with the 4 (cos, sin) pairs of
-    // freqs_cis row p.
-    if (lane * 8 < a.R) {
-        const u32x4 rv = ld16(src + a.K * 2 + lane * 16);
+    // Request of each token: entries b < batch with input_row_offsets[b] <= t
+    // form a prefix (the offsets do not decrease); its last index is the
+    // request (empty requests are skipped by taking the last).
+    uint32_t cnt[TW];
+#pragma unroll
+    for (int k = 0; k < TW; ++k)
+        cnt[k] = 0;
+    for (uint32_t c = 0; c < a.L.batch; c += 256) {
+        uint32_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t j = c + u * 64 + lane;
+            v[u] = j < a.L.batch ? a.iro[j] : 0xFFFFFFFFu;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int k = 0; k < TW; ++k)
+                cnt[k] += (uint32_t)__popcll(__ballot(v[u] <= (uint32_t)(t0 + k)));
+    }
+
+    // Per token: request, position, destination and its freqs_cis row, all
+    // loaded before the first store.
+    int64_t off[TW];
+    f32x4 fr0[TW], fr1[TW];
+#pragma unroll
+    for (int k = 0; k < TW; ++k) {
+        const uint32_t t = (uint32_t)min(t0 + k, a.T - 1);
+        const uint32_t b = cnt[k] == 0 ? 0u : min(cnt[k], a.L.batch) - 1;
+        const uint32_t p = a.cache_len[b] + (t - a.iro[b]);
+        const uint32_t pf = p < (uint32_t)a.max_seq ? p : (uint32_t)a.max_seq - 1;   // freqs row, clamped
+        off[k] = token_offset(a.L, b, p);
         const float* f = a.freqs + (int64_t)pf * a.R + lane * 8;
-        const f32x4 f0 = *reinterpret_cast<const f32x4*>(f), f1 = *reinterpret_cast<const f32x4*>(f + 4);
-        const float cs[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
-        u32x4 y;
+        fr0[k] = rot ? *reinterpret_cast<const f32x4*>(f) : f32x4{0.f, 0.f, 0.f, 0.f};
+        fr1[k] = rot ? *reinterpret_cast<const f32x4*>(f + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    f32x4 g0 = {0.f, 0.f, 0.f, 0.f}, g1 = {0.f, 0.f, 0.f, 0.f};
+    if (lat) {
+        g0 = *reinterpret_cast<const f32x4*>(a.gamma + lane * 8);
+        g1 = *reinterpret_cast<const f32x4*>(a.gamma + lane * 8 + 4);
+    }
+    const float gg[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+
+#pragma unroll
+    for (int k = 0; k < TW; ++k) {
+        if (t0 + k >= a.T)
+            break;
+        char* dst = const_cast<char*>(a.L.base) + off[k];
+
+        // Latent part: RMS over the K latent values, scaled by gamma.
+        float x[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float x0 = bf16_lo(rv[i]), x1 = bf16_hi(rv[i]);
-            const float c = cs[2 * i], s = cs[2 * i + 1];
-            y[i] = pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
+            x[2 * i] = bf16_lo(xv[k][i]);
+            x[2 * i + 1] = bf16_hi(xv[k][i]);
         }
-        st16(dst + a.K * 2 + lane * 16, y);
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            ss += x[i] * x[i];
+        ss = wave_sum(ss);
+        const float inv = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+        if (lat) {
+            u32x4 y;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                y[i] = pack_bf16x2(gg[2 * i] * (x[2 * i] * inv), gg[2 * i + 1] * (x[2 * i + 1] * inv));
+            st16(dst + lane * 16, y);
+        }
+
+        // Rope part: 4 pairs per lane with the 4 (cos, sin) pairs of freqs_cis row p.
+        if (rot) {
+            const float cs[8] = {fr0[k][0], fr0[k][1], fr0[k][2], fr0[k][3], fr1[k][0], fr1[k][1], fr1[k][2], fr1[k][3]};
+            u32x4 y;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x0 = bf16_lo(rv[k][i]), x1 = bf16_hi(rv[k][i]);
+                const float c = cs[2 * i], s = cs[2 * i + 1];
+                y[i] = pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
+            }
+            st16(dst + a.K * 2 + lane * 16, y);
+        }
     }
 }
 
@@ -91,8 +146,8 @@ __global__ void __launch_bounds__(64 * WRITE_WAVES) latent_write_kernel(LatentWr
 
 hipError_t launch_latent_write(const LatentWriteArgs& a, hipStream_t s)
 {
-    hipLaunchKernelGGL(latent_write_kernel, dim3((a.T + WRITE_WAVES - 1) / WRITE_WAVES), dim3(64 * WRITE_WAVES), 0,
-                       s, a);
+    constexpr int per_block = WRITE_WAVES * TOKENS_PER_WAVE;
+    hipLaunchKernelGGL(latent_write_kernel, dim3((a.T + per_block - 1) / per_block), dim3(64 * WRITE_WAVES), 0, s, a);
     return hipGetLastError();
 }
 

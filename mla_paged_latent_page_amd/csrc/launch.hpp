@@ -27,6 +27,15 @@ struct DecompressArgs {
     const float* W2_scale;
     void* out2;
     int N2;
+    // fp8 cache: the scale pool's layer view (one fp32 per 128 columns of a
+    // token row, nblk per row), where the gather copies each row's scales
+    // (lat_scale [M][nblk]; null: no scales), and the row strides the fp8
+    // product reads its activation codes and scales with (q_ld bytes, qs_ld
+    // floats; 0 means K and K/128).
+    PagedLayer Ls;
+    float* lat_scale;
+    int nblk;
+    int q_ld, qs_ld;
 };
 
 struct KvMatmulArgs {
@@ -60,6 +69,7 @@ hipError_t launch_decompress_fp8(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_decompress_kv_bf16(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_decompress_kv_f32(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_decompress_kv_fp8(const DecompressArgs& a, hipStream_t s);
+hipError_t launch_decompress_fp8_cache(const DecompressArgs& a, hipStream_t s);
 // The same arguments with the second projection moved into the first slot.
 inline DecompressArgs second_projection(const DecompressArgs& a)
 {

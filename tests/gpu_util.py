@@ -135,3 +135,22 @@ def check_close(got, ref, tol, what):
     say(f"[gpu] {what}: max|err|={err:.3e} max|ref|={scale:.3e} ratio={err / max(scale, 1e-30):.2e} (tol {tol})")
     assert err <= tol * scale, f"{what}: max|err| {err} > {tol} * {scale}"
     return err, scale
+
+
+def run_decompress_fp8_cache(case, extra_rows=0):
+    """Run mla_decompress_k_paged_fp8_cache on a case with an e4m3 cache.
+    Outputs are over-allocated by extra_rows rows of poison (codes 0x7F,
+    scales NaN, k_buffer POISON_OUT)."""
+    dc, t = W.device_decompress(case)
+    M, D, N = case.M, case.D_c, case.N
+    nblk = case.cache.scale_blocks
+    lat = torch.full((M + extra_rows, D), 0x7F, dtype=torch.uint8, device="cuda")
+    lsc = torch.full((M + extra_rows, nblk), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.empty((M + extra_rows, N), dtype=torch.bfloat16, device="cuda")
+    out.view(torch.int16).fill_(POISON_OUT)
+    cache = mp.PagedKVCache(dc.pool, dc.page_table, dc.cache_lengths, scales=dc.scales)
+    say(f"[gpu] {case.name} fp8 cache: M={M} N={N} K={case.K} D={D} nblk={nblk}")
+    mp.mla_decompress_k_paged_fp8_cache(t["buffer_row_offsets"], t["cache_offsets"], M, t["weight_q"],
+                                        t["weight_scale"], cache, case.layer_idx, lat, lsc, out)
+    torch.cuda.synchronize()
+    return {"lat": lat, "scales": lsc, "out": out}

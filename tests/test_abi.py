@@ -292,3 +292,52 @@ def test_write_latent_error_paths(lib):
     assert write_latent(lib, d, layer=2) == RANGE
     assert write_latent(lib, d, T=0, x=None, iro=None, g=None, f=None) == OK
     assert write_latent(lib, d) == DEV
+
+
+def scales_desc(gran=128, nblk=5, page_size=128, layers=2):
+    s = mp.ScalesDesc()
+    s.scales = FAKE
+    s.granularity = gran
+    s.stride_token = nblk
+    s.stride_kv = nblk * page_size
+    s.stride_layer = s.stride_kv
+    s.stride_page = s.stride_layer * layers
+    return s
+
+
+def fp8_cache(lib, d, s, M=100, N=512, K=512, layer=1, **ptrs):
+    p = dict(bro=FAKE, co=FAKE, w=FAKE, ws=FAKE, lat=FAKE, lsc=FAKE, out=FAKE)
+    p.update(ptrs)
+    return lib.mla_decompress_k_paged_fp8_cache(p["bro"], p["co"], M, p["w"], p["ws"], N, K,
+                                                ctypes.byref(d) if d is not None else None,
+                                                ctypes.byref(s) if s is not None else None, layer,
+                                                p["lat"], p["lsc"], p["out"], None)
+
+
+def test_fp8_cache_error_paths(lib):
+    d = cache_desc(dtype=2)
+    s = scales_desc()
+    assert fp8_cache(lib, None, s) == NULLP
+    assert fp8_cache(lib, d, None) == NULLP
+    for k in ("bro", "co", "w", "ws", "lat", "lsc", "out"):
+        assert fp8_cache(lib, d, s, **{k: None}) == NULLP
+    sn = scales_desc()
+    sn.scales = None
+    assert fp8_cache(lib, d, sn) == NULLP
+    assert fp8_cache(lib, d, s, M=-1) == SHAPE
+    assert fp8_cache(lib, d, s, N=500) == SHAPE                     # N % 128
+    assert fp8_cache(lib, d, s, K=320) == SHAPE                     # K % 128
+    assert fp8_cache(lib, d, s, K=640) == SHAPE                     # K > D_c
+    assert fp8_cache(lib, d, scales_desc(gran=64)) == SHAPE         # only 128-column scale blocks
+    assert fp8_cache(lib, d, scales_desc(nblk=4)) == SHAPE          # scale rows shorter than ceil(576/128)
+    assert fp8_cache(lib, d, s, M=4_000_000) == SHAPE               # M * D_c >= 2^31
+    assert fp8_cache(lib, cache_desc(dtype=2, num_kv=2), s) == SHAPE
+    assert fp8_cache(lib, cache_desc(dtype=1), s) == DTYPE          # a bf16 pool has no scales
+    assert fp8_cache(lib, d, s, w=FAKE + 8) == MISAL
+    assert fp8_cache(lib, d, s, lat=FAKE + 8) == MISAL
+    assert fp8_cache(lib, d, s, ws=FAKE + 2) == MISAL
+    assert fp8_cache(lib, d, s, lsc=FAKE + 2) == MISAL
+    assert fp8_cache(lib, cache_desc(dtype=2, head_dim=584), s) == MISAL   # 584-byte rows are not 16-byte granules
+    assert fp8_cache(lib, d, s, layer=2) == RANGE
+    assert fp8_cache(lib, d, s, M=0, bro=None, co=None, w=None, ws=None, lat=None, lsc=None, out=None) == OK
+    assert fp8_cache(lib, d, s) == DEV
