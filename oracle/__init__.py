@@ -277,6 +277,25 @@ def decompress_k_fp8_cache(case, rows=None):
     return codes, scales, out
 
 
+def absorb_q(case):
+    """(latent part binary64 [T, H, kv_latent_dim], rope part bits [T, H, d_rope]
+    or None): query absorption (page "mla_prefill_decode_graph_fp8", Args q
+    [tot_seq_len, num_heads, qk_nope_head_dim + qk_rope_head_dim] and w_uk
+    [num_heads, kv_latent_dim, qk_nope_head_dim], which takes the non-rope part
+    of each query head into the latent space):
+        latent[t, h, c] = sum_{d < d_nope} q[t, h, d] * w_uk[h, c, d]
+    one product per head, and the rope part q[t, h, d_nope:] carried over
+    unchanged after it when case.copy_rope."""
+    T, H, _ = case.q.shape
+    DN, NL = case.d_nope, case.kv_latent_dim
+    out = np.empty((T, H, NL), np.float64)
+    for h in range(H):
+        a = np.ascontiguousarray(case.q[:, h, :DN])
+        out[:, h, :] = matmul_nt(a, "bf16", np.ascontiguousarray(case.w_uk[h]), "bf16", DN)
+    rope = np.ascontiguousarray(case.q[:, :, DN:]) if case.copy_rope else None
+    return out, rope
+
+
 def decompress_kv(case_k, case_v, rows=None):
     """(k_latent bits, k_buffer rows, v_buffer rows), binary64 products.
 

@@ -403,6 +403,49 @@ def c5_latent_write(seed=5) -> LatentWriteCase:
 
 
 # --------------------------------------------------------------------------
+# query absorption cases (q_nope x w_uk per head)
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class AbsorbCase:
+    name: str
+    q: np.ndarray          # uint16 bf16 bits [T, H, d_nope + d_rope]
+    w_uk: np.ndarray       # uint16 bf16 bits [H, kv_latent_dim, d_nope]
+    d_nope: int
+    copy_rope: bool = True
+
+    @property
+    def T(self) -> int: return self.q.shape[0]
+    @property
+    def H(self) -> int: return self.q.shape[1]
+    @property
+    def d_rope(self) -> int: return self.q.shape[2] - self.d_nope
+    @property
+    def kv_latent_dim(self) -> int: return self.w_uk.shape[1]
+    @property
+    def out_dim(self) -> int: return self.kv_latent_dim + (self.d_rope if self.copy_rope else 0)
+
+
+def absorb_case(name, *, seed, T, H=128, d_nope=128, d_rope=64, kv_latent_dim=512, w_std=0.05,
+                copy_rope=True) -> AbsorbCase:
+    """Queries bf16 N(0, 1) [T, H, d_nope + d_rope]; w_uk bf16 N(0, w_std)
+    [H, kv_latent_dim, d_nope]."""
+    rng = np.random.default_rng(seed)
+    q = to_bf16_bits(rng.standard_normal((T, H, d_nope + d_rope), dtype=np.float32))
+    w = to_bf16_bits(rng.standard_normal((H, kv_latent_dim, d_nope), dtype=np.float32) * np.float32(w_std))
+    return AbsorbCase(name, q, w, d_nope, copy_rope)
+
+
+def c7_absorb(seed=7) -> AbsorbCase:
+    """A decode step of 128 requests, one new token each: 128 query heads of
+    128 nope + 64 rope columns, w_uk [128, 512, 128]."""
+    return absorb_case("c7_absorb", seed=seed, T=128)
+
+
+def device_absorb(case: AbsorbCase, device="cuda"):
+    return {"q": _bits_to_torch(case.q, device), "w_uk": _bits_to_torch(case.w_uk, device)}
+
+
+# --------------------------------------------------------------------------
 # the named workloads
 # --------------------------------------------------------------------------
 def c0_tiny(seed=0) -> DecompressCase:
