@@ -20,6 +20,8 @@ The JSON line also carries the other rows of the path, each timed the same way:
   c2_tp8_share one GPU's share of W_k when 8 GPUs split the heads (N = 2048)
   c5_latent_write  RMSNorm + rope rotation + scatter of 88994 new tokens'
                rows into the MLA pages (HBM-bound)
+  c7_absorb    query absorption for a decode batch of 128 tokens x 128 heads
+               (w_uk [128, 512, 128]; HIP-graph replay like p64/p256)
   p64, p256    1 and 4 newest rows per request of the decode batch (weight-bound;
                timed by HIP-graph replay over 32 weight copies, see probe_row)
 
@@ -54,6 +56,7 @@ KERNEL_SOURCES = {
     "kv_matmul_ring": ("kv_matmul_ring.hip", "kv_matmul.hip", "bf16_tile_common.hpp"),
     "decompress_small_bf16": ("decompress_small.hip",),
     "latent_write_kernel": ("latent_write.hip",),
+    "absorb_bf16": ("absorb.hip",),
 }
 
 
@@ -223,6 +226,57 @@ def probe_row(torch, mp, W, pc, warmup, copies=32, reps=20):
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", traffic_from_profile("decompress_small_bf16", pc.name)),
             "kernel": "decompress_small_bf16 (gather + product in one launch)",
             "timing": f"HIP graph of {copies} launches on {copies} weight copies, replayed {reps} times"}
+
+
+def absorb_row(torch, mp, W, warmup, copies=32, reps=20):
+    """Query absorption for a decode batch (a few microseconds per call), timed
+    like the few-rows probes: `copies` launches on their own copies of w_uk
+    (16 MiB each, so every launch reads its weight from HBM), captured in one
+    HIP graph and replayed `reps` times; checked against an eager call first."""
+    c = W.c7_absorb()
+    t = W.device_absorb(c)
+    out = torch.empty((c.T, c.H, c.out_dim), dtype=torch.bfloat16, device="cuda")
+    weights = [t["w_uk"].clone() for _ in range(copies)]
+
+    def call(w):
+        mp.mla_absorb_q(t["q"], w, out, d_nope=c.d_nope, copy_rope=c.copy_rope)
+    call(weights[0])
+    torch.cuda.synchronize()
+    eager = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for w in weights[:3]:
+            call(w)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for w in weights:
+            call(w)
+    for _ in range(max(1, warmup)):
+        g.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out.view(torch.int16), eager.view(torch.int16)):
+        raise RuntimeError("c7_absorb: graph replay differs from the eager call")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * copies)
+    T, H, L, Dq = c.T, c.H, c.kv_latent_dim, c.q.shape[2]
+    b = H * L * c.d_nope * 2 + T * H * Dq * 2 + T * H * c.out_dim * 2
+    gbs = b / (ms * 1e-3) / 1e9
+    del g, weights
+    return {"tokens": T, "heads": H, "us_per_call": round(ms * 1e3, 3),
+            "tflops": round(2.0 * T * H * L * c.d_nope / (ms * 1e-3) / 1e12, 2),
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", traffic_from_profile("absorb_bf16", "c7_absorb")),
+            "kernel": "absorb_bf16",
+            "timing": f"HIP graph of {copies} launches on {copies} weight copies, replayed {reps} times",
+            "note": "algorithmic bytes: w_uk once (16 MiB), the queries (nope + rope) once, the output once"}
 
 
 def roofline(bound, achieved, peak, unit, traffic):
@@ -466,6 +520,10 @@ def main():
                                    "note": "per token: read the 1152-byte row and its 256-byte rope table row, "
                                            "write the 1152-byte cache row"}
         print(f"[bench] c5_latent_write: {t.avg_launch_ms:.4f} ms, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+        rows["c7_absorb"] = absorb_row(torch, mp, W, args.warmup)
+        r = rows["c7_absorb"]
+        print(f"[bench] c7_absorb: {r['us_per_call']:.2f} us/call (graph replay), "
+              f"{r['roofline']['achieved']:.0f} GB/s", file=sys.stderr, flush=True)
         result["rows"] = rows
 
     if args.cpu_seconds > 0:

@@ -324,6 +324,33 @@ mla_status_t mla_decompress_k_paged_fp8_cache(const uint32_t* buffer_row_offsets
                                               void* k_buffer, void* stream);
 
 /*
+ * Query absorption for decode (page "mla_prefill_decode_graph_fp8", Args q
+ * [tot_seq_len, num_heads, qk_nope_head_dim + qk_rope_head_dim] and w_uk
+ * [num_heads, kv_latent_dim, qk_nope_head_dim], the weight that projects the
+ * non-rope part of each query head to the KV latent space), bf16:
+ *
+ *   q_latent[t][h][c] = bf16( sum_{d < d_nope} q[t][h][d] * w_uk[h][c][d] ),  c < kv_latent_dim
+ *   q_latent[t][h][kv_latent_dim + i] = q[t][h][d_nope + i],  i < d_rope   (copy_rope = 1 only)
+ *
+ * fp32 accumulation, round to nearest even.  With copy_rope = 1 an absorbed head
+ * has the layout of an MLA cache row (latent, then rope).
+ *
+ * q             [device] bf16 [total_tokens][num_heads][d_nope + d_rope], 16-byte aligned
+ * d_nope        128 (the supported qk_nope_head_dim); d_rope % 8 == 0
+ * w_uk          [device] bf16 [num_heads][kv_latent_dim][d_nope], 16-byte aligned
+ * kv_latent_dim % 128 == 0
+ * copy_rope     0 or 1
+ * q_latent      [device] bf16 [total_tokens][num_heads][kv_latent_dim + (copy_rope ? d_rope : 0)],
+ *               16-byte aligned, written
+ * (total_tokens + 128) * num_heads * (d_nope + d_rope) * 2 < 2^31.
+ * Errors and validation order as for the other calls (pointers, shapes,
+ * alignment, device).
+ */
+mla_status_t mla_absorb_q(const void* q, int32_t total_tokens, int32_t num_heads, int32_t d_nope,
+                          int32_t d_rope, const void* w_uk, int32_t kv_latent_dim, int32_t copy_rope,
+                          void* q_latent, void* stream);
+
+/*
  * The latent write path: new tokens' latent rows, normalised and rotated, into
  * the MLA cache pages this library's decompress calls read (page
  * "mla_prefill_decode_graph_fp8", Args kv_input_fn (the latent values,

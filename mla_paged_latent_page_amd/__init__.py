@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
   mla_decompress_kv_paged(_fp8)  one gather, K and V up-projections
   mla_decompress_k_paged_fp8_cache  the fp8 form on an e4m3 cache with per-128-column scales
   mla_write_latent_paged       RMSNorm + rope rotation of new tokens' rows into the cache pages
+  mla_absorb_q                 per-head product of the non-rope query columns with w_uk (decode)
   kv_matmul_paged              project hidden states and write them into K/V cache pages
   mla_gather_latent_paged      the gather step alone
   mla_latent_matmul            the up-projection step alone (rows already gathered)
@@ -35,7 +36,7 @@ EXPORTS = ("mla_paged_cache_default_strides", "mla_decompress_k_paged", "mla_gat
            "mla_latent_matmul", "mla_decompress_k_paged_fp8_workspace_size", "mla_decompress_k_paged_fp8",
            "kv_matmul_paged", "mla_check_indices", "mla_status_string", "mla_last_hip_error",
            "mla_abi_version", "mla_decompress_kv_paged", "mla_decompress_kv_paged_fp8",
-           "mla_write_latent_paged", "mla_decompress_k_paged_fp8_cache")
+           "mla_write_latent_paged", "mla_decompress_k_paged_fp8_cache", "mla_absorb_q")
 
 
 class MlaError(RuntimeError):
@@ -103,6 +104,8 @@ def lib():
             L.mla_decompress_k_paged_fp8_cache.argtypes = [vp, vp, i32, vp, vp, i32, i32, ctypes.POINTER(CacheDesc),
                                                            ctypes.POINTER(ScalesDesc), u32, vp, vp, vp, vp]
             L.mla_decompress_k_paged_fp8_cache.restype = i32
+            L.mla_absorb_q.argtypes = [vp, i32, i32, i32, i32, vp, i32, i32, vp, vp]
+            L.mla_absorb_q.restype = i32
             L.kv_matmul_paged.argtypes = [vp, vp, i32, i32, vp, ctypes.POINTER(CacheDesc), u32, vp]
             L.kv_matmul_paged.restype = i32
             L.mla_gather_latent_paged.argtypes = [vp, vp, i32, ctypes.POINTER(CacheDesc), u32, vp, vp]
@@ -384,6 +387,26 @@ def mla_decompress_k_paged_fp8_cache(buffer_row_offsets, cache_offsets, buffer_l
                                                 ctypes.byref(sdesc), int(layer_idx), k_latent_buffer.data_ptr(),
                                                 k_latent_scales.data_ptr(), k_buffer.data_ptr(), _stream(stream))
     _check(st, "mla_decompress_k_paged_fp8_cache")
+
+
+def mla_absorb_q(q, w_uk, q_latent, d_nope: int = 128, copy_rope: bool = True, stream=None) -> None:
+    """q_latent[t, h, :L] = q[t, h, :d_nope] @ w_uk[h].T per head (L = kv_latent_dim),
+    then, with copy_rope, the rope columns q[t, h, d_nope:] after it."""
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [T, H, d_nope + d_rope] tensor")
+    if w_uk.dim() != 3 or not w_uk.is_contiguous():
+        raise ValueError("w_uk must be a contiguous [H, kv_latent_dim, d_nope] tensor")
+    T, H, Dq = q.shape
+    if w_uk.shape[0] != H or w_uk.shape[2] != d_nope:
+        raise ValueError(f"w_uk must be [{H}, kv_latent_dim, {d_nope}]")
+    L = w_uk.shape[1]
+    d_rope = Dq - d_nope
+    Do = L + (d_rope if copy_rope else 0)
+    if tuple(q_latent.shape) != (T, H, Do) or not q_latent.is_contiguous():
+        raise ValueError(f"q_latent must be a contiguous [{T}, {H}, {Do}] tensor")
+    st = lib().mla_absorb_q(q.data_ptr(), T, H, int(d_nope), int(d_rope), w_uk.data_ptr(), int(L),
+                            1 if copy_rope else 0, q_latent.data_ptr(), _stream(stream))
+    _check(st, "mla_absorb_q")
 
 
 def mla_write_latent_paged(kv_input, input_row_offsets, kv_norm_gamma, epsilon: float, freqs_cis, K: int,

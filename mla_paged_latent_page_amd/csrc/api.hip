@@ -486,6 +486,40 @@ MLA_API mla_status_t mla_decompress_k_paged_fp8_cache(const uint32_t* buffer_row
     return e == hipSuccess ? MLA_OK : hip_failed(e);
 }
 
+MLA_API mla_status_t mla_absorb_q(const void* q, int32_t total_tokens, int32_t num_heads, int32_t d_nope,
+                                  int32_t d_rope, const void* w_uk, int32_t kv_latent_dim, int32_t copy_rope,
+                                  void* q_latent, void* stream)
+{
+    const int32_t T = total_tokens;
+    const bool work = T > 0;
+    if (work && (!q || !w_uk || !q_latent))
+        return MLA_ERR_NULL_POINTER;
+    const int64_t Dq = (int64_t)d_nope + d_rope;
+    if (T < 0 || num_heads <= 0 || d_nope != 128 || d_rope < 0 || d_rope % 8 || kv_latent_dim <= 0 ||
+        kv_latent_dim % 128 || (copy_rope != 0 && copy_rope != 1) ||
+        ((int64_t)T + 128) * num_heads * Dq * 2 >= (int64_t(1) << 31) ||
+        (int64_t)num_heads * kv_latent_dim * d_nope * 2 >= (int64_t(1) << 40))
+        return MLA_ERR_INVALID_SHAPE;
+    if (!aligned16(q) || !aligned16(w_uk) || !aligned16(q_latent))
+        return MLA_ERR_MISALIGNED;
+    if (!work)
+        return MLA_OK;
+    if (mla_status_t st = check_device())
+        return st;
+    mla::AbsorbArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.w = static_cast<const uint16_t*>(w_uk);
+    a.out = static_cast<uint16_t*>(q_latent);
+    a.T = T;
+    a.H = num_heads;
+    a.NL = kv_latent_dim;
+    a.Dq = (int)Dq;
+    a.R = copy_rope ? d_rope : 0;
+    a.Do = kv_latent_dim + a.R;
+    const hipError_t e = mla::launch_absorb_bf16(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MLA_OK : hip_failed(e);
+}
+
 MLA_API mla_status_t mla_write_latent_paged(const void* kv_input, const uint32_t* input_row_offsets,
                                             int32_t total_tokens, const float* kv_norm_gamma, float epsilon,
                                             const float* freqs_cis, int32_t max_seq_len, int32_t K,

@@ -58,7 +58,15 @@ struct LatentWriteArgs {
     int T, K, R, D, max_seq;
 };
 
+struct AbsorbArgs {
+    const uint16_t* q;         // bf16 [T][H][Dq]: 128 nope columns, then rope
+    const uint16_t* w;         // w_uk bf16 [H][NL][128]
+    uint16_t* out;             // bf16 [T][H][Do]: NL latent columns, then R rope columns
+    int T, H, NL, Dq, Do, R;   // R: rope columns copied (0: none)
+};
+
 hipError_t launch_gather_rows(const DecompressArgs& a, int elem_bytes, hipStream_t s);
+hipError_t launch_absorb_bf16(const AbsorbArgs& a, hipStream_t s);
 hipError_t launch_latent_write(const LatentWriteArgs& a, hipStream_t s);
 hipError_t launch_product_bf16(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_product_f32(const DecompressArgs& a, hipStream_t s);

@@ -341,3 +341,27 @@ def test_fp8_cache_error_paths(lib):
     assert fp8_cache(lib, d, s, layer=2) == RANGE
     assert fp8_cache(lib, d, s, M=0, bro=None, co=None, w=None, ws=None, lat=None, lsc=None, out=None) == OK
     assert fp8_cache(lib, d, s) == DEV
+
+
+def absorb(lib, T=64, H=16, dn=128, dr=64, L=512, copy=1, **ptrs):
+    p = dict(q=FAKE, w=FAKE, out=FAKE)
+    p.update(ptrs)
+    return lib.mla_absorb_q(p["q"], T, H, dn, dr, p["w"], L, copy, p["out"], None)
+
+
+def test_absorb_error_paths(lib):
+    for k in ("q", "w", "out"):
+        assert absorb(lib, **{k: None}) == NULLP
+    assert absorb(lib, T=-1) == SHAPE
+    assert absorb(lib, H=0) == SHAPE
+    assert absorb(lib, dn=64) == SHAPE                 # only qk_nope_head_dim 128
+    assert absorb(lib, dr=60) == SHAPE                 # rope columns in 16-byte pieces
+    assert absorb(lib, L=500) == SHAPE                 # kv_latent_dim % 128
+    assert absorb(lib, copy=2) == SHAPE
+    assert absorb(lib, T=60000, H=128) == SHAPE        # query offsets past 2^31
+    assert absorb(lib, q=FAKE + 8) == MISAL
+    assert absorb(lib, w=FAKE + 8) == MISAL
+    assert absorb(lib, out=FAKE + 2) == MISAL
+    assert absorb(lib, T=0, q=None, w=None, out=None) == OK
+    assert absorb(lib, dr=0, copy=0) == DEV
+    assert absorb(lib) == DEV

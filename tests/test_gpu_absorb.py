@@ -1,0 +1,75 @@
+"""GPU parity of mla_absorb_q (per-head product of the non-rope query columns
+with w_uk, the rope columns carried over) against the CPU oracle.
+
+The latent part is a bf16 product with fp32 accumulation over 128 terms: within
+1e-2 * max|ref| of the oracle's binary64 sum (the bf16 product bound); the rope
+part is a bit copy.  Outputs are over-allocated by poisoned tokens that must
+keep their bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mla_paged_latent_page_amd as mp
+import oracle
+import workloads as W
+from gpu_util import BF16_TOL, POISON_OUT, check_close, say, to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(case, extra=3):
+    t = W.device_absorb(case)
+    T, H = case.T, case.H
+    buf = torch.empty((T + extra, H, case.out_dim), dtype=torch.bfloat16, device="cuda")
+    buf.view(torch.int16).fill_(POISON_OUT)
+    say(f"[gpu] {case.name}: T={T} H={H} L={case.kv_latent_dim} rope={case.d_rope} copy={case.copy_rope}")
+    mp.mla_absorb_q(t["q"], t["w_uk"], buf[:T], d_nope=case.d_nope, copy_rope=case.copy_rope)
+    torch.cuda.synchronize()
+    return buf
+
+
+def _check(case, extra=3):
+    buf = _run(case, extra)
+    T, NL = case.T, case.kv_latent_dim
+    lat, rope = oracle.absorb_q(case)
+    got = buf[:T, :, :NL].double().cpu().numpy()
+    check_close(got.reshape(T, -1), lat.reshape(T, -1), BF16_TOL, f"{case.name} q_latent")
+    bits = to_bits(buf)
+    if case.copy_rope:
+        assert np.array_equal(bits[:T, :, NL:], rope)
+    assert np.all(bits[T:] == POISON_OUT)
+    return buf
+
+
+@pytest.mark.parametrize("T,H,L,dr", [(1, 8, 512, 64), (128, 16, 512, 64), (129, 3, 256, 64), (300, 9, 128, 32),
+                                      (64, 128, 512, 64)])
+def test_full_compare(T, H, L, dr):
+    _check(W.absorb_case(f"ab_{T}_{H}_{L}_{dr}", seed=T + H, T=T, H=H, kv_latent_dim=L, d_rope=dr))
+
+
+def test_without_rope_copy_and_without_rope():
+    _check(W.absorb_case("ab_nocopy", seed=40, T=77, H=5, copy_rope=False))
+    _check(W.absorb_case("ab_norope", seed=41, T=33, H=4, d_rope=0))
+
+
+def test_many_chunks():
+    """Prefill-sized T: several 128-row chunks per block, with a ragged last one."""
+    _check(W.absorb_case("ab_long", seed=42, T=1000, H=12, kv_latent_dim=512), extra=0)
+
+
+def test_selection_weight_is_exact():
+    """w_uk[h, c, d] = 1 where d = (c + 3h) % 128: every latent output is a query
+    value, exactly (one nonzero term)."""
+    c = W.absorb_case("ab_sel", seed=43, T=50, H=10, kv_latent_dim=256)
+    w = np.zeros((c.H, c.kv_latent_dim, 128), np.float32)
+    for h in range(c.H):
+        w[h, np.arange(c.kv_latent_dim), (np.arange(c.kv_latent_dim) + 3 * h) % 128] = 1.0
+    c.w_uk = W.to_bf16_bits(w)
+    buf = _check(c)
+    lat, _ = oracle.absorb_q(c)
+    assert np.array_equal(buf[:c.T, :, :c.kv_latent_dim].double().cpu().numpy(), lat)
+
+
+def test_c7_decode_batch():
+    _check(W.c7_absorb(), extra=0)
