@@ -27,7 +27,9 @@ The JSON line also carries the other rows of the path, each timed the same way:
 
 Timing: HIP events recorded on the stream the library launches on (torch's
 current stream), per launch and around the whole timed region, bracketed by
-torch.cuda.synchronize().  The CPU baseline times the oracle on the host cores
+torch.cuda.synchronize().  The untimed warmup is W calls, continued until the
+GPU has been busy for 0.2 s (its clock ramps up over the first tens of ms after
+the host-side set-up); `warmup_run` reports how many calls that took.  The CPU baseline times the oracle on the host cores
 on a bounded sample of the same workload and is a reported baseline only.
 """
 import argparse
@@ -83,14 +85,27 @@ def traffic_from_profile(kernel, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+WARM_SECONDS = 0.2   # the GPU's clock ramps up over some tens of ms after host-side set-up
+
+
 class Timed:
-    """Run fn() warmup + steps times on the current stream with HIP events."""
+    """Run fn() warmup + steps times on the current stream with HIP events.
+
+    The untimed warmup is `warmup` calls, continued until they have kept the
+    GPU busy for WARM_SECONDS: timed right after the inputs are built, the
+    first ~30 ms of calls run several per cent slow while the clock ramps up."""
 
     def __init__(self, torch, fn, steps, warmup):
         self.torch = torch
         stream = torch.cuda.current_stream()
-        for _ in range(warmup):
+        w0 = time.perf_counter()
+        n = 0
+        while n < warmup or time.perf_counter() - w0 < WARM_SECONDS:
             fn()
+            n += 1
+            if n % 8 == 0 or n == warmup:
+                torch.cuda.synchronize()
+        self.warmup_run = n
         torch.cuda.synchronize()
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -365,7 +380,7 @@ def main():
     rows_per_s = case.M * args.steps / (tm.total_ms * 1e-3)
     result = {
         "metric": METRIC, "value": round(rows_per_s, 1), "unit": "rows/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(tm.ms_per_step, 4),
+        "steps": args.steps, "warmup": args.warmup, "warmup_run": tm.warmup_run, "ms_per_step": round(tm.ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "c1_decode: bf16 decode-sized batch, 64 requests with cached lengths "
