@@ -92,15 +92,17 @@ class Timed:
     """Run fn() warmup + steps times on the current stream with HIP events.
 
     The untimed warmup is `warmup` calls, continued until they have kept the
-    GPU busy for WARM_SECONDS: timed right after the inputs are built, the
+    GPU busy for warm_seconds: timed right after the inputs are built, the
     first ~30 ms of calls run several per cent slow while the clock ramps up."""
+
+    warm_seconds = WARM_SECONDS
 
     def __init__(self, torch, fn, steps, warmup):
         self.torch = torch
         stream = torch.cuda.current_stream()
         w0 = time.perf_counter()
         n = 0
-        while n < warmup or time.perf_counter() - w0 < WARM_SECONDS:
+        while n < warmup or time.perf_counter() - w0 < Timed.warm_seconds:
             fn()
             n += 1
             if n % 8 == 0 or n == warmup:
@@ -329,6 +331,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warm-seconds", type=float, default=WARM_SECONDS,
+                    help="keep warming up until the GPU has been busy this long (0: exactly --warmup calls)")
     ap.add_argument("--rows", choices=["all", "main"], default="all",
                     help="also time the other rows of the path (default) or only the main workload")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -336,6 +340,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
+    Timed.warm_seconds = args.warm_seconds
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the path is measured on a single MI355X; "
               "multi-GPU sharding is a design note, not a measured configuration.", file=sys.stderr)

@@ -49,7 +49,8 @@ __device__ inline Segment segment_of(const GemmParams& P, int tn)
 // runs all N-tiles of an M-tile side by side, so each activation tile is
 // fetched from HBM once and the whole weight, small enough for the last-level
 // cache, is re-read from there.  Suits long activation rows with few N-tiles
-// (the kv projection: 8 KB rows, 8 N-tiles).
+// (the kv projection: 8 KB rows, 8 N-tiles) and weights that fit in an XCD's
+// L2 (a decompress weight of at most 2 MiB).
 // xcd_map 3 (two projections, weight-stationary in two passes): XCD x walks the
 // M-tiles over its eighth of the first projection's N-tiles, then over its
 // eighth of the second's, so only one projection's eighth of the weight has to
@@ -186,6 +187,11 @@ inline GemmParams make_gemm_params(const DecompressArgs& a, int BM, int BN, int 
     if (a.N2 > 0) {   // the first projection's width is then a multiple of BN
         P.tiles_n += (a.N2 + BN - 1) / BN;
         P.xcd_map = (P.tiles_n1 % 8 == 0 && (P.tiles_n - P.tiles_n1) % 8 == 0 && cus % 8 == 0) ? 3 : 0;
+    } else if ((int64_t)a.N * a.K * 2 <= (int64_t(2) << 20) && cus % 8 == 0) {
+        // The whole weight fits in half of one XCD's L2 (a tensor-parallel
+        // share of the heads): each XCD owns whole M-tiles, so every activation
+        // row is read from HBM once instead of once per XCD.
+        P.xcd_map = 2;
     } else {
         P.xcd_map = (P.tiles_n % 8 == 0 && cus % 8 == 0) ? 1 : 0;
     }
