@@ -296,6 +296,27 @@ def absorb_q(case):
     return out, rope
 
 
+def absorb_q_fp8(case):
+    """(latent part binary64 [T, H, kv_latent_dim], rope bits or None, query codes
+    uint8 [T, H, d_nope], query scales float32 [T, H]): the fp8 form of query
+    absorption (page "mla_prefill_decode_graph_fp8": w_uk in fp8_dtype with
+    w_uk_scale, granularities m 1, n 128, k 128).  Each head's non-rope query
+    part is quantised per 1 x 128 block like the decompress activations, then
+    multiplied block by block with the e4m3 w_uk of that head and both scales."""
+    T, H, _ = case.q.shape
+    DN, NL = case.d_nope, case.kv_latent_dim
+    out = np.empty((T, H, NL), np.float64)
+    codes = np.empty((T, H, DN), np.uint8)
+    scales = np.empty((T, H), np.float32)
+    for h in range(H):
+        qa, sa = quantize_e4m3_rows(np.ascontiguousarray(case.q[:, h, :DN]), DN, 128)
+        codes[:, h], scales[:, h] = qa, sa[:, 0]
+        out[:, h, :] = fp8_matmul_nt(qa, sa, np.ascontiguousarray(case.w_q[h]),
+                                     np.ascontiguousarray(case.w_scale[h]), 128, 128)
+    rope = np.ascontiguousarray(case.q[:, :, DN:]) if case.copy_rope else None
+    return out, rope, codes, scales
+
+
 def decompress_kv(case_k, case_v, rows=None):
     """(k_latent bits, k_buffer rows, v_buffer rows), binary64 products.
 

@@ -412,6 +412,8 @@ class AbsorbCase:
     w_uk: np.ndarray       # uint16 bf16 bits [H, kv_latent_dim, d_nope]
     d_nope: int
     copy_rope: bool = True
+    w_q: Optional[np.ndarray] = None       # e4m3 form: uint8 codes [H, kv_latent_dim, d_nope]
+    w_scale: Optional[np.ndarray] = None   # float32 [H, kv_latent_dim / 128, d_nope / 128]
 
     @property
     def T(self) -> int: return self.q.shape[0]
@@ -426,13 +428,18 @@ class AbsorbCase:
 
 
 def absorb_case(name, *, seed, T, H=128, d_nope=128, d_rope=64, kv_latent_dim=512, w_std=0.05,
-                copy_rope=True) -> AbsorbCase:
+                copy_rope=True, fp8=False) -> AbsorbCase:
     """Queries bf16 N(0, 1) [T, H, d_nope + d_rope]; w_uk bf16 N(0, w_std)
-    [H, kv_latent_dim, d_nope]."""
+    [H, kv_latent_dim, d_nope].  fp8: w_uk as e4m3 codes of N(0, 1) with fp32
+    scales U[0.04, 0.06] per 128 x 128 block of each head (about N(0, 0.05))."""
     rng = np.random.default_rng(seed)
     q = to_bf16_bits(rng.standard_normal((T, H, d_nope + d_rope), dtype=np.float32))
     w = to_bf16_bits(rng.standard_normal((H, kv_latent_dim, d_nope), dtype=np.float32) * np.float32(w_std))
-    return AbsorbCase(name, q, w, d_nope, copy_rope)
+    case = AbsorbCase(name, q, w, d_nope, copy_rope)
+    if fp8:
+        case.w_q = to_e4m3_bits(rng.standard_normal((H, kv_latent_dim, d_nope), dtype=np.float32))
+        case.w_scale = rng.uniform(0.04, 0.06, size=(H, -(-kv_latent_dim // 128), -(-d_nope // 128))).astype(np.float32)
+    return case
 
 
 def c7_absorb(seed=7) -> AbsorbCase:
@@ -441,8 +448,17 @@ def c7_absorb(seed=7) -> AbsorbCase:
     return absorb_case("c7_absorb", seed=seed, T=128)
 
 
+def c7_absorb_fp8(seed=7) -> AbsorbCase:
+    """c7_absorb with an e4m3 w_uk and its 128 x 128 block scales."""
+    return absorb_case("c7_absorb_fp8", seed=seed, T=128, fp8=True)
+
+
 def device_absorb(case: AbsorbCase, device="cuda"):
-    return {"q": _bits_to_torch(case.q, device), "w_uk": _bits_to_torch(case.w_uk, device)}
+    t = {"q": _bits_to_torch(case.q, device), "w_uk": _bits_to_torch(case.w_uk, device)}
+    if case.w_q is not None:
+        t["w_uk_e4m3"] = _bits_to_torch(case.w_q, device)
+        t["w_uk_scale"] = torch.from_numpy(np.ascontiguousarray(case.w_scale)).to(device)
+    return t
 
 
 # --------------------------------------------------------------------------
