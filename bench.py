@@ -21,7 +21,8 @@ The JSON line also carries the other rows of the path, each timed the same way:
   c5_latent_write  RMSNorm + rope rotation + scatter of 88994 new tokens'
                rows into the MLA pages (HBM-bound)
   c7_absorb    query absorption for a decode batch of 128 tokens x 128 heads
-               (w_uk [128, 512, 128]; HIP-graph replay like p64/p256)
+               (w_uk [128, 512, 128]; HIP-graph replay like p64/p256), and
+               c7_absorb_fp8 with an e4m3 w_uk and 128x128 block scales
   p64, p256    1 and 4 newest rows per request of the decode batch (weight-bound;
                timed by HIP-graph replay over 32 weight copies, see probe_row)
 
@@ -59,6 +60,7 @@ KERNEL_SOURCES = {
     "decompress_small_bf16": ("decompress_small.hip",),
     "latent_write_kernel": ("latent_write.hip",),
     "absorb_bf16": ("absorb.hip",),
+    "absorb_fp8": ("absorb.hip",),
 }
 
 
@@ -245,18 +247,21 @@ def probe_row(torch, mp, W, pc, warmup, copies=32, reps=20):
             "timing": f"HIP graph of {copies} launches on {copies} weight copies, replayed {reps} times"}
 
 
-def absorb_row(torch, mp, W, warmup, copies=32, reps=20):
+def absorb_row(torch, mp, W, warmup, copies=32, reps=20, fp8=False):
     """Query absorption for a decode batch (a few microseconds per call), timed
     like the few-rows probes: `copies` launches on their own copies of w_uk
     (16 MiB each, so every launch reads its weight from HBM), captured in one
     HIP graph and replayed `reps` times; checked against an eager call first."""
-    c = W.c7_absorb()
+    c = W.c7_absorb_fp8() if fp8 else W.c7_absorb()
     t = W.device_absorb(c)
     out = torch.empty((c.T, c.H, c.out_dim), dtype=torch.bfloat16, device="cuda")
-    weights = [t["w_uk"].clone() for _ in range(copies)]
+    weights = [t["w_uk_e4m3" if fp8 else "w_uk"].clone() for _ in range(copies)]
 
     def call(w):
-        mp.mla_absorb_q(t["q"], w, out, d_nope=c.d_nope, copy_rope=c.copy_rope)
+        if fp8:
+            mp.mla_absorb_q_fp8(t["q"], w, t["w_uk_scale"], out, d_nope=c.d_nope, copy_rope=c.copy_rope)
+        else:
+            mp.mla_absorb_q(t["q"], w, out, d_nope=c.d_nope, copy_rope=c.copy_rope)
     call(weights[0])
     torch.cuda.synchronize()
     eager = out.clone()
@@ -275,7 +280,7 @@ def absorb_row(torch, mp, W, warmup, copies=32, reps=20):
         g.replay()
     torch.cuda.synchronize()
     if not torch.equal(out.view(torch.int16), eager.view(torch.int16)):
-        raise RuntimeError("c7_absorb: graph replay differs from the eager call")
+        raise RuntimeError(f"{c.name}: graph replay differs from the eager call")
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -285,15 +290,18 @@ def absorb_row(torch, mp, W, warmup, copies=32, reps=20):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / (reps * copies)
     T, H, L, Dq = c.T, c.H, c.kv_latent_dim, c.q.shape[2]
-    b = H * L * c.d_nope * 2 + T * H * Dq * 2 + T * H * c.out_dim * 2
+    wb = H * L * c.d_nope + c.w_scale.nbytes if fp8 else H * L * c.d_nope * 2
+    b = wb + T * H * Dq * 2 + T * H * c.out_dim * 2
     gbs = b / (ms * 1e-3) / 1e9
+    kern = "absorb_fp8" if fp8 else "absorb_bf16"
     del g, weights
     return {"tokens": T, "heads": H, "us_per_call": round(ms * 1e3, 3),
             "tflops": round(2.0 * T * H * L * c.d_nope / (ms * 1e-3) / 1e12, 2),
-            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", traffic_from_profile("absorb_bf16", "c7_absorb")),
-            "kernel": "absorb_bf16",
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", traffic_from_profile(kern, c.name)),
+            "kernel": kern,
             "timing": f"HIP graph of {copies} launches on {copies} weight copies, replayed {reps} times",
-            "note": "algorithmic bytes: w_uk once (16 MiB), the queries (nope + rope) once, the output once"}
+            "note": "algorithmic bytes: w_uk once (16 MiB bf16, 8 MiB e4m3 + scales), the queries (nope + rope) "
+                    "once, the output once"}
 
 
 def roofline(bound, achieved, peak, unit, traffic):
@@ -540,10 +548,11 @@ def main():
                                    "note": "per token: read the 1152-byte row and its 256-byte rope table row, "
                                            "write the 1152-byte cache row"}
         print(f"[bench] c5_latent_write: {t.avg_launch_ms:.4f} ms, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
-        rows["c7_absorb"] = absorb_row(torch, mp, W, args.warmup)
-        r = rows["c7_absorb"]
-        print(f"[bench] c7_absorb: {r['us_per_call']:.2f} us/call (graph replay), "
-              f"{r['roofline']['achieved']:.0f} GB/s", file=sys.stderr, flush=True)
+        for name, f8 in (("c7_absorb", False), ("c7_absorb_fp8", True)):
+            rows[name] = absorb_row(torch, mp, W, args.warmup, fp8=f8)
+            r = rows[name]
+            print(f"[bench] {name}: {r['us_per_call']:.2f} us/call (graph replay), "
+                  f"{r['roofline']['achieved']:.0f} GB/s", file=sys.stderr, flush=True)
         result["rows"] = rows
 
     if args.cpu_seconds > 0:

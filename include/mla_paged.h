@@ -351,6 +351,28 @@ mla_status_t mla_absorb_q(const void* q, int32_t total_tokens, int32_t num_heads
                           void* q_latent, void* stream);
 
 /*
+ * The fp8 form of mla_absorb_q (page "mla_prefill_decode_graph_fp8": w_uk in
+ * fp8_dtype with w_uk_scale, Parameters m/n/k_scale_granularity).  The non-rope
+ * part of each query head is quantised per 1 x 128 block as in
+ * mla_decompress_k_paged_fp8 (s_q = amax / 448, codes = e4m3fn(x * (448 / amax)),
+ * binary32 quotients, round to nearest even; an all-zero block takes s_q = 1):
+ *
+ *   q_latent[t][h][c] = bf16( s_q[t][h] * w_uk_scale[h][c / 128][0]
+ *                             * sum_{d < 128} codes[t][h][d] * w_uk_e4m3[h][c][d] )
+ *
+ * with fp32 accumulation; the rope part as in mla_absorb_q.
+ *
+ * w_uk_e4m3     [device] e4m3fn codes [num_heads][kv_latent_dim][d_nope], 16-byte aligned
+ * w_uk_scale    [device] float [num_heads][kv_latent_dim / 128][d_nope / 128], 4-byte aligned
+ * m_gran, n_gran, k_gran  supported: 1, 128, 128
+ * Other arguments, limits and errors as in mla_absorb_q.
+ */
+mla_status_t mla_absorb_q_fp8(const void* q, int32_t total_tokens, int32_t num_heads, int32_t d_nope,
+                              int32_t d_rope, const void* w_uk_e4m3, const float* w_uk_scale,
+                              int32_t kv_latent_dim, int32_t m_gran, int32_t n_gran, int32_t k_gran,
+                              int32_t copy_rope, void* q_latent, void* stream);
+
+/*
  * The latent write path: new tokens' latent rows, normalised and rotated, into
  * the MLA cache pages this library's decompress calls read (page
  * "mla_prefill_decode_graph_fp8", Args kv_input_fn (the latent values,

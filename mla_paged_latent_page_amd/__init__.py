@@ -11,7 +11,7 @@ Entry points (same names as the C ABI):
   mla_decompress_kv_paged(_fp8)  one gather, K and V up-projections
   mla_decompress_k_paged_fp8_cache  the fp8 form on an e4m3 cache with per-128-column scales
   mla_write_latent_paged       RMSNorm + rope rotation of new tokens' rows into the cache pages
-  mla_absorb_q                 per-head product of the non-rope query columns with w_uk (decode)
+  mla_absorb_q(_fp8)           per-head product of the non-rope query columns with w_uk (decode)
   kv_matmul_paged              project hidden states and write them into K/V cache pages
   mla_gather_latent_paged      the gather step alone
   mla_latent_matmul            the up-projection step alone (rows already gathered)
@@ -36,7 +36,7 @@ EXPORTS = ("mla_paged_cache_default_strides", "mla_decompress_k_paged", "mla_gat
            "mla_latent_matmul", "mla_decompress_k_paged_fp8_workspace_size", "mla_decompress_k_paged_fp8",
            "kv_matmul_paged", "mla_check_indices", "mla_status_string", "mla_last_hip_error",
            "mla_abi_version", "mla_decompress_kv_paged", "mla_decompress_kv_paged_fp8",
-           "mla_write_latent_paged", "mla_decompress_k_paged_fp8_cache", "mla_absorb_q")
+           "mla_write_latent_paged", "mla_decompress_k_paged_fp8_cache", "mla_absorb_q", "mla_absorb_q_fp8")
 
 
 class MlaError(RuntimeError):
@@ -106,6 +106,8 @@ def lib():
             L.mla_decompress_k_paged_fp8_cache.restype = i32
             L.mla_absorb_q.argtypes = [vp, i32, i32, i32, i32, vp, i32, i32, vp, vp]
             L.mla_absorb_q.restype = i32
+            L.mla_absorb_q_fp8.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+            L.mla_absorb_q_fp8.restype = i32
             L.kv_matmul_paged.argtypes = [vp, vp, i32, i32, vp, ctypes.POINTER(CacheDesc), u32, vp]
             L.kv_matmul_paged.restype = i32
             L.mla_gather_latent_paged.argtypes = [vp, vp, i32, ctypes.POINTER(CacheDesc), u32, vp, vp]
@@ -407,6 +409,30 @@ def mla_absorb_q(q, w_uk, q_latent, d_nope: int = 128, copy_rope: bool = True, s
     st = lib().mla_absorb_q(q.data_ptr(), T, H, int(d_nope), int(d_rope), w_uk.data_ptr(), int(L),
                             1 if copy_rope else 0, q_latent.data_ptr(), _stream(stream))
     _check(st, "mla_absorb_q")
+
+
+def mla_absorb_q_fp8(q, w_uk_e4m3, w_uk_scale, q_latent, d_nope: int = 128, copy_rope: bool = True,
+                     stream=None) -> None:
+    """The fp8 form: each head's non-rope query part quantised per 1x128 block,
+    times the e4m3 w_uk with its 128x128 block scales."""
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [T, H, d_nope + d_rope] tensor")
+    if w_uk_e4m3.dim() != 3 or not w_uk_e4m3.is_contiguous() or w_uk_e4m3.element_size() != 1:
+        raise ValueError("w_uk_e4m3 must be a contiguous 1-byte [H, kv_latent_dim, d_nope] tensor")
+    T, H, Dq = q.shape
+    if w_uk_e4m3.shape[0] != H or w_uk_e4m3.shape[2] != d_nope:
+        raise ValueError(f"w_uk_e4m3 must be [{H}, kv_latent_dim, {d_nope}]")
+    L = w_uk_e4m3.shape[1]
+    if w_uk_scale.numel() < H * (-(-L // 128)) * (-(-d_nope // 128)) or w_uk_scale.element_size() != 4:
+        raise ValueError("w_uk_scale must hold float32 [H, kv_latent_dim / 128, d_nope / 128]")
+    d_rope = Dq - d_nope
+    Do = L + (d_rope if copy_rope else 0)
+    if tuple(q_latent.shape) != (T, H, Do) or not q_latent.is_contiguous():
+        raise ValueError(f"q_latent must be a contiguous [{T}, {H}, {Do}] tensor")
+    st = lib().mla_absorb_q_fp8(q.data_ptr(), T, H, int(d_nope), int(d_rope), w_uk_e4m3.data_ptr(),
+                                w_uk_scale.data_ptr(), int(L), 1, 128, 128, 1 if copy_rope else 0,
+                                q_latent.data_ptr(), _stream(stream))
+    _check(st, "mla_absorb_q_fp8")
 
 
 def mla_write_latent_paged(kv_input, input_row_offsets, kv_norm_gamma, epsilon: float, freqs_cis, K: int,

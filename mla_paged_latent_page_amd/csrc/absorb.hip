@@ -121,7 +121,161 @@ __global__ void __launch_bounds__(AB_NT, 2) absorb_bf16(AbsorbArgs a)
     }
 }
 
+// The fp8 form (w_uk in e4m3 with fp32 scales per 128 x 128 block of each
+// head; the query's non-rope part quantised per 1 x 128 block like the
+// decompress activations: s_q = amax / 448, codes = e4m3(x * (448 / amax))):
+//   out[t][h][c] = bf16( s_q[t][h] * w_uk_scale[h][c / 128][0]
+//                        * sum_{d < 128} codes_q[t][h][d] * w_uk[h][c][d] )
+// Same blocks as the bf16 form.  Each block quantises its query chunk in LDS
+// (16 lanes per row, amax by a 16-lane butterfly), then runs
+// v_mfma_scale_f32_32x32x64_f8f6f4 with unit E8M0 scales: the 128 columns are
+// one scale block, so the epilogue applies s_q * s_w once.  fp8 tile rows are
+// 128 bytes, 8 granules XOR-swizzled by (row / 2) % 8.
+constexpr int AF_ROWB = AB_K;
+
+__device__ inline int f8_granule(int row, int g) { return (g ^ ((row >> 1) & 7)) * 16; }
+
+__device__ inline i32x8 join16(u32x4 lo, u32x4 hi)
+{
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+__global__ void __launch_bounds__(AB_NT, 2) absorb_fp8(AbsorbArgs a)
+{
+    __shared__ __attribute__((aligned(1024))) char wt[AB_N * AF_ROWB];   // weight codes
+    __shared__ __attribute__((aligned(1024))) char at[AB_M * AB_ROWB];   // bf16 query rows
+    __shared__ __attribute__((aligned(1024))) char qt[AB_M * AF_ROWB];   // query codes
+    __shared__ float qsc[AB_M];                                          // query scales
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tpn = a.NL / AB_N;
+    const int j = (int)(blockIdx.x >> 3);
+    const int nt = j % tpn, h = (j / tpn) * 8 + (int)(blockIdx.x & 7);
+    if (h >= a.H)
+        return;
+    const int n0 = nt * AB_N;
+    const uint32_t wt_lds = lds_addr(wt), at_lds = lds_addr(at);
+
+    // Weight codes: rows n0 .. n0 + 127 of head h (16 KB).  One load = 8 rows:
+    // lane l fills physical granule l % 8 of row 8 i + l / 8.
+    const i32x4 wr = make_srd(a.wq + ((int64_t)h * a.NL + n0) * AB_K, (uint32_t)(AB_N * AF_ROWB));
+    {
+        const int fr = lane >> 3, fg = lane & 7;
+        for (int i = wave; i < AB_N / 8; i += 4) {
+            const int row = 8 * i + fr;
+            asm_ld16_lds(wr, wt_lds + i * 1024, (uint32_t)(row * AF_ROWB + ((fg ^ ((row >> 1) & 7)) * 16)), 0u);
+        }
+    }
+    const float sw = a.wscale[(int64_t)h * tpn + nt];
+    const int lr = lane >> 4, lg = lane & 15;
+    const i32x4 qr = make_srd(a.q, (uint32_t)((int64_t)a.T * a.H * a.Dq * 2));
+    auto load_chunk = [&](int t0) __attribute__((always_inline)) {
+        for (int i = wave; i < AB_M / 4; i += 4) {
+            const int row = 4 * i + lr;
+            const uint32_t off = (uint32_t)(((int64_t)(t0 + row) * a.H + h) * a.Dq * 2);
+            asm_ld16_lds(qr, at_lds + i * 1024, off + (uint32_t)((lg ^ (row & 15)) * 16), 0u);
+        }
+    };
+    load_chunk(0);
+
+    const int frow = lane & 31, half = lane >> 5;
+    const int wrow = wave * 32 + frow;
+    uint16_t* out = a.out;
+    for (int t0 = 0; t0 < a.T; t0 += AB_M) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        // Quantise the chunk: lanes 16 k .. 16 k + 15 hold row 16 p + 4 wave + k,
+        // 8 values each (one granule of the bf16 row).
+#pragma unroll
+        for (int p = 0; p < AB_M / 16; ++p) {
+            const int r = 16 * p + 4 * wave + lr;
+            const u32x4 v = lds_ld16(at + r * AB_ROWB + ((lg ^ (r & 15)) * 16));
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = bf16_lo(v[i]);
+                x[2 * i + 1] = bf16_hi(v[i]);
+            }
+            float am = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                am = fmaxf(am, fabsf(x[i]));
+            am = fmaxf(am, __shfl_xor(am, 1));
+            am = fmaxf(am, __shfl_xor(am, 2));
+            am = fmaxf(am, __shfl_xor(am, 4));
+            am = fmaxf(am, __shfl_xor(am, 8));
+            float sq = 1.0f, inv = 1.0f;
+            if (am > 0.0f) {
+                sq = am / 448.0f;
+                inv = 448.0f / am;
+            }
+            const u32x2 codes = {pack_e4m3x2(x[0] * inv, x[1] * inv) | (pack_e4m3x2(x[2] * inv, x[3] * inv) << 16),
+                                 pack_e4m3x2(x[4] * inv, x[5] * inv) | (pack_e4m3x2(x[6] * inv, x[7] * inv) << 16)};
+            lds_st8(qt + r * AF_ROWB + f8_granule(r, lg >> 1) + (lg & 1) * 8, codes);
+            if (lg == 0)
+                qsc[r] = sq;
+        }
+        lds_barrier();
+        f32x16 acc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc[i] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int g0 = 4 * kk + 2 * half;   // lane's 32 codes: granules g0, g0 + 1
+            const i32x8 wf = join16(lds_ld16(wt + wrow * AF_ROWB + f8_granule(wrow, g0)),
+                                    lds_ld16(wt + wrow * AF_ROWB + f8_granule(wrow, g0 + 1)));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 32 * i + frow;
+                const i32x8 af = join16(lds_ld16(qt + r * AF_ROWB + f8_granule(r, g0)),
+                                        lds_ld16(qt + r * AF_ROWB + f8_granule(r, g0 + 1)));
+                acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, af, acc[i], 0, 0, 0, 127, 0, 127);
+            }
+        }
+        float rs[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            rs[i] = qsc[32 * i + frow] * sw;
+        lds_barrier();
+        if (t0 + AB_M < a.T)
+            load_chunk(t0 + AB_M);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 32 * i + frow;
+            if (t < a.T) {
+                uint16_t* orow = out + ((int64_t)t * a.H + h) * a.Do + n0 + 32 * wave + 4 * half;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x2 v = {pack_bf16x2(acc[i][4 * q] * rs[i], acc[i][4 * q + 1] * rs[i]),
+                                     pack_bf16x2(acc[i][4 * q + 2] * rs[i], acc[i][4 * q + 3] * rs[i])};
+                    *reinterpret_cast<u32x2*>(orow + 8 * q) = v;
+                }
+            }
+        }
+        if (a.R > 0 && nt == 0) {
+            const int gpr = a.R / 8;
+            for (int idx = tid; idx < AB_M * gpr; idx += AB_NT) {
+                const int r = idx / gpr, g = idx - r * gpr;
+                const int t = t0 + r;
+                if (t < a.T) {
+                    const int64_t th = (int64_t)t * a.H + h;
+                    st16(out + th * a.Do + a.NL + g * 8, ld16(a.q + th * a.Dq + AB_K + g * 8));
+                }
+            }
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_absorb_fp8(const AbsorbArgs& a, hipStream_t s)
+{
+    const int heads8 = (a.H + 7) / 8 * 8;
+    hipLaunchKernelGGL(absorb_fp8, dim3(heads8 * (a.NL / AB_N)), dim3(AB_NT), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_absorb_bf16(const AbsorbArgs& a, hipStream_t s)
 {

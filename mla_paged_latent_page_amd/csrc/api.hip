@@ -520,6 +520,42 @@ MLA_API mla_status_t mla_absorb_q(const void* q, int32_t total_tokens, int32_t n
     return e == hipSuccess ? MLA_OK : hip_failed(e);
 }
 
+MLA_API mla_status_t mla_absorb_q_fp8(const void* q, int32_t total_tokens, int32_t num_heads, int32_t d_nope,
+                                      int32_t d_rope, const void* w_uk_e4m3, const float* w_uk_scale,
+                                      int32_t kv_latent_dim, int32_t m_gran, int32_t n_gran, int32_t k_gran,
+                                      int32_t copy_rope, void* q_latent, void* stream)
+{
+    const int32_t T = total_tokens;
+    const bool work = T > 0;
+    if (work && (!q || !w_uk_e4m3 || !w_uk_scale || !q_latent))
+        return MLA_ERR_NULL_POINTER;
+    const int64_t Dq = (int64_t)d_nope + d_rope;
+    if (T < 0 || num_heads <= 0 || d_nope != 128 || d_rope < 0 || d_rope % 8 || kv_latent_dim <= 0 ||
+        kv_latent_dim % 128 || m_gran != 1 || n_gran != 128 || k_gran != 128 || (copy_rope != 0 && copy_rope != 1) ||
+        ((int64_t)T + 128) * num_heads * Dq * 2 >= (int64_t(1) << 31))
+        return MLA_ERR_INVALID_SHAPE;
+    if (!aligned16(q) || !aligned16(w_uk_e4m3) || !aligned16(q_latent) ||
+        (reinterpret_cast<uintptr_t>(w_uk_scale) & 3u))
+        return MLA_ERR_MISALIGNED;
+    if (!work)
+        return MLA_OK;
+    if (mla_status_t st = check_device())
+        return st;
+    mla::AbsorbArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.wq = static_cast<const uint8_t*>(w_uk_e4m3);
+    a.wscale = w_uk_scale;
+    a.out = static_cast<uint16_t*>(q_latent);
+    a.T = T;
+    a.H = num_heads;
+    a.NL = kv_latent_dim;
+    a.Dq = (int)Dq;
+    a.R = copy_rope ? d_rope : 0;
+    a.Do = kv_latent_dim + a.R;
+    const hipError_t e = mla::launch_absorb_fp8(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MLA_OK : hip_failed(e);
+}
+
 MLA_API mla_status_t mla_write_latent_paged(const void* kv_input, const uint32_t* input_row_offsets,
                                             int32_t total_tokens, const float* kv_norm_gamma, float epsilon,
                                             const float* freqs_cis, int32_t max_seq_len, int32_t K,

@@ -61,12 +61,15 @@ struct LatentWriteArgs {
 struct AbsorbArgs {
     const uint16_t* q;         // bf16 [T][H][Dq]: 128 nope columns, then rope
     const uint16_t* w;         // w_uk bf16 [H][NL][128]
+    const uint8_t* wq;         // fp8 form: w_uk e4m3 codes [H][NL][128]
+    const float* wscale;       // fp8 form: [H][NL / 128] (one 128 x 128 block per latent tile)
     uint16_t* out;             // bf16 [T][H][Do]: NL latent columns, then R rope columns
     int T, H, NL, Dq, Do, R;   // R: rope columns copied (0: none)
 };
 
 hipError_t launch_gather_rows(const DecompressArgs& a, int elem_bytes, hipStream_t s);
 hipError_t launch_absorb_bf16(const AbsorbArgs& a, hipStream_t s);
+hipError_t launch_absorb_fp8(const AbsorbArgs& a, hipStream_t s);
 hipError_t launch_latent_write(const LatentWriteArgs& a, hipStream_t s);
 hipError_t launch_product_bf16(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_product_f32(const DecompressArgs& a, hipStream_t s);

@@ -365,3 +365,24 @@ def test_absorb_error_paths(lib):
     assert absorb(lib, T=0, q=None, w=None, out=None) == OK
     assert absorb(lib, dr=0, copy=0) == DEV
     assert absorb(lib) == DEV
+
+
+def absorb_fp8(lib, T=64, H=16, dn=128, dr=64, L=512, grans=(1, 128, 128), copy=1, **ptrs):
+    p = dict(q=FAKE, w=FAKE, ws=FAKE, out=FAKE)
+    p.update(ptrs)
+    return lib.mla_absorb_q_fp8(p["q"], T, H, dn, dr, p["w"], p["ws"], L, *grans, copy, p["out"], None)
+
+
+def test_absorb_fp8_error_paths(lib):
+    for k in ("q", "w", "ws", "out"):
+        assert absorb_fp8(lib, **{k: None}) == NULLP
+    assert absorb_fp8(lib, T=-1) == SHAPE
+    assert absorb_fp8(lib, dn=256) == SHAPE
+    assert absorb_fp8(lib, L=384 + 64) == SHAPE
+    for g in ((2, 128, 128), (1, 64, 128), (1, 128, 64)):
+        assert absorb_fp8(lib, grans=g) == SHAPE
+    assert absorb_fp8(lib, copy=-1) == SHAPE
+    assert absorb_fp8(lib, w=FAKE + 4) == MISAL
+    assert absorb_fp8(lib, ws=FAKE + 1) == MISAL
+    assert absorb_fp8(lib, T=0, q=None, w=None, ws=None, out=None) == OK
+    assert absorb_fp8(lib) == DEV

@@ -73,3 +73,58 @@ def test_selection_weight_is_exact():
 
 def test_c7_decode_batch():
     _check(W.c7_absorb(), extra=0)
+
+
+def _check_fp8(case, extra=3):
+    t = W.device_absorb(case)
+    T, H, NL = case.T, case.H, case.kv_latent_dim
+    buf = torch.empty((T + extra, H, case.out_dim), dtype=torch.bfloat16, device="cuda")
+    buf.view(torch.int16).fill_(POISON_OUT)
+    say(f"[gpu] {case.name} fp8: T={T} H={H} L={NL} rope={case.d_rope} copy={case.copy_rope}")
+    mp.mla_absorb_q_fp8(t["q"], t["w_uk_e4m3"], t["w_uk_scale"], buf[:T], d_nope=case.d_nope,
+                        copy_rope=case.copy_rope)
+    torch.cuda.synchronize()
+    lat, rope, _, _ = oracle.absorb_q_fp8(case)
+    got = buf[:T, :, :NL].double().cpu().numpy()
+    check_close(got.reshape(T, -1), lat.reshape(T, -1), BF16_TOL, f"{case.name} q_latent fp8")
+    bits = to_bits(buf)
+    if case.copy_rope:
+        assert np.array_equal(bits[:T, :, NL:], rope)
+    assert np.all(bits[T:] == POISON_OUT)
+    return buf
+
+
+@pytest.mark.parametrize("T,H,L,dr", [(1, 8, 512, 64), (128, 16, 512, 64), (129, 3, 256, 64), (300, 9, 128, 32)])
+def test_fp8_full_compare(T, H, L, dr):
+    _check_fp8(W.absorb_case(f"abf_{T}_{H}_{L}_{dr}", seed=100 + T + H, T=T, H=H, kv_latent_dim=L, d_rope=dr,
+                             fp8=True))
+
+
+def test_fp8_zero_query_blocks_and_no_rope_copy():
+    c = W.absorb_case("abf_zero", seed=130, T=40, H=5, kv_latent_dim=256, copy_rope=False, fp8=True)
+    c.q[3, 2, :128] = 0          # an all-zero block: scale 1, codes 0, output 0
+    c.q[7, :, :128] = 0
+    buf = _check_fp8(c)
+    assert torch.all(buf[3, 2, :256].float() == 0) and torch.all(buf[7, :, :256].float() == 0)
+
+
+def test_fp8_lossless_queries_match_the_dequantised_bf16_form():
+    """Query blocks that quantise losslessly (e4m3 values with the block maximum
+    at 448 * 2^e) give the product of the queries with the dequantised weight."""
+    c = W.absorb_case("abf_lossless", seed=131, T=70, H=6, kv_latent_dim=384, fp8=True)
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 0x7E, size=(c.T, c.H, 128)).astype(np.uint8)
+    vals = oracle.e4m3_decode(codes) * np.where(rng.integers(0, 2, size=codes.shape) == 1, 1.0, -1.0)
+    vals[..., 0] = 448.0
+    vals *= 2.0 ** rng.integers(-8, 2, size=(c.T, c.H, 1))
+    c.q[:, :, :128] = W.to_bf16_bits(vals.astype(np.float32))
+    buf = _check_fp8(c)
+    w = oracle.e4m3_decode(c.w_q) * np.repeat(c.w_scale.astype(np.float64), 128, axis=1)[:, :, :1]
+    plain = np.einsum("thd,hcd->thc", vals, w)
+    check_close(buf[:c.T, :, :384].double().cpu().numpy().reshape(c.T, -1), plain.reshape(c.T, -1), BF16_TOL,
+                "lossless fp8 queries vs dequantised product")
+
+
+def test_fp8_many_chunks_and_c7_shape():
+    _check_fp8(W.absorb_case("abf_long", seed=132, T=700, H=10, fp8=True), extra=0)
+    _check_fp8(W.c7_absorb_fp8(), extra=0)
