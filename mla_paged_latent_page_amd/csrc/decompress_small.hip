@@ -5,191 +5,408 @@
 //
 // With M <= 256 rows the call is bound by reading the weight (N x 512 bf16,
 // 16 MiB at N = 16384) once from HBM, so the whole weight must be in flight at
-// once and the call must be one launch.  One block of 4 waves per 64 weight
-// rows (256 blocks at N = 16384, one per CU):
-//  * waves 1..3 put the block's 64 x 512 weight tile (64 KB) in flight first,
-//    while wave 0 resolves the rows' cache addresses (one lane per request:
-//    its offsets, then the page-table entries of its rows; gathering form);
-//  * then the rows' first 512 columns, 64 columns (128 bytes) per chunk, go
-//    straight into LDS (loads with an LDS destination: the weight as a buffer,
-//    the rows by per-lane addresses, 8 rows of 128 bytes per load).  As many
-//    row chunks as fit (all 8 for 64 rows, 3 for 256) are in flight together;
-//    the rest follow as chunks are consumed;
-//  * v_mfma_f32_32x32x16_bf16 with the weight as the row operand: wave w owns
-//    weight rows 32 (w % 2) .. +32 and the 32-row blocks w/2, w/2 + 2, ... of
-//    the M rows; outputs go straight to k_buffer (4 consecutive columns per
-//    lane);
-//  * in the gathering form, block b finally copies rows b, b + grid, ... into
-//    k_latent_buffer (whole cache rows), by the lanes that loaded them.
-// All loads into LDS are issued from inline assembly and ordered by explicit
-// waits and barriers (the compiler adds none of its own for them).
+// once, the product must run while it streams in, and the call must be one
+// launch.  One block of 8 waves per 64 weight rows (256 blocks at N = 16384,
+// one per CU).  The block's 64 x 512 weight tile (64 KB) and the rows' first
+// 512 columns go into LDS in K order, in chunks of 64 columns (128-byte row
+// pieces; weight chunk q is 8 KB):
+//  * at kernel start waves 5..7 put weight chunks 0 and 1 in flight while
+//    wave 4 resolves the rows' cache addresses (one lane per request reads its
+//    offsets, then one lane per row its page-table entry) into a table in LDS;
+//  * then waves 4..7 each issue, chunk after chunk, their share of row chunk c
+//    and of weight chunk c + 2, so rows and weight arrive together in K order.
+//    A CU serves the vector loads of its waves in issue order: rows queued
+//    behind the whole weight tile would start the product only after the
+//    weight had streamed in, and a tile queued behind slow index loads would
+//    leave HBM idle.  Row chunks that do not fit in LDS at once go through a
+//    ring of slots refilled as chunks are consumed;
+//  * waves 0..3 run v_mfma_f32_32x32x16_bf16 on chunk q as soon as its pieces
+//    have landed, with the weight as the row operand: up to 160 rows, wave w
+//    owns weight rows 32 (w % 2) .. +32 and the 32-row blocks w/2, w/2 + 2, ...
+//    of the M rows; above that, both weight blocks and the M blocks w, w + 4
+//    (fewer LDS fragment reads per MFMA);
+//  * wave 4 also puts this block's share of the k_latent_buffer copy (whole
+//    cache rows r with r % grid == block) in flight into registers early and
+//    stores it at the end.
+// The accumulators go through LDS so that every k_buffer store writes whole
+// 128-byte row segments.  Loader waves order their loads against the compute
+// waves' LDS reads with explicit vmcnt waits and one barrier per chunk; the
+// loads into LDS are issued from inline assembly, so the compiler adds no
+// waits of its own for them.
 #include "launch.hpp"
 
 namespace mla {
 namespace {
 
-constexpr int SBN = 64, SNT = 256, SK = 512, SMAX_M = 256;
-constexpr int W_BYTES = SBN * SK * 2;            // 64 KB weight tile, rows of 1 KB
+constexpr int SBN = 64, SK = 512, SMAX_M = 256;
+constexpr int SNT = 512;                         // 8 waves
+constexpr int W_BYTES = SBN * SK * 2;            // 64 KB weight tile
 constexpr int CHUNK_K = 64, CHUNKS = SK / CHUNK_K, CROWB = CHUNK_K * 2;
-constexpr int A_AREA = 96 * 1024;                // row chunks (and, first, the row table)
+constexpr int W_CHUNK_BYTES = SBN * CROWB;       // 8 KB: one chunk of the weight tile
+constexpr int A_AREA = 96 * 1024;                // row chunks (first the row table, last the output staging)
+constexpr int W_LOADS = W_BYTES / 1024;          // 64 loads of 1 KB
+constexpr int W_WAVES = 3;
+// Weight chunks put in flight before the rows are: each CU serves its vector
+// loads in issue order, so the row wave's index and row loads wait behind
+// every weight load issued before them.
+constexpr int W_EARLY_CHUNKS = 2;
+constexpr int EARLY_COPY_ROWS = 2;               // k_latent_buffer rows per block copied through registers
+constexpr int EARLY_COPY_GRANULES = 128;         // up to 2048-byte cache rows
+
+// vmcnt is a 6-bit counter: a wave never has more than 63 vector memory
+// operations outstanding (issue waits instead), so a wait for at most 63
+// younger operations is the weakest one needed.
+template <int N>
+__device__ inline void vm_wait()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Loads and stores through global (not flat) addresses: pointers read back
+// from LDS are generic, and flat accesses would also count against lgkmcnt,
+// which every LDS wait here would then wait for.
+typedef __attribute__((address_space(1))) u32x4 g_u32x4;
+__device__ inline u32x4 gld16(const void* p) { return *(const g_u32x4*)p; }
+__device__ inline void gst16(void* p, u32x4 v) { *(g_u32x4*)p = v; }
 
 template <int MB>
 struct SmallCfg {
     static constexpr int ROWS = 32 * MB;                         // rows loaded (M rounded up)
     static constexpr int CHUNK_BYTES = ROWS * CROWB;
-    static constexpr int SLOTS = (A_AREA / CHUNK_BYTES) < CHUNKS ? (A_AREA / CHUNK_BYTES) : CHUNKS;
-    static constexpr int LOADS_PER_CHUNK = ROWS / 8 / 4;         // per wave (8 rows per load, 4 waves)
-    static_assert(SLOTS >= 2 && LOADS_PER_CHUNK >= 1 && ROWS % 32 == 0, "chunk ring");
-    static_assert(W_BYTES + A_AREA <= 163840 && SMAX_M * 8 <= CHUNK_BYTES * SLOTS, "LDS budget");
+    static constexpr int FIT = A_AREA / CHUNK_BYTES;
+    static constexpr bool RING = FIT < CHUNKS;
+    static constexpr int SLOTS = RING ? FIT : CHUNKS;
+    static constexpr int INITIAL = RING ? SLOTS - 1 : CHUNKS;    // chunks issued before the loop
+    static_assert(SLOTS >= 2 && ROWS % 32 == 0, "chunk ring");
+    static_assert(W_BYTES + A_AREA <= 163840 && ROWS * CROWB <= A_AREA, "LDS budget");
+    static_assert(SMAX_M * 16 <= W_CHUNK_BYTES, "row table fits in one weight chunk");
+    static_assert(W_EARLY_CHUNKS < CHUNKS, "the row table's chunk is loaded after the table is read");
 };
 
-// s_waitcnt vmcnt(n) for a value known only after unrolling.
-__device__ inline void vm_wait(int n)
+// Loader wave (each issues, per chunk c, MB row loads and then, from chunk
+// W_EARLY_CHUNKS on, two weight loads of chunk c + W_EARLY_CHUNKS): chunk q's
+// row loads and weight loads must have landed.  The weight loads of chunk q
+// went out before its row loads, so the loads still allowed in flight are the
+// ones issued after chunk q's row loads.
+template <int MB>
+constexpr int loads_after(int q)
 {
-    switch (n) {
-#define MLA_VMW(k) \
-    case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
-        MLA_VMW(1) MLA_VMW(2) MLA_VMW(3) MLA_VMW(4) MLA_VMW(5) MLA_VMW(6) MLA_VMW(7) MLA_VMW(8)
-        MLA_VMW(9) MLA_VMW(10) MLA_VMW(11) MLA_VMW(12) MLA_VMW(14) MLA_VMW(15) MLA_VMW(16)
-        MLA_VMW(18) MLA_VMW(20) MLA_VMW(21) MLA_VMW(24)
-#undef MLA_VMW
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    using C = SmallCfg<MB>;
+    const int issued = C::RING ? (C::INITIAL + q < CHUNKS ? C::INITIAL + q : CHUNKS) : CHUNKS;
+    int n = q + W_EARLY_CHUNKS < CHUNKS ? 2 : 0;
+    for (int c = q + 1; c < issued; ++c)
+        n += MB + (c + W_EARLY_CHUNKS < CHUNKS ? 2 : 0);
+    return n;
+}
+template <int MB, int Q>
+__device__ inline void wait_loads()
+{
+    vm_wait<loads_after<MB>(Q)>();
+}
+
+// Waves 0..3: the product, chunk by chunk as the pieces land, then the
+// outputs staged in LDS.  A wave owns NBW 32-row blocks of the weight tile
+// starting at block nb0 and the 32-row blocks MB0, MB0 + MSTEP, ... of the M
+// rows; every weight fragment it reads serves all its M blocks and every row
+// fragment all its weight blocks.
+template <int MB, int MB0, int MSTEP, int NBW>
+__device__ inline void compute_waves(const char* wt, char* at, int nb0, int lane)
+{
+    using C = SmallCfg<MB>;
+    constexpr int SLOTS = C::SLOTS;
+    constexpr int NBLK = MB > MB0 ? (MB - MB0 + MSTEP - 1) / MSTEP : 0;   // M blocks of this wave
+    // Independent accumulators per output block (k steps split round-robin,
+    // summed at the end), so a wave with one or two output blocks still keeps
+    // four MFMA chains in flight instead of waiting on each result.
+    constexpr int NACC = NBW * (NBLK > 0 ? NBLK : 1);
+    constexpr int KSPLIT = NACC >= 4 ? 1 : 4 / NACC;
+    const int frow = lane & 31, half = lane >> 5;
+    const int rsw = (frow >> 1) & 7;          // granule swizzle of every row this lane reads
+    f32x16 acc[KSPLIT][NBW][NBLK > 0 ? NBLK : 1];
+#pragma unroll
+    for (int s = 0; s < KSPLIT; ++s)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int i = 0; i < NBLK; ++i)
+                acc[s][j][i] = f32x16{};
+#pragma unroll
+    for (int q = 0; q < CHUNKS; ++q) {
+        lds_barrier();
+        const char* ws = wt + q * W_CHUNK_BYTES + (nb0 * 32 + frow) * CROWB;
+        const char* as = at + (q % SLOTS) * C::CHUNK_BYTES + frow * CROWB;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int g = (2 * kk + half) ^ rsw;
+            bf16x8 wf[NBW], af[NBLK > 0 ? NBLK : 1];
+#pragma unroll
+            for (int j = 0; j < NBW; ++j)
+                wf[j] = as_bf16x8(lds_ld16(ws + j * 32 * CROWB + g * 16));
+#pragma unroll
+            for (int i = 0; i < NBLK; ++i)
+                af[i] = as_bf16x8(lds_ld16(as + (MB0 + MSTEP * i) * 32 * CROWB + g * 16));
+#pragma unroll
+            for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                for (int i = 0; i < NBLK; ++i)
+                    acc[kk % KSPLIT][j][i] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], af[i], acc[kk % KSPLIT][j][i], 0, 0, 0);
+        }
     }
+    // Every wave is past its last LDS read of the chunks: stage the outputs.
+    // Lane holds rows 32 mb + frow, columns 32 nb + 8 q + 4 half + 0..3 (q < 4).
+#pragma unroll
+    for (int s = 1; s < KSPLIT; ++s)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int i = 0; i < NBLK; ++i)
+                acc[0][j][i] += acc[s][j][i];
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int i = 0; i < NBLK; ++i) {
+            const int m = (MB0 + MSTEP * i) * 32 + frow;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int g = (nb0 + j) * 4 + q;
+                const u32x2 v = {pack_bf16x2(acc[0][j][i][4 * q], acc[0][j][i][4 * q + 1]),
+                                 pack_bf16x2(acc[0][j][i][4 * q + 2], acc[0][j][i][4 * q + 3])};
+                lds_st8(at + m * CROWB + ((g ^ (m & 7)) * 16) + half * 8, v);
+            }
+        }
 }
 
 template <int MB>
 __global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a, int gather)
 {
     using C = SmallCfg<MB>;
-    constexpr int SLOTS = C::SLOTS, LPC = C::LOADS_PER_CHUNK;
+    constexpr int SLOTS = C::SLOTS;
     __shared__ __attribute__((aligned(1024))) char wt[W_BYTES];
     __shared__ __attribute__((aligned(1024))) char at[A_AREA];
-    // The row table lives at the start of the chunk area until every lane has
-    // copied the addresses it loads from into registers.
-    uint64_t* rowaddr = reinterpret_cast<uint64_t*>(at);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n0 = blockIdx.x * SBN;
     const int M = a.M;
-
-    // 1. The weight tile does not depend on the rows: waves 1..3 put all of it
-    //    in flight first (row c is one 1 KB load; lane l fills physical granule
-    //    l, which holds logical granule l ^ (c % 16)), while wave 0 resolves the
-    //    rows.  Wave 0 issues none of these loads, so the waits the compiler
-    //    puts on its index loads do not wait for the weight.
+    const int grid = gridDim.x;
     const uint32_t wt_lds = lds_addr(wt), at_lds = lds_addr(at);
-    if (wave > 0) {
-        const i32x4 wr = make_srd(a.W, (uint32_t)((int64_t)a.N * SK * 2));
-        for (int c = wave - 1; c < SBN; c += 3)
-            asm_ld16_lds(wr, wt_lds + c * 1024, (uint32_t)((lane ^ (c & 15)) * 16), (uint32_t)((n0 + c) * SK * 2));
-    }
-
-    // 2. Row addresses (wave 0): the first columns of row r start at
-    //    rowaddr[r]; rows M .. ROWS-1 repeat row M-1 (loaded, never stored).
-    if (wave > 0) {
-    } else if (gather) {
-        for (uint32_t b = lane; b < a.L.batch; b += 64) {
-            const uint32_t lo = a.bro[b], hi0 = a.bro[b + 1], c0 = a.co[b];
-            const uint32_t hi = hi0 < (uint32_t)M ? hi0 : (uint32_t)M;
-            for (uint32_t r = lo; r < hi; ++r)
-                rowaddr[r] = (uint64_t)(a.L.base + token_offset(a.L, b, c0 + (r - lo)));
-        }
-    } else {
-        for (int r = lane; r < M; r += 64)
-            rowaddr[r] = (uint64_t)(static_cast<const char*>(a.lat) + (int64_t)r * a.D * 2);
-    }
-    lds_barrier();
-    if (tid >= M && tid < C::ROWS)
-        rowaddr[tid] = rowaddr[M - 1];
-    lds_barrier();
-
-    // Row chunks: chunk q holds columns 64 q .. 64 q + 63 of every row, rows of
-    // 128 bytes (8 granules XOR-swizzled by (row / 2) % 8).  A load covers 8
-    // rows: lane l takes row 8 i + l / 8, physical granule l % 8.
+    const int gpr = a.D * 2 / 16;                // 16-byte granules per cache row
+    const bool early_copy = gather && gpr <= EARLY_COPY_GRANULES;
     const int lrow = lane >> 3, lpos = lane & 7;
-    const char* src_row[LPC];
-#pragma unroll
-    for (int i = 0; i < LPC; ++i) {
-        const int r = (wave * LPC + i) * 8 + lrow;
-        src_row[i] = reinterpret_cast<const char*>(rowaddr[r]) + (lpos ^ ((r >> 1) & 7)) * 16;
-    }
-    lds_barrier();
-    auto issue_chunk = [&](int q, int slot) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < LPC; ++i) {
-            const int r8 = (wave * LPC + i) * 8;
-            asm_gld16_lds(src_row[i] + q * CROWB, at_lds + slot * C::CHUNK_BYTES + r8 * CROWB);
-        }
+    // The row table (first columns of row r at rowaddr[r]; rows M .. ROWS-1
+    // repeat row M-1, loaded and never stored) lives where weight chunk 7
+    // lands, until every loader wave has read its rows' addresses.
+    char* tbl = wt + (CHUNKS - 1) * W_CHUNK_BYTES;
+    uint64_t* rowaddr = reinterpret_cast<uint64_t*>(tbl);
+
+    // Weight load (c, p): chunk c, tile rows 8 p .. 8 p + 7, one 128-byte row
+    // piece per 8 lanes; lane l fills granule position l % 8 of row
+    // 8 p + l / 8 with logical granule (l % 8) ^ ((row / 2) % 8).
+    const i32x4 wr = make_srd(a.W, (uint32_t)((int64_t)a.N * SK * 2));
+    auto issue_w = [&](int c, int p) __attribute__((always_inline)) {
+        const int row = 8 * p + lrow;
+        const uint32_t voff = (uint32_t)(row * SK * 2 + ((lpos ^ ((row >> 1) & 7)) * 16));
+        asm_ld16_lds(wr, wt_lds + c * W_CHUNK_BYTES + p * 1024, voff, (uint32_t)(n0 * SK * 2 + c * CROWB));
     };
-#pragma unroll
-    for (int q = 0; q < SLOTS - 1; ++q)
-        issue_chunk(q, q);
 
-    // 3. The product.
-    const int nb = wave & 1, mb0 = wave >> 1;
-    const int frow = lane & 31, half = lane >> 5;
-    const char* wrow = wt + (nb * 32 + frow) * (SK * 2);
-    const int wsw = frow & 15;
-    f32x16 acc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        acc[i] = f32x16{};
-
-#pragma unroll
-    for (int q = 0; q < CHUNKS; ++q) {
-        // Chunk q (and, at q = 0, the weight tile) has landed for this thread;
-        // younger loads are the chunks issued after it.
-        vm_wait((q + SLOTS - 2 < CHUNKS - 1 ? SLOTS - 2 : CHUNKS - 1 - q) * LPC);
-        lds_barrier();
-        // Everyone is done with chunk q-1: refill its slot.
-        if (q + SLOTS - 1 < CHUNKS)
-            issue_chunk(q + SLOTS - 1, (q + SLOTS - 1) % SLOTS);
-        const char* as = at + (q % SLOTS) * C::CHUNK_BYTES;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int g = q * 8 + 2 * kk + half;     // weight logical granule
-            const bf16x8 wf = as_bf16x8(lds_ld16(wrow + (((g & ~15) | ((g & 15) ^ wsw)) * 16)));
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (mb0 + 2 * i < MB) {
-                    const int r = (mb0 + 2 * i) * 32 + frow;
-                    const bf16x8 af = as_bf16x8(lds_ld16(as + r * CROWB + ((2 * kk + half) ^ ((r >> 1) & 7)) * 16));
-                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, af, acc[i], 0, 0, 0);
+    // 1. The first weight chunks (waves 5..7) while wave 4 builds the row table.
+    if (wave >= 5) {
+        for (int j = wave - 5; j < 8 * W_EARLY_CHUNKS; j += W_WAVES)
+            issue_w(j >> 3, j & 7);
+    } else if (wave == 4) {
+        if (gather) {
+            // Two rounds of loads whatever the rows per request: one lane per
+            // request reads its offsets and writes each of its rows' request and
+            // token position into LDS; then one lane per row reads the page-table
+            // entry of its row.  Rows no request covers (buffer_row_offsets
+            // ending short of M) read the pool's first row.
+            uint32_t* row_req = reinterpret_cast<uint32_t*>(tbl + SMAX_M * 8);
+            uint32_t* row_pos = row_req + SMAX_M;
+            for (int r = lane; r < C::ROWS; r += 64)
+                row_req[r] = ~0u;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            // Every load of a round is issued before any of them is used
+            // (indices clamped into the arrays instead of branching around
+            // the loads), so each round costs one memory latency.
+            for (uint32_t b0 = 0; b0 < a.L.batch; b0 += 64) {
+                // Lane b reads buffer_row_offsets[b] and cache_offsets[b]; a
+                // request's end is its neighbour lane's start (the last lane's
+                // comes from one more, wave-uniform, load).
+                const uint32_t b = b0 + lane;
+                const uint32_t bc = b < a.L.batch ? b : a.L.batch - 1;
+                const uint32_t bend = b0 + 64 < a.L.batch ? b0 + 64 : a.L.batch;
+                uint32_t lo = a.bro[bc], c0 = a.co[bc], last = a.bro[bend];
+                // One use of all three here keeps the compiler from sinking a
+                // load into the branch that needs it (a second round trip).
+                asm volatile("" : "+v"(lo), "+v"(c0), "+v"(last));
+                const uint32_t next = (uint32_t)__shfl_down((int)lo, 1);
+                const uint32_t hi0 = lane == 63 || b + 1 >= a.L.batch ? last : next;
+                const uint32_t hi = b >= a.L.batch ? lo : hi0 < (uint32_t)M ? hi0 : (uint32_t)M;
+                for (uint32_t r = lo; r < hi; ++r) {
+                    row_req[r] = b;
+                    row_pos[r] = c0 + (r - lo);
                 }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            constexpr int RPL = (C::ROWS + 63) / 64;
+            const PagedLayer& L = a.L;
+            uint32_t pgv[RPL], slot[RPL];
+            bool valid[RPL];
+#pragma unroll
+            for (int k = 0; k < RPL; ++k) {
+                const int r = lane + 64 * k;
+                const uint32_t b = r < C::ROWS ? row_req[r] : ~0u;
+                valid[k] = b != ~0u;
+                const uint32_t pos = valid[k] ? row_pos[r] : 0u, bb = valid[k] ? b : 0u;
+                uint32_t lp = pos / L.page_size;
+                slot[k] = pos - lp * L.page_size;
+                lp = lp < L.max_pages ? lp : L.max_pages - 1;
+                pgv[k] = L.page_table[(size_t)bb * L.max_pages + lp];
+            }
+#pragma unroll
+            for (int k = 0; k < RPL; ++k) {
+                const uint32_t pg = pgv[k] < L.num_pages ? pgv[k] : L.num_pages - 1;
+                const int64_t off = valid[k] ? (int64_t)pg * L.stride_page + (int64_t)slot[k] * L.stride_token : 0;
+                if (lane + 64 * k < C::ROWS)
+                    rowaddr[lane + 64 * k] = (uint64_t)(L.base + off);
+            }
+        } else {
+            for (int r = lane; r < M; r += 64)
+                rowaddr[r] = (uint64_t)(static_cast<const char*>(a.lat) + (int64_t)r * a.D * 2);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        for (int r = M + lane; r < C::ROWS; r += 64)
+            rowaddr[r] = rowaddr[M - 1];
+        // The compiler's own wait (vmcnt(0), known to its wait pass): no load
+        // of this branch is left pending where the wave roles' code joins,
+        // so no conservative wait lands on the weight waves, whose loads into
+        // LDS it cannot see and would wait for too.
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    lds_barrier();              // row table written
+
+    // 2. Loader waves 4..7 (w = wave - 4) take the row loads i = w, w + 4, ...
+    //    of every chunk (lane l: row 8 i + l / 8, granule position l % 8 with
+    //    logical granule (l % 8) ^ ((row / 2) % 8)) and the weight loads
+    //    p = 2 w, 2 w + 1 of every chunk from W_EARLY_CHUNKS on.
+    const int w = wave - 4;
+    const char* src_row[MB];
+    u32x4 cp[EARLY_COPY_ROWS][2];
+    if (wave >= 4) {
+#pragma unroll
+        for (int k = 0; k < MB; ++k) {
+            const int r = 8 * (w + 4 * k) + lrow;
+            src_row[k] = reinterpret_cast<const char*>(rowaddr[r]) + (lpos ^ ((r >> 1) & 7)) * 16;
+        }
+        // This block's first k_latent_buffer rows (r = block, block + grid):
+        // whole cache rows, granules lane and lane + 64, in flight now and
+        // stored at the end.
+        if (w == 0 && early_copy) {
+#pragma unroll
+            for (int j = 0; j < EARLY_COPY_ROWS; ++j) {
+                const int r = blockIdx.x + j * grid;
+                const char* base = reinterpret_cast<const char*>(rowaddr[r < M ? r : M - 1]);
+                cp[j][0] = lane < gpr ? gld16(base + lane * 16) : u32x4{};
+                cp[j][1] = lane + 64 < gpr ? gld16(base + (lane + 64) * 16) : u32x4{};
+            }
         }
     }
+    lds_barrier();              // row table read: weight chunk 7 may land on it
 
-    // 4. Outputs: lane holds rows 32 mb + frow, columns 8q + 4 half + 0..3.
+    if (wave >= 4) {
+        // Chunk c: this wave's row loads, then its share of weight chunk
+        // c + W_EARLY_CHUNKS, so rows and weight arrive in K order.
+        auto issue_chunk = [&](int c) __attribute__((always_inline)) {
+            const int slot = c % SLOTS;
+#pragma unroll
+            for (int k = 0; k < MB; ++k)
+                asm_gld16_lds(src_row[k] + c * CROWB, at_lds + slot * C::CHUNK_BYTES + (w + 4 * k) * 1024);
+            if (c + W_EARLY_CHUNKS < CHUNKS) {
+                issue_w(c + W_EARLY_CHUNKS, 2 * w);
+                issue_w(c + W_EARLY_CHUNKS, 2 * w + 1);
+            }
+        };
+#pragma unroll
+        for (int c = 0; c < C::INITIAL; ++c)
+            issue_chunk(c);
+#pragma unroll
+        for (int q = 0; q < CHUNKS; ++q) {
+            switch (q) {
+            case 0: wait_loads<MB, 0>(); break;
+            case 1: wait_loads<MB, 1>(); break;
+            case 2: wait_loads<MB, 2>(); break;
+            case 3: wait_loads<MB, 3>(); break;
+            case 4: wait_loads<MB, 4>(); break;
+            case 5: wait_loads<MB, 5>(); break;
+            case 6: wait_loads<MB, 6>(); break;
+            default: wait_loads<MB, 7>(); break;
+            }
+            lds_barrier();
+            // Every wave is done with chunk q-1: refill its slot.
+            if (C::RING && q + SLOTS - 1 < CHUNKS)
+                issue_chunk(q + SLOTS - 1);
+        }
+
+        // k_latent_buffer: the rows copied through registers, then (few weight
+        // tiles, or rows wider than 2 KB) the rest of this block's rows r with
+        // r % grid == block, by the 8 lanes that hold r's address.
+        if (gather) {
+            char* lat = static_cast<char*>(a.lat);
+            if (w == 0 && early_copy) {
+#pragma unroll
+                for (int j = 0; j < EARLY_COPY_ROWS; ++j) {
+                    const int r = blockIdx.x + j * grid;
+                    if (r < M) {
+                        char* dst = lat + (int64_t)r * a.D * 2;
+                        if (lane < gpr)
+                            gst16(dst + lane * 16, cp[j][0]);
+                        if (lane + 64 < gpr)
+                            gst16(dst + (lane + 64) * 16, cp[j][1]);
+                    }
+                }
+            }
+            const int first = early_copy ? (int)blockIdx.x + EARLY_COPY_ROWS * grid : (int)blockIdx.x;
+#pragma unroll
+            for (int k = 0; k < MB; ++k) {
+                const int r = 8 * (w + 4 * k) + lrow;
+                if (r < M && r >= first && r % grid == (int)blockIdx.x) {
+                    const char* base = src_row[k] - (lpos ^ ((r >> 1) & 7)) * 16;
+                    char* dst = lat + (int64_t)r * a.D * 2;
+                    for (int g = lpos; g < gpr; g += 8)
+                        gst16(dst + g * 16, gld16(base + g * 16));
+                }
+            }
+        }
+        lds_barrier();          // matches the compute waves' barrier before staging
+    } else if constexpr (MB >= 6) {
+        // 3. The product.  Many rows: wave v owns both weight blocks and M
+        //    blocks v, v + 4 (one LDS fragment read per MFMA).
+        switch (wave) {
+        case 0: compute_waves<MB, 0, 4, 2>(wt, at, 0, lane); break;
+        case 1: compute_waves<MB, 1, 4, 2>(wt, at, 0, lane); break;
+        case 2: compute_waves<MB, 2, 4, 2>(wt, at, 0, lane); break;
+        default: compute_waves<MB, 3, 4, 2>(wt, at, 0, lane); break;
+        }
+    } else if (wave < 2) {
+        // Few rows: wave v owns weight block v % 2 and M blocks v / 2, v / 2 + 2, ...
+        compute_waves<MB, 0, 2, 1>(wt, at, wave & 1, lane);
+    } else {
+        compute_waves<MB, 1, 2, 1>(wt, at, wave & 1, lane);
+    }
+    lds_barrier();              // outputs staged
+
+    // 4. Outputs: each store writes 8 whole 128-byte row segments (lane l: row
+    //    8 s + l / 8, granule l % 8).
     uint16_t* out = static_cast<uint16_t*>(a.out);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = (mb0 + 2 * i) * 32 + frow;
-        if (mb0 + 2 * i < MB && m < M) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + nb * 32 + 8 * q + 4 * half;
-                const u32x2 v = {pack_bf16x2(acc[i][4 * q], acc[i][4 * q + 1]),
-                                 pack_bf16x2(acc[i][4 * q + 2], acc[i][4 * q + 3])};
-                *reinterpret_cast<u32x2*>(out + (int64_t)m * a.N + n) = v;
-            }
-        }
-    }
-
-    // 5. Gathering form: this block's rows of k_latent_buffer (rows r with
-    //    r % grid == block), whole cache rows.  The 8 lanes that loaded row r
-    //    still hold its address; each copies every 8th granule.
-    if (gather) {
-        const int gpr = a.D * 2 / 16;
-#pragma unroll
-        for (int i = 0; i < LPC; ++i) {
-            const int r = (wave * LPC + i) * 8 + lrow;
-            if (r < M && r % (int)gridDim.x == (int)blockIdx.x) {
-                const char* base = src_row[i] - (lpos ^ ((r >> 1) & 7)) * 16;
-                char* dst = static_cast<char*>(a.lat) + (int64_t)r * a.D * 2;
-                for (int g = lpos; g < gpr; g += 8)
-                    st16(dst + g * 16, ld16(base + g * 16));
-            }
+    const int sg = lane & 7;
+    for (int s = wave; s * 8 < M; s += SNT / 64) {
+        const int m = 8 * s + lrow;
+        if (m < M) {
+            const u32x4 v = lds_ld16(at + m * CROWB + ((sg ^ (m & 7)) * 16));
+            gst16(out + (int64_t)m * a.N + n0 + 8 * sg, v);
         }
     }
 }
