@@ -53,6 +53,16 @@ def test_ragged_small_batches(lens, offs, ps):
     _check_full(case)
 
 
+@pytest.mark.parametrize("lens,offs,rope,N", [([80, 70], [0, 3], 576, 2048), ([60, 50, 40], [5, 0, 9], 64, 16384)])
+def test_wide_rows_and_mid_row_counts(lens, offs, rope, N):
+    """Rows wider than 2 KB (k_latent_buffer copied without the early register
+    copy) and row counts that take the chunk ring (MB = 5: 147 and 136 rows)."""
+    case = W.decompress_case("small_wide", seed=25, cache_lengths=lens, cache_offsets=offs, page_size=16,
+                             kv_lora_rank=512, rope_dim=rope, N=N)
+    assert 128 < case.M <= 160
+    _check_full(case)
+
+
 def test_k1024_and_empty_requests():
     case = W.decompress_case("small_k1024", seed=22, cache_lengths=[50, 10, 0, 77], cache_offsets=[20, 10, 0, 0],
                              page_size=16, kv_lora_rank=1024, rope_dim=64, N=512)
