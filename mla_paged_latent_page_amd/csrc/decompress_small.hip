@@ -10,11 +10,11 @@
 // one per CU).  The block's 64 x 512 weight tile (64 KB) and the rows' first
 // 512 columns go into LDS in K order, in chunks of 64 columns (128-byte row
 // pieces; weight chunk q is 8 KB):
-//  * at kernel start waves 5..7 put weight chunks 0 and 1 in flight while
+//  * at kernel start waves 5..7 put weight chunk 0 in flight while
 //    wave 4 resolves the rows' cache addresses (one lane per request reads its
 //    offsets, then one lane per row its page-table entry) into a table in LDS;
 //  * then waves 4..7 each issue, chunk after chunk, their share of row chunk c
-//    and of weight chunk c + 2, so rows and weight arrive together in K order.
+//    and of weight chunk c + 1, so rows and weight arrive together in K order.
 //    A CU serves the vector loads of its waves in issue order: rows queued
 //    behind the whole weight tile would start the product only after the
 //    weight had streamed in, and a tile queued behind slow index loads would
@@ -49,7 +49,7 @@ constexpr int W_WAVES = 3;
 // Weight chunks put in flight before the rows are: each CU serves its vector
 // loads in issue order, so the row wave's index and row loads wait behind
 // every weight load issued before them.
-constexpr int W_EARLY_CHUNKS = 2;
+constexpr int W_EARLY_CHUNKS = 1;
 constexpr int EARLY_COPY_ROWS = 2;               // k_latent_buffer rows per block copied through registers
 constexpr int EARLY_COPY_GRANULES = 128;         // up to 2048-byte cache rows
 
