@@ -91,7 +91,7 @@ __global__ void __launch_bounds__(AB_NT, 1) absorb_bf16(AbsorbArgs a)
     // The rope part (the block with the head's first tiles copies it): R * 2
     // bytes per row, granule idx of the chunk = row idx / gpr, granule idx % gpr.
     const bool rope = a.R > 0 && u == 0;
-    const int gpr = a.R / 8;
+    const int gpr = a.R > 0 ? a.R / 8 : 1;   // granules per rope row (1 when there is none: a safe divisor)
     u32x4 rp[AB_ROPE_REGS];
     auto load_rope = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
@@ -276,7 +276,7 @@ __global__ void __launch_bounds__(AB_NT, 1) absorb_fp8(AbsorbArgs a)
         }
     };
     const bool rope = a.R > 0 && u == 0;
-    const int gpr = a.R / 8;
+    const int gpr = a.R > 0 ? a.R / 8 : 1;   // granules per rope row (1 when there is none: a safe divisor)
     u32x4 rp[AB_ROPE_REGS];
     auto load_rope = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
