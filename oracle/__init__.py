@@ -79,6 +79,7 @@ def _load():
         lib.or_gather.restype = _int
         lib.or_matmul_nt.argtypes = [_p, _int, _i64, _p, _int, _i64, _i64, _i64, _p, _i64, _p]
         lib.or_quantize_e4m3_rows.argtypes = [_p, _i64, _i64, _i64, _i64, _p, _p]
+        lib.or_quantize_f32_rows.argtypes = [_p, _i64, _i64, _i64, _p, _p]
         lib.or_fp8_matmul_nt.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _i64, _p]
         lib.or_matmul_nn.argtypes = [_p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p]
         lib.or_kv_destinations.argtypes = [_i64, _i64, _i64, _i64, _u32, _u32, _u32, _p, _u32,
@@ -203,6 +204,19 @@ def quantize_e4m3_rows(A_bf16_bits, K, k_gran=128):
     s = np.empty((M, nkb), np.float32)
     if M:
         _load().or_quantize_e4m3_rows(_ptr(A), A.shape[1], M, K, k_gran, _ptr(q), _ptr(s))
+    return q, s
+
+
+def quantize_f32_rows(Y, gran=128):
+    """(codes uint8 [T, D], scales float32 [T, ceil(D/gran)]) of binary32 rows
+    (blocks of gran columns, the last one possibly shorter)."""
+    Y = np.ascontiguousarray(Y, dtype=np.float32)
+    T, D = Y.shape
+    nb = -(-D // gran)
+    q = np.empty((T, D), np.uint8)
+    s = np.empty((T, nb), np.float32)
+    if T:
+        _load().or_quantize_f32_rows(_ptr(Y), T, D, gran, _ptr(q), _ptr(s))
     return q, s
 
 
@@ -376,6 +390,25 @@ def latent_write(case):
         if rc != 0:
             raise OracleError(f"latent write precondition failed ({rc})")
     return out, kv_destinations(case)[:, 0]
+
+
+def latent_write_fp8(case):
+    """(codes uint8 [T, D_c], scales float32 [T, nblk], row values binary64
+    [T, D_c], element offsets int64 [T] of each token's cache row, float offsets
+    int64 [T] of its scales) for an e4m3 cache: the latent write path's values
+    (latent_write), rounded to binary32 (the precision the quantisation
+    decisions are taken in) and quantised per scale block of the cache
+    (quantize_f32_rows)."""
+    c = case.cache
+    if c.dtype != "e4m3" or c.scales is None:
+        raise OracleError("an e4m3 cache with scales is required")
+    ref, dst = latent_write(case)
+    q, s = quantize_f32_rows(ref.astype(np.float32), c.scale_gran)
+    sp, sl, skv, st = c.scale_strides()
+    pos_page = dst // c.strides()[0]
+    slot = (dst - pos_page * c.strides()[0] - case.layer_idx * c.strides()[1]) // c.strides()[3]
+    sdst = pos_page * sp + case.layer_idx * sl + slot * st
+    return q, s, ref, dst, sdst
 
 
 def kv_matmul(case, rows=None):

@@ -270,6 +270,40 @@ void or_quantize_e4m3_rows(const uint16_t* A_bf16, int64_t lda, int64_t M, int64
     }
 }
 
+/* ------------------------------------------------------------------------
+ * Quantisation of binary32 rows into an e4m3fn paged cache (the collection's
+ * scale_dtype_ fp32 and quantization_granularity_ of page
+ * "generic_flare_mla_decompress_k_cache_ragged_paged"): the same rule as the
+ * activation quantisation above, per row and per block of gran columns (the
+ * last block may be shorter): amax = max |y| over the block, s = amax / 448,
+ * codes e4m3fn(y * (448 / amax)), quotients rounded to binary32; an all-zero
+ * block takes s = 1 and codes 0.
+ * ---------------------------------------------------------------------- */
+void or_quantize_f32_rows(const float* Y, int64_t T, int64_t D, int64_t gran, uint8_t* q, float* s)
+{
+    int64_t nb = (D + gran - 1) / gran;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < T; ++r) {
+        for (int64_t kb = 0; kb < nb; ++kb) {
+            int64_t k0 = kb * gran, k1 = k0 + gran < D ? k0 + gran : D;
+            float amax = 0.0f;
+            for (int64_t k = k0; k < k1; ++k) {
+                float a = fabsf(Y[r * D + k]);
+                if (a > amax)
+                    amax = a;
+            }
+            float scale = 1.0f, inv = 1.0f;
+            if (amax > 0.0f) {
+                scale = amax / 448.0f;
+                inv = 448.0f / amax;
+            }
+            s[r * nb + kb] = scale;
+            for (int64_t k = k0; k < k1; ++k)
+                q[r * D + k] = float_to_e4m3(Y[r * D + k] * inv);
+        }
+    }
+}
+
 /* out[j][n] = sum_kb s_a[r][kb] * s_w[n/n_gran][kb] * sum_{k in block kb} qa[r][k] qw[n][k]
  * with the codes decoded exactly and everything summed in binary64. */
 void or_fp8_matmul_nt(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,

@@ -373,15 +373,17 @@ def rope_table(max_seq_len, R, base=10000.0):
 
 
 def latent_write_case(name, *, seed, seq_lens, start_lengths, page_size, K=512, R=64, num_layers=2,
-                      layer_idx=1, eps=1e-6, max_seq_len=None) -> LatentWriteCase:
+                      layer_idx=1, eps=1e-6, max_seq_len=None, dtype="bf16", fill="normal") -> LatentWriteCase:
     """New tokens (latent N(0,1), rope N(0,1), bf16) appended after each request's
-    cached ones in an MLA cache of rows K + R; RMSNorm weights U[0.5, 1.5]."""
+    cached ones in an MLA cache of rows K + R; RMSNorm weights U[0.5, 1.5].
+    dtype="e4m3": an e4m3 cache with one fp32 scale per 128 columns (fill as
+    make_paged_cache)."""
     rng = np.random.default_rng(seed)
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
     start_lengths = np.asarray(start_lengths, dtype=np.int64)
     cache = make_paged_cache(rng, cache_lengths=start_lengths, page_size=page_size, num_heads=1,
-                             head_dim=K + R, dtype="bf16", num_kv=1, num_layers=num_layers,
-                             layer_idx=layer_idx, extra_tokens=seq_lens)
+                             head_dim=K + R, dtype=dtype, num_kv=1, num_layers=num_layers,
+                             layer_idx=layer_idx, extra_tokens=seq_lens, fill=fill)
     T = int(seq_lens.sum())
     iro = np.zeros(len(seq_lens) + 1, dtype=np.uint32)
     iro[1:] = np.cumsum(seq_lens)
@@ -390,6 +392,14 @@ def latent_write_case(name, *, seed, seq_lens, start_lengths, page_size, K=512, 
     if max_seq_len is None:
         max_seq_len = int((start_lengths + seq_lens).max()) + 1
     return LatentWriteCase(name, cache, layer_idx, x, iro, gamma, float(eps), rope_table(max_seq_len, R), K)
+
+
+def c5_latent_write_fp8(seed=5) -> LatentWriteCase:
+    """The c5 write batch into an e4m3 cache (one fp32 scale per 128 columns)."""
+    rng = np.random.default_rng(seed + 1000)
+    lens = lognormal_lengths(rng, 128, 512, 1.0, 8192)
+    return latent_write_case("c5_latent_write_fp8", seed=seed, seq_lens=lens, start_lengths=np.zeros(128, np.int64),
+                             page_size=128, dtype="e4m3")
 
 
 def c5_latent_write(seed=5) -> LatentWriteCase:
