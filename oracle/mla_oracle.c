@@ -292,14 +292,14 @@ void or_quantize_f32_rows(const float* Y, int64_t T, int64_t D, int64_t gran, ui
                 if (a > amax)
                     amax = a;
             }
-            float scale = 1.0f, inv = 1.0f;
+            float block_scale = 1.0f, to_codes = 1.0f;
             if (amax > 0.0f) {
-                scale = amax / 448.0f;
-                inv = 448.0f / amax;
+                block_scale = amax / 448.0f;
+                to_codes = 448.0f / amax;
             }
-            s[r * nb + kb] = scale;
+            s[r * nb + kb] = block_scale;
             for (int64_t k = k0; k < k1; ++k)
-                q[r * D + k] = float_to_e4m3(Y[r * D + k] * inv);
+                q[r * D + k] = float_to_e4m3(Y[r * D + k] * to_codes);
         }
     }
 }

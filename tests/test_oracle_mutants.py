@@ -12,7 +12,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "mla_oracle.c")
 PINS = ["tests/test_oracle_codecs.py", "tests/test_oracle_gather.py",
-        "tests/test_oracle_products.py", "tests/test_oracle_kv.py", "tests/test_oracle_latent_write.py"]
+        "tests/test_oracle_products.py", "tests/test_oracle_kv.py", "tests/test_oracle_latent_write.py",
+        "tests/test_oracle_latent_write_fp8.py"]
 
 MUTANTS = {
     "slot_uses_page_index": ("(p % P->page_size) * P->stride_token", "(p / P->page_size) * P->stride_token"),
@@ -39,6 +40,8 @@ MUTANTS = {
     "rope_sign": ("y[K + 2 * j] = x0 * c - x1 * s;", "y[K + 2 * j] = x0 * c + x1 * s;"),
     "rope_pair_swapped": ("double c = freqs[pos[t] * R + 2 * j], s = freqs[pos[t] * R + 2 * j + 1];",
                           "double s = freqs[pos[t] * R + 2 * j], c = freqs[pos[t] * R + 2 * j + 1];"),
+    "cache_block_scale_inverted": ("to_codes = 448.0f / amax;", "to_codes = amax / 448.0f;"),
+    "cache_short_block_widened": ("k1 = k0 + gran < D ? k0 + gran : D;", "k1 = k0 + gran;"),
     "rope_row_of_token": ("double c = freqs[pos[t] * R + 2 * j], s = freqs[pos[t] * R + 2 * j + 1];",
                           "double c = freqs[t * R + 2 * j], s = freqs[t * R + 2 * j + 1];"),
 }
