@@ -407,6 +407,32 @@ mla_status_t mla_write_latent_paged(const void* kv_input, const uint32_t* input_
                                     const mla_paged_cache_t* cache, uint32_t layer_idx, void* stream);
 
 /*
+ * The latent write path into an e4m3 cache (page "mla_prefill_decode_graph_fp8",
+ * Args kv_input_fn, kv_norm_gamma, epsilon, freqs_cis, input_row_offsets,
+ * kv_collection, layer_idx; the collection's scale_dtype_ fp32 and
+ * quantization_granularity_ 128 of page
+ * "generic_flare_mla_decompress_k_cache_ragged_paged"): the rows of
+ * mla_write_latent_paged, computed the same way in fp32, then quantised per
+ * block of 128 columns of the row:
+ *   y = the fp32 row values (RMS-normalised latent part, rotated rope part)
+ *   amax_j = max |y| over block j, s_j = amax_j / 448 (1 for an all-zero block)
+ *   codes = e4m3fn(y * (448 / amax_j)), round to nearest even; s_j into the scale pool
+ * at the token's (page, slot) in layer layer_idx, codes into the e4m3 pool.
+ * mla_decompress_k_paged_fp8_cache reads what this writes.
+ *
+ * cache            [host] num_kv == 1, dtype F8E4M3FN, D_c % 16 == 0, cache_lengths set;
+ *                  pages are WRITTEN
+ * cache_scales     [host] granularity 128, stride_token >= ceil(D_c / 128); WRITTEN
+ * K                kv_lora_rank: K % 128 == 0, K <= 512; R = D_c - K: R % 8 == 0, R <= 512
+ * Other arguments, errors and validation order as in mla_write_latent_paged.
+ */
+mla_status_t mla_write_latent_paged_fp8(const void* kv_input, const uint32_t* input_row_offsets,
+                                        int32_t total_tokens, const float* kv_norm_gamma, float epsilon,
+                                        const float* freqs_cis, int32_t max_seq_len, int32_t K,
+                                        const mla_paged_cache_t* cache, const mla_cache_scales_t* cache_scales,
+                                        uint32_t layer_idx, void* stream);
+
+/*
  * Project hidden states and write them into the paged K/V cache (page
  * "kv_matmul_ragged_paged", summary and Args).
  *

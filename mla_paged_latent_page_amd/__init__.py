@@ -36,7 +36,8 @@ EXPORTS = ("mla_paged_cache_default_strides", "mla_decompress_k_paged", "mla_gat
            "mla_latent_matmul", "mla_decompress_k_paged_fp8_workspace_size", "mla_decompress_k_paged_fp8",
            "kv_matmul_paged", "mla_check_indices", "mla_status_string", "mla_last_hip_error",
            "mla_abi_version", "mla_decompress_kv_paged", "mla_decompress_kv_paged_fp8",
-           "mla_write_latent_paged", "mla_decompress_k_paged_fp8_cache", "mla_absorb_q", "mla_absorb_q_fp8")
+           "mla_write_latent_paged", "mla_decompress_k_paged_fp8_cache", "mla_absorb_q", "mla_absorb_q_fp8",
+           "mla_write_latent_paged_fp8")
 
 
 class MlaError(RuntimeError):
@@ -101,6 +102,9 @@ def lib():
             L.mla_write_latent_paged.argtypes = [vp, vp, i32, vp, ctypes.c_float, vp, i32, i32,
                                                  ctypes.POINTER(CacheDesc), u32, vp]
             L.mla_write_latent_paged.restype = i32
+            L.mla_write_latent_paged_fp8.argtypes = [vp, vp, i32, vp, ctypes.c_float, vp, i32, i32,
+                                                     ctypes.POINTER(CacheDesc), ctypes.POINTER(ScalesDesc), u32, vp]
+            L.mla_write_latent_paged_fp8.restype = i32
             L.mla_decompress_k_paged_fp8_cache.argtypes = [vp, vp, i32, vp, vp, i32, i32, ctypes.POINTER(CacheDesc),
                                                            ctypes.POINTER(ScalesDesc), u32, vp, vp, vp, vp]
             L.mla_decompress_k_paged_fp8_cache.restype = i32
@@ -451,6 +455,26 @@ def mla_write_latent_paged(kv_input, input_row_offsets, kv_norm_gamma, epsilon: 
                                       freqs_cis.data_ptr() if freqs_cis is not None else None, int(max_seq),
                                       int(K), ctypes.byref(desc), int(layer_idx), _stream(stream))
     _check(st, "mla_write_latent_paged")
+
+
+def mla_write_latent_paged_fp8(kv_input, input_row_offsets, kv_norm_gamma, epsilon: float, freqs_cis, K: int,
+                               cache: PagedKVCache, layer_idx: int, stream=None) -> None:
+    """mla_write_latent_paged into an e4m3 cache: the same fp32 rows, quantised
+    per 128 columns (codes into the pool, fp32 scales into the cache's scale pool)."""
+    if kv_input.dim() != 2 or not kv_input.is_contiguous():
+        raise ValueError("kv_input must be a contiguous [T, D_c] tensor")
+    T = kv_input.shape[0]
+    desc = cache.descriptor()
+    sdesc = cache.scales_descriptor()
+    if kv_input.shape[1] != desc.num_heads * desc.head_dim:
+        raise ValueError("kv_input rows must be as wide as the cache rows")
+    max_seq = freqs_cis.shape[0] if freqs_cis is not None else 0
+    st = lib().mla_write_latent_paged_fp8(kv_input.data_ptr(), _u32(input_row_offsets, "input_row_offsets"), T,
+                                          kv_norm_gamma.data_ptr(), float(epsilon),
+                                          freqs_cis.data_ptr() if freqs_cis is not None else None, int(max_seq),
+                                          int(K), ctypes.byref(desc), ctypes.byref(sdesc), int(layer_idx),
+                                          _stream(stream))
+    _check(st, "mla_write_latent_paged_fp8")
 
 
 def kv_matmul_paged(hidden_state, input_row_offsets, weight, cache: PagedKVCache, layer_idx: int,

@@ -604,6 +604,64 @@ MLA_API mla_status_t mla_write_latent_paged(const void* kv_input, const uint32_t
     return e == hipSuccess ? MLA_OK : hip_failed(e);
 }
 
+MLA_API mla_status_t mla_write_latent_paged_fp8(const void* kv_input, const uint32_t* input_row_offsets,
+                                                int32_t total_tokens, const float* kv_norm_gamma, float epsilon,
+                                                const float* freqs_cis, int32_t max_seq_len, int32_t K,
+                                                const mla_paged_cache_t* cache, const mla_cache_scales_t* cache_scales,
+                                                uint32_t layer_idx, void* stream)
+{
+    if (!cache || !cache_scales)
+        return MLA_ERR_NULL_POINTER;
+    const bool work = total_tokens > 0;
+    const int64_t D = (int64_t)cache->num_heads * cache->head_dim;
+    const int64_t R = D - K;   // rope columns after the K latent ones
+    if (work && (!kv_input || !input_row_offsets || !kv_norm_gamma || !cache->blocks || !cache->page_table ||
+                 !cache->cache_lengths || !cache_scales->scales || (R > 0 && !freqs_cis)))
+        return MLA_ERR_NULL_POINTER;
+    const int64_t nblk = (D + 127) / 128;
+    if (total_tokens < 0 || K <= 0 || K % 128 || K > 512 || R < 0 || R % 8 || R > 512 || D % 16 ||
+        (R > 0 && max_seq_len <= 0) || !(epsilon >= 0.0f) || cache_scales->granularity != 128 ||
+        cache_scales->stride_token < nblk || cache_scales->stride_page <= 0 || cache_scales->stride_layer < 0 ||
+        cache_scales->stride_kv < 0)
+        return MLA_ERR_INVALID_SHAPE;
+    if (mla_status_t st = check_cache_shape(cache, 1))
+        return st;
+    if (cache->dtype != MLA_DTYPE_F8E4M3FN)
+        return MLA_ERR_INVALID_DTYPE;
+    if (!aligned16(kv_input) || !aligned16(kv_norm_gamma) || !aligned16(freqs_cis) ||
+        (reinterpret_cast<uintptr_t>(cache_scales->scales) & 3u))
+        return MLA_ERR_MISALIGNED;
+    if (mla_status_t st = check_cache_alignment(cache))
+        return st;
+    if (layer_idx >= cache->num_layers)
+        return MLA_ERR_OUT_OF_RANGE;
+    if (!work)
+        return MLA_OK;
+    if (mla_status_t st = check_device())
+        return st;
+
+    mla::LatentWriteArgs a{};
+    a.X = static_cast<const uint16_t*>(kv_input);
+    a.iro = input_row_offsets;
+    a.cache_len = cache->cache_lengths;
+    a.gamma = kv_norm_gamma;
+    a.freqs = freqs_cis;
+    a.eps = epsilon;
+    a.L = layer_view(cache, layer_idx);
+    a.Ls = a.L;
+    a.Ls.base = reinterpret_cast<const char*>(cache_scales->scales + (int64_t)layer_idx * cache_scales->stride_layer);
+    a.Ls.stride_page = cache_scales->stride_page * 4;
+    a.Ls.stride_token = cache_scales->stride_token * 4;
+    a.Ls.stride_kv = cache_scales->stride_kv * 4;
+    a.T = total_tokens;
+    a.K = K;
+    a.R = (int)R;
+    a.D = (int)D;
+    a.max_seq = R > 0 ? max_seq_len : 1;
+    const hipError_t e = mla::launch_latent_write_fp8(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MLA_OK : hip_failed(e);
+}
+
 MLA_API mla_status_t kv_matmul_paged(const void* hidden_state, const uint32_t* input_row_offsets,
                                      int32_t total_tokens, int32_t hidden_dim, const void* weight,
                                      const mla_paged_cache_t* cache, uint32_t layer_idx, void* stream)

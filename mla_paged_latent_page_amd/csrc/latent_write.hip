@@ -20,6 +20,14 @@
 // of entries <= t, minus one, counted by ballots.  Then come the dependent
 // loads of both tokens (cache length, page table, freqs_cis row), and only
 // after them the stores.
+//
+// e4m3 cache (the collection's scale_dtype_ fp32 and quantization_granularity_
+// 128 of page "generic_flare_mla_decompress_k_cache_ragged_paged"): the same
+// fp32 values, quantised per 128-column block of the row (K % 128 == 0, so the
+// rope columns start a block): amax over the block by a 16-lane butterfly
+// (8 columns per lane), s = amax / 448 (1 for an all-zero block), codes
+// e4m3fn(y * (448 / amax)) rounded to nearest even; each lane stores its 8
+// codes, the first lane of a block stores s into the scale pool.
 #include "launch.hpp"
 
 namespace mla {
@@ -36,6 +44,35 @@ __device__ inline float wave_sum(float v)
     return v;
 }
 
+// Max over the 16-lane group of this lane.
+__device__ inline float group16_max(float v)
+{
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1)
+        v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+// Eight fp32 values of one 128-column block, quantised with the block's scale:
+// the 8 codes (packed little-endian) and, returned, the scale.
+__device__ inline float quantise8(const float (&y)[8], u32x2& codes)
+{
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        am = fmaxf(am, fabsf(y[i]));
+    am = group16_max(am);
+    float s = 1.0f, to_codes = 1.0f;
+    if (am > 0.0f) {
+        s = am / 448.0f;
+        to_codes = 448.0f / am;
+    }
+    codes = {pack_e4m3x2(y[0] * to_codes, y[1] * to_codes) | (pack_e4m3x2(y[2] * to_codes, y[3] * to_codes) << 16),
+             pack_e4m3x2(y[4] * to_codes, y[5] * to_codes) | (pack_e4m3x2(y[6] * to_codes, y[7] * to_codes) << 16)};
+    return s;
+}
+
+template <bool FP8>
 __global__ void __launch_bounds__(64 * WRITE_WAVES) latent_write_kernel(LatentWriteArgs a)
 {
     constexpr int TW = TOKENS_PER_WAVE;
@@ -80,7 +117,7 @@ __global__ void __launch_bounds__(64 * WRITE_WAVES) latent_write_kernel(LatentWr
 
     // Per token: request, position, destination and its freqs_cis row, all
     // loaded before the first store.
-    int64_t off[TW];
+    int64_t off[TW], soff[TW];
     f32x4 fr0[TW], fr1[TW];
 #pragma unroll
     for (int k = 0; k < TW; ++k) {
@@ -89,6 +126,7 @@ __global__ void __launch_bounds__(64 * WRITE_WAVES) latent_write_kernel(LatentWr
         const uint32_t p = a.cache_len[b] + (t - a.iro[b]);
         const uint32_t pf = p < (uint32_t)a.max_seq ? p : (uint32_t)a.max_seq - 1;   // freqs row, clamped
         off[k] = token_offset(a.L, b, p);
+        soff[k] = FP8 ? token_offset(a.Ls, b, p) : 0;
         const float* f = a.freqs + (int64_t)pf * a.R + lane * 8;
         fr0[k] = rot ? *reinterpret_cast<const f32x4*>(f) : f32x4{0.f, 0.f, 0.f, 0.f};
         fr1[k] = rot ? *reinterpret_cast<const f32x4*>(f + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -119,25 +157,58 @@ __global__ void __launch_bounds__(64 * WRITE_WAVES) latent_write_kernel(LatentWr
             ss += x[i] * x[i];
         ss = wave_sum(ss);
         const float inv = 1.0f / sqrtf(ss / (float)a.K + a.eps);
-        if (lat) {
-            u32x4 y;
+        float yl[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                y[i] = pack_bf16x2(gg[2 * i] * (x[2 * i] * inv), gg[2 * i + 1] * (x[2 * i + 1] * inv));
-            st16(dst + lane * 16, y);
-        }
+        for (int i = 0; i < 8; ++i)
+            yl[i] = lat ? gg[i] * (x[i] * inv) : 0.0f;
 
         // Rope part: 4 pairs per lane with the 4 (cos, sin) pairs of freqs_cis row p.
-        if (rot) {
+        float yr[8];
+        {
             const float cs[8] = {fr0[k][0], fr0[k][1], fr0[k][2], fr0[k][3], fr1[k][0], fr1[k][1], fr1[k][2], fr1[k][3]};
-            u32x4 y;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float x0 = bf16_lo(rv[k][i]), x1 = bf16_hi(rv[k][i]);
                 const float c = cs[2 * i], s = cs[2 * i + 1];
-                y[i] = pack_bf16x2(x0 * c - x1 * s, x0 * s + x1 * c);
+                yr[2 * i] = rot ? x0 * c - x1 * s : 0.0f;
+                yr[2 * i + 1] = rot ? x0 * s + x1 * c : 0.0f;
             }
-            st16(dst + a.K * 2 + lane * 16, y);
+        }
+
+        if constexpr (!FP8) {
+            if (lat) {
+                u32x4 y;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    y[i] = pack_bf16x2(yl[2 * i], yl[2 * i + 1]);
+                st16(dst + lane * 16, y);
+            }
+            if (rot) {
+                u32x4 y;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    y[i] = pack_bf16x2(yr[2 * i], yr[2 * i + 1]);
+                st16(dst + a.K * 2 + lane * 16, y);
+            }
+        } else {
+            // Codes at byte 8 lane (latent) and K + 8 lane (rope); block j of
+            // the row is lanes 16 j .. 16 j + 15 of the latent part, and block
+            // K / 128 + j lanes 16 j .. of the rope part.  Lanes past the row
+            // hold zeros, which leave every amax unchanged.
+            float* sdst = reinterpret_cast<float*>(const_cast<char*>(a.Ls.base) + soff[k]);
+            u32x2 cl, cr;
+            const float sl = quantise8(yl, cl);
+            const float sr = quantise8(yr, cr);
+            if (lat) {
+                *reinterpret_cast<u32x2*>(dst + lane * 8) = cl;
+                if ((lane & 15) == 0)
+                    sdst[lane >> 4] = sl;
+            }
+            if (rot) {
+                *reinterpret_cast<u32x2*>(dst + a.K + lane * 8) = cr;
+                if ((lane & 15) == 0)
+                    sdst[a.K / 128 + (lane >> 4)] = sr;
+            }
         }
     }
 }
@@ -147,7 +218,16 @@ __global__ void __launch_bounds__(64 * WRITE_WAVES) latent_write_kernel(LatentWr
 hipError_t launch_latent_write(const LatentWriteArgs& a, hipStream_t s)
 {
     constexpr int per_block = WRITE_WAVES * TOKENS_PER_WAVE;
-    hipLaunchKernelGGL(latent_write_kernel, dim3((a.T + per_block - 1) / per_block), dim3(64 * WRITE_WAVES), 0, s, a);
+    hipLaunchKernelGGL(latent_write_kernel<false>, dim3((a.T + per_block - 1) / per_block), dim3(64 * WRITE_WAVES), 0, s,
+                       a);
+    return hipGetLastError();
+}
+
+hipError_t launch_latent_write_fp8(const LatentWriteArgs& a, hipStream_t s)
+{
+    constexpr int per_block = WRITE_WAVES * TOKENS_PER_WAVE;
+    hipLaunchKernelGGL(latent_write_kernel<true>, dim3((a.T + per_block - 1) / per_block), dim3(64 * WRITE_WAVES), 0, s,
+                       a);
     return hipGetLastError();
 }
 

@@ -56,6 +56,9 @@ struct LatentWriteArgs {
     float eps;
     PagedLayer L;              // layer view of the latent pool
     int T, K, R, D, max_seq;
+    // e4m3 cache only: the scale pool's layer view (one fp32 per 128 columns
+    // of a token row, byte strides).
+    PagedLayer Ls;
 };
 
 struct AbsorbArgs {
@@ -71,6 +74,7 @@ hipError_t launch_gather_rows(const DecompressArgs& a, int elem_bytes, hipStream
 hipError_t launch_absorb_bf16(const AbsorbArgs& a, hipStream_t s);
 hipError_t launch_absorb_fp8(const AbsorbArgs& a, hipStream_t s);
 hipError_t launch_latent_write(const LatentWriteArgs& a, hipStream_t s);
+hipError_t launch_latent_write_fp8(const LatentWriteArgs& a, hipStream_t s);
 hipError_t launch_product_bf16(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_product_f32(const DecompressArgs& a, hipStream_t s);
 hipError_t launch_decompress_bf16(const DecompressArgs& a, hipStream_t s);

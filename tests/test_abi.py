@@ -386,3 +386,35 @@ def test_absorb_fp8_error_paths(lib):
     assert absorb_fp8(lib, ws=FAKE + 1) == MISAL
     assert absorb_fp8(lib, T=0, q=None, w=None, ws=None, out=None) == OK
     assert absorb_fp8(lib) == DEV
+
+
+def write_latent_fp8(lib, d, s, T=50, K=512, max_seq=4096, eps=1e-6, layer=1, **ptrs):
+    p = dict(x=FAKE, iro=FAKE, g=FAKE, f=FAKE)
+    p.update(ptrs)
+    return lib.mla_write_latent_paged_fp8(p["x"], p["iro"], T, p["g"], eps, p["f"], max_seq, K,
+                                          ctypes.byref(d) if d is not None else None,
+                                          ctypes.byref(s) if s is not None else None, layer, None)
+
+
+def test_write_latent_fp8_error_paths(lib):
+    d = cache_desc(dtype=2, with_lengths=True)
+    s = scales_desc()
+    assert write_latent_fp8(lib, None, s) == NULLP
+    assert write_latent_fp8(lib, d, None) == NULLP
+    for k in ("x", "iro", "g", "f"):
+        assert write_latent_fp8(lib, d, s, **{k: None}) == NULLP
+    bad = scales_desc()
+    bad.scales = None
+    assert write_latent_fp8(lib, d, bad) == NULLP
+    assert write_latent_fp8(lib, d, s, K=448) == SHAPE                # K % 128
+    assert write_latent_fp8(lib, d, scales_desc(gran=64)) == SHAPE
+    assert write_latent_fp8(lib, d, scales_desc(nblk=4)) == SHAPE     # stride_token < ceil(576 / 128)
+    assert write_latent_fp8(lib, d, s, eps=-1.0) == SHAPE
+    assert write_latent_fp8(lib, cache_desc(dtype=1, with_lengths=True), s) == DTYPE   # a bf16 cache
+    assert write_latent_fp8(lib, d, s, x=FAKE + 8) == MISAL
+    mis = scales_desc()
+    mis.scales = FAKE + 2
+    assert write_latent_fp8(lib, d, mis) == MISAL
+    assert write_latent_fp8(lib, d, s, layer=2) == RANGE
+    assert write_latent_fp8(lib, d, s, T=0, x=None, iro=None, g=None, f=None) == OK
+    assert write_latent_fp8(lib, d, s) == DEV
