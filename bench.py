@@ -19,7 +19,8 @@ The JSON line also carries the other rows of the path, each timed the same way:
   c2_fused_kv  K and V decompression in one call, against two separate calls
   c2_tp8_share one GPU's share of W_k when 8 GPUs split the heads (N = 2048)
   c5_latent_write  RMSNorm + rope rotation + scatter of 88994 new tokens'
-               rows into the MLA pages (HBM-bound)
+               rows into the MLA pages (HBM-bound), and c5_latent_write_fp8
+               into an e4m3 cache (codes + fp32 scale per 128 columns)
   c7_absorb    query absorption for a decode batch of 128 tokens x 128 heads
                (w_uk [128, 512, 128]; HIP-graph replay like p64/p256), and
                c7_absorb_fp8 with an e4m3 w_uk and 128x128 block scales
@@ -548,6 +549,29 @@ def main():
                                    "note": "per token: read the 1152-byte row and its 256-byte rope table row, "
                                            "write the 1152-byte cache row"}
         print(f"[bench] c5_latent_write: {t.avg_launch_ms:.4f} ms, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+        del ldc, lt, lcache
+        # the same batch written into an e4m3 cache (codes + one fp32 scale per 128 columns)
+        lc8 = W.c5_latent_write_fp8()
+        ldc8, lt8 = W.device_latent_write(lc8)
+        lcache8 = mp.PagedKVCache(ldc8.pool, ldc8.page_table, ldc8.cache_lengths, scales=ldc8.scales)
+
+        def lw8_fn():
+            mp.mla_write_latent_paged_fp8(lt8["x"], lt8["input_row_offsets"], lt8["gamma"], lc8.eps, lt8["freqs"],
+                                          lc8.K, lcache8, lc8.layer_idx)
+        t = Timed(torch, lw8_fn, steps, args.warmup)
+        D = lc8.x.shape[1]
+        nblk = -(-D // 128)
+        b = lc8.T * (D * 2 + (D - lc8.K) * 4 + D + nblk * 4) + lc8.K * 4
+        gbs = b / (t.avg_launch_ms * 1e-3) / 1e9
+        rows["c5_latent_write_fp8"] = {
+            "tokens": lc8.T, "ms": round(t.avg_launch_ms, 4), "hbm_gbs_algorithmic": round(gbs, 1),
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s",
+                                 traffic_from_profile("latent_write_kernel", "c5_latent_write_fp8")),
+            "kernel": "latent_write_kernel<true>",
+            "note": "per token: read the 1152-byte row and its 256-byte rope table row, write 576 e4m3 codes "
+                    "and 5 fp32 scales"}
+        print(f"[bench] c5_latent_write_fp8: {t.avg_launch_ms:.4f} ms, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+        del ldc8, lt8, lcache8
         for name, f8 in (("c7_absorb", False), ("c7_absorb_fp8", True)):
             rows[name] = absorb_row(torch, mp, W, args.warmup, fp8=f8)
             r = rows[name]
