@@ -324,6 +324,29 @@ mla_status_t mla_decompress_k_paged_fp8_cache(const uint32_t* buffer_row_offsets
                                               void* k_buffer, void* stream);
 
 /*
+ * K and V decompression from an e4m3 cache in one call (the fused form of
+ * mla_decompress_kv_paged_fp8 on the cache of mla_decompress_k_paged_fp8_cache;
+ * page "mla_prefill_decode_graph_fp8", Args w_k, w_k_scale, w_uv, w_uv_scale):
+ * one gather of codes and scales, then
+ *   k_buffer[r][n] as mla_decompress_k_paged_fp8_cache with w_k_e4m3 / w_k_scale (N_k columns)
+ *   v_buffer[r][n] the same with w_v_e4m3 / w_v_scale (N_v columns)
+ * in one product launch over both projections' column tiles.
+ *
+ * w_v_e4m3         [device] [N_v][K] e4m3fn codes, 16-byte aligned; N_v % 128 == 0
+ * w_v_scale        [device] float [N_v/128][K/128], 4-byte aligned
+ * v_buffer         [device] bf16 [>= M][N_v], 16-byte aligned, written
+ * Other arguments, errors and validation order as in mla_decompress_k_paged_fp8_cache.
+ */
+mla_status_t mla_decompress_kv_paged_fp8_cache(const uint32_t* buffer_row_offsets,
+                                               const uint32_t* cache_offsets, int32_t buffer_length,
+                                               const void* w_k_e4m3, const float* w_k_scale, int32_t N_k,
+                                               const void* w_v_e4m3, const float* w_v_scale, int32_t N_v,
+                                               int32_t K, const mla_paged_cache_t* cache,
+                                               const mla_cache_scales_t* cache_scales, uint32_t layer_idx,
+                                               void* k_latent_buffer, float* k_latent_scales,
+                                               void* k_buffer, void* v_buffer, void* stream);
+
+/*
  * Query absorption for decode (page "mla_prefill_decode_graph_fp8", Args q
  * [tot_seq_len, num_heads, qk_nope_head_dim + qk_rope_head_dim] and w_uk
  * [num_heads, kv_latent_dim, qk_nope_head_dim], the weight that projects the

@@ -37,7 +37,7 @@ EXPORTS = ("mla_paged_cache_default_strides", "mla_decompress_k_paged", "mla_gat
            "kv_matmul_paged", "mla_check_indices", "mla_status_string", "mla_last_hip_error",
            "mla_abi_version", "mla_decompress_kv_paged", "mla_decompress_kv_paged_fp8",
            "mla_write_latent_paged", "mla_decompress_k_paged_fp8_cache", "mla_absorb_q", "mla_absorb_q_fp8",
-           "mla_write_latent_paged_fp8")
+           "mla_write_latent_paged_fp8", "mla_decompress_kv_paged_fp8_cache")
 
 
 class MlaError(RuntimeError):
@@ -108,6 +108,10 @@ def lib():
             L.mla_decompress_k_paged_fp8_cache.argtypes = [vp, vp, i32, vp, vp, i32, i32, ctypes.POINTER(CacheDesc),
                                                            ctypes.POINTER(ScalesDesc), u32, vp, vp, vp, vp]
             L.mla_decompress_k_paged_fp8_cache.restype = i32
+            L.mla_decompress_kv_paged_fp8_cache.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, i32, i32,
+                                                            ctypes.POINTER(CacheDesc), ctypes.POINTER(ScalesDesc), u32,
+                                                            vp, vp, vp, vp, vp]
+            L.mla_decompress_kv_paged_fp8_cache.restype = i32
             L.mla_absorb_q.argtypes = [vp, i32, i32, i32, i32, vp, i32, i32, vp, vp]
             L.mla_absorb_q.restype = i32
             L.mla_absorb_q_fp8.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp]
@@ -393,6 +397,41 @@ def mla_decompress_k_paged_fp8_cache(buffer_row_offsets, cache_offsets, buffer_l
                                                 ctypes.byref(sdesc), int(layer_idx), k_latent_buffer.data_ptr(),
                                                 k_latent_scales.data_ptr(), k_buffer.data_ptr(), _stream(stream))
     _check(st, "mla_decompress_k_paged_fp8_cache")
+
+
+def mla_decompress_kv_paged_fp8_cache(buffer_row_offsets, cache_offsets, buffer_length: int, w_k_e4m3, w_k_scale,
+                                      w_v_e4m3, w_v_scale, cache: PagedKVCache, layer_idx: int, k_latent_buffer,
+                                      k_latent_scales, k_buffer, v_buffer, stream=None) -> None:
+    """mla_decompress_k_paged_fp8_cache for K and, from the same gathered codes and
+    scales, v_buffer = block-scaled rows @ w_v.T, in one gather and one product launch."""
+    N, K = _weight_shape(w_k_e4m3, "w_k_e4m3")
+    Nv, Kv = _weight_shape(w_v_e4m3, "w_v_e4m3")
+    if Kv != K:
+        raise ValueError("w_k_e4m3 and w_v_e4m3 must have the same K")
+    desc = cache.descriptor()
+    sdesc = cache.scales_descriptor()
+    D = desc.num_heads * desc.head_dim
+    nblk = -(-D // 128)
+    if k_latent_buffer.numel() * k_latent_buffer.element_size() < buffer_length * D or \
+            not k_latent_buffer.is_contiguous() or k_latent_buffer.element_size() != 1:
+        raise ValueError(f"k_latent_buffer must be a contiguous 1-byte tensor of at least [{buffer_length}, {D}]")
+    if k_latent_scales.numel() < buffer_length * nblk or not k_latent_scales.is_contiguous() or \
+            k_latent_scales.element_size() != 4:
+        raise ValueError(f"k_latent_scales must be a contiguous float32 tensor of at least [{buffer_length}, {nblk}]")
+    for name, buf, n in (("k_buffer", k_buffer, N), ("v_buffer", v_buffer, Nv)):
+        if buf.numel() < buffer_length * n or not buf.is_contiguous():
+            raise ValueError(f"{name} must be contiguous and hold at least [{buffer_length}, {n}]")
+    for name, sc, n in (("w_k_scale", w_k_scale, N), ("w_v_scale", w_v_scale, Nv)):
+        if sc.numel() < -(-n // 128) * -(-K // 128) or sc.element_size() != 4:
+            raise ValueError(f"{name} must hold float32 [{n}/128, K/128]")
+    st = lib().mla_decompress_kv_paged_fp8_cache(_u32(buffer_row_offsets, "buffer_row_offsets"),
+                                                 _u32(cache_offsets, "cache_offsets"), int(buffer_length),
+                                                 w_k_e4m3.data_ptr(), w_k_scale.data_ptr(), N,
+                                                 w_v_e4m3.data_ptr(), w_v_scale.data_ptr(), Nv, K,
+                                                 ctypes.byref(desc), ctypes.byref(sdesc), int(layer_idx),
+                                                 k_latent_buffer.data_ptr(), k_latent_scales.data_ptr(),
+                                                 k_buffer.data_ptr(), v_buffer.data_ptr(), _stream(stream))
+    _check(st, "mla_decompress_kv_paged_fp8_cache")
 
 
 def mla_absorb_q(q, w_uk, q_latent, d_nope: int = 128, copy_rope: bool = True, stream=None) -> None:

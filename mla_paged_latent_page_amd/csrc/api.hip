@@ -431,23 +431,29 @@ MLA_API mla_status_t mla_decompress_kv_paged_fp8(const uint32_t* buffer_row_offs
     return e == hipSuccess ? MLA_OK : hip_failed(e);
 }
 
-MLA_API mla_status_t mla_decompress_k_paged_fp8_cache(const uint32_t* buffer_row_offsets,
-                                                      const uint32_t* cache_offsets, int32_t buffer_length,
-                                                      const void* weight_e4m3, const float* weight_scale,
-                                                      int32_t N, int32_t K, const mla_paged_cache_t* cache,
-                                                      const mla_cache_scales_t* cache_scales, uint32_t layer_idx,
-                                                      void* k_latent_buffer, float* k_latent_scales,
-                                                      void* k_buffer, void* stream)
+namespace {
+
+// The fp8-cache decompress calls (K alone, or K and V): validation in the
+// documented order (pointers, shapes, dtype, alignment, ranges), then one
+// gather of codes and scales and one product launch over both projections.
+mla_status_t decompress_fp8_cache(const uint32_t* buffer_row_offsets, const uint32_t* cache_offsets,
+                                  int32_t buffer_length, const void* weight_e4m3, const float* weight_scale,
+                                  int32_t N, int32_t K, const mla_paged_cache_t* cache,
+                                  const mla_cache_scales_t* cache_scales, uint32_t layer_idx,
+                                  void* k_latent_buffer, float* k_latent_scales, void* k_buffer, const Second& v,
+                                  void* stream)
 {
     if (!cache || !cache_scales)
         return MLA_ERR_NULL_POINTER;
     const int32_t M = buffer_length;
     const bool work = M > 0;
     if (work && (!buffer_row_offsets || !cache_offsets || !weight_e4m3 || !weight_scale || !k_latent_buffer ||
-                 !k_latent_scales || !k_buffer || !cache->blocks || !cache->page_table || !cache_scales->scales))
+                 !k_latent_scales || !k_buffer || !cache->blocks || !cache->page_table || !cache_scales->scales ||
+                 (v.present && (!v.w || !v.scale || !v.out))))
         return MLA_ERR_NULL_POINTER;
     if (M < 0 || N <= 0 || K <= 0 || N % 128 || K % 128 || (int64_t)N * K >= (int64_t(1) << 31) ||
-        cache_scales->granularity != 128)
+        cache_scales->granularity != 128 ||
+        (v.present && (v.N <= 0 || v.N % 128 || (int64_t)v.N * K >= (int64_t(1) << 31))))
         return MLA_ERR_INVALID_SHAPE;
     if (mla_status_t st = check_cache_shape(cache, 1))
         return st;
@@ -460,7 +466,8 @@ MLA_API mla_status_t mla_decompress_k_paged_fp8_cache(const uint32_t* buffer_row
         return MLA_ERR_INVALID_DTYPE;
     if (!aligned16(weight_e4m3) || !aligned16(k_latent_buffer) || !aligned16(k_buffer) ||
         (reinterpret_cast<uintptr_t>(weight_scale) & 3u) || (reinterpret_cast<uintptr_t>(k_latent_scales) & 3u) ||
-        (reinterpret_cast<uintptr_t>(cache_scales->scales) & 3u))
+        (reinterpret_cast<uintptr_t>(cache_scales->scales) & 3u) ||
+        (v.present && (!aligned16(v.w) || !aligned16(v.out) || (reinterpret_cast<uintptr_t>(v.scale) & 3u))))
         return MLA_ERR_MISALIGNED;
     if (mla_status_t st = check_cache_alignment(cache))
         return st;
@@ -471,9 +478,8 @@ MLA_API mla_status_t mla_decompress_k_paged_fp8_cache(const uint32_t* buffer_row
     if (mla_status_t st = check_device())
         return st;
 
-    const Second none;
     mla::DecompressArgs a = decompress_args(buffer_row_offsets, cache_offsets, M, weight_e4m3, N, K, cache,
-                                            layer_idx, k_latent_buffer, k_buffer, D, none);
+                                            layer_idx, k_latent_buffer, k_buffer, D, v);
     a.W_scale = weight_scale;
     a.Ls = a.L;
     a.Ls.base = reinterpret_cast<const char*>(cache_scales->scales + (int64_t)layer_idx * cache_scales->stride_layer);
@@ -484,6 +490,42 @@ MLA_API mla_status_t mla_decompress_k_paged_fp8_cache(const uint32_t* buffer_row
     a.nblk = (int)nblk;
     const hipError_t e = mla::launch_decompress_fp8_cache(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MLA_OK : hip_failed(e);
+}
+
+}  // namespace
+
+MLA_API mla_status_t mla_decompress_k_paged_fp8_cache(const uint32_t* buffer_row_offsets,
+                                                      const uint32_t* cache_offsets, int32_t buffer_length,
+                                                      const void* weight_e4m3, const float* weight_scale,
+                                                      int32_t N, int32_t K, const mla_paged_cache_t* cache,
+                                                      const mla_cache_scales_t* cache_scales, uint32_t layer_idx,
+                                                      void* k_latent_buffer, float* k_latent_scales,
+                                                      void* k_buffer, void* stream)
+{
+    const Second none;
+    return decompress_fp8_cache(buffer_row_offsets, cache_offsets, buffer_length, weight_e4m3, weight_scale, N, K,
+                                cache, cache_scales, layer_idx, k_latent_buffer, k_latent_scales, k_buffer, none,
+                                stream);
+}
+
+MLA_API mla_status_t mla_decompress_kv_paged_fp8_cache(const uint32_t* buffer_row_offsets,
+                                                       const uint32_t* cache_offsets, int32_t buffer_length,
+                                                       const void* w_k_e4m3, const float* w_k_scale, int32_t N_k,
+                                                       const void* w_v_e4m3, const float* w_v_scale, int32_t N_v,
+                                                       int32_t K, const mla_paged_cache_t* cache,
+                                                       const mla_cache_scales_t* cache_scales, uint32_t layer_idx,
+                                                       void* k_latent_buffer, float* k_latent_scales,
+                                                       void* k_buffer, void* v_buffer, void* stream)
+{
+    Second v;
+    v.w = w_v_e4m3;
+    v.scale = w_v_scale;
+    v.N = N_v;
+    v.out = v_buffer;
+    v.present = true;
+    return decompress_fp8_cache(buffer_row_offsets, cache_offsets, buffer_length, w_k_e4m3, w_k_scale, N_k, K,
+                                cache, cache_scales, layer_idx, k_latent_buffer, k_latent_scales, k_buffer, v,
+                                stream);
 }
 
 MLA_API mla_status_t mla_absorb_q(const void* q, int32_t total_tokens, int32_t num_heads, int32_t d_nope,

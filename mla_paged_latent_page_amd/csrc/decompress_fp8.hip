@@ -292,7 +292,7 @@ hipError_t launch_decompress_fp8_cache(const DecompressArgs& a, hipStream_t s)
     const hipError_t e = launch_gather_rows(a, 1, s);
     if (e != hipSuccess)
         return e;
-    DecompressArgs p = first_projection(a);
+    DecompressArgs p = a;   // both projections when a second one is present
     p.q = a.lat;
     p.q_scale = a.lat_scale;
     p.q_ld = a.D;

@@ -291,6 +291,19 @@ def decompress_k_fp8_cache(case, rows=None):
     return codes, scales, out
 
 
+def decompress_kv_fp8_cache(case_k, case_v, rows=None):
+    """(codes, scales, k_buffer rows, v_buffer rows): decompress_k_fp8_cache for
+    W_k and for W_uv on the same gathered codes and scales (case_v is case_k
+    with the weight replaced by W_uv).  Pinned through its parts: the gather,
+    the scale gather and the block-scaled product each have their own pins."""
+    assert case_v.cache is case_k.cache and case_v.K == case_k.K
+    codes, scales, k = decompress_k_fp8_cache(case_k, rows)
+    kb = -(-case_v.K // case_v.k_gran)
+    v = fp8_matmul_nt(codes[:, :case_v.K], scales[:, :kb], case_v.weight_q, case_v.weight_scale,
+                      case_v.n_gran, case_v.k_gran, rows)
+    return codes, scales, k, v
+
+
 def absorb_q(case):
     """(latent part binary64 [T, H, kv_latent_dim], rope part bits [T, H, d_rope]
     or None): query absorption (page "mla_prefill_decode_graph_fp8", Args q

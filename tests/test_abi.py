@@ -418,3 +418,31 @@ def test_write_latent_fp8_error_paths(lib):
     assert write_latent_fp8(lib, d, s, layer=2) == RANGE
     assert write_latent_fp8(lib, d, s, T=0, x=None, iro=None, g=None, f=None) == OK
     assert write_latent_fp8(lib, d, s) == DEV
+
+
+def fp8_cache_kv(lib, d, s, M=100, Nk=512, Nv=256, K=512, layer=1, **ptrs):
+    p = dict(bro=FAKE, co=FAKE, wk=FAKE, sk=FAKE, wv=FAKE, sv=FAKE, lat=FAKE, lsc=FAKE, kout=FAKE, vout=FAKE)
+    p.update(ptrs)
+    return lib.mla_decompress_kv_paged_fp8_cache(p["bro"], p["co"], M, p["wk"], p["sk"], Nk, p["wv"], p["sv"], Nv, K,
+                                                 ctypes.byref(d) if d is not None else None,
+                                                 ctypes.byref(s) if s is not None else None, layer,
+                                                 p["lat"], p["lsc"], p["kout"], p["vout"], None)
+
+
+def test_fp8_cache_kv_error_paths(lib):
+    d = cache_desc(dtype=2)
+    s = scales_desc()
+    assert fp8_cache_kv(lib, None, s) == NULLP
+    assert fp8_cache_kv(lib, d, None) == NULLP
+    for k in ("bro", "co", "wk", "sk", "wv", "sv", "lat", "lsc", "kout", "vout"):
+        assert fp8_cache_kv(lib, d, s, **{k: None}) == NULLP
+    assert fp8_cache_kv(lib, d, s, Nv=192) == SHAPE                 # N_v % 128
+    assert fp8_cache_kv(lib, d, s, Nv=0) == SHAPE
+    assert fp8_cache_kv(lib, d, s, K=640) == SHAPE                  # K > D_c
+    assert fp8_cache_kv(lib, cache_desc(dtype=1), s) == DTYPE
+    assert fp8_cache_kv(lib, d, s, wv=FAKE + 8) == MISAL
+    assert fp8_cache_kv(lib, d, s, vout=FAKE + 8) == MISAL
+    assert fp8_cache_kv(lib, d, s, sv=FAKE + 2) == MISAL
+    assert fp8_cache_kv(lib, d, s, layer=2) == RANGE
+    assert fp8_cache_kv(lib, d, s, M=0) == OK
+    assert fp8_cache_kv(lib, d, s) == DEV

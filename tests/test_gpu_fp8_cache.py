@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+import mla_paged_latent_page_amd as mp
 import oracle
 import workloads as W
 from gpu_util import BF16_TOL, POISON_OUT, check_close, rows_as_f64, run_decompress, run_decompress_fp8_cache, \
@@ -96,3 +97,52 @@ def test_c6_full_size_sampled():
     rows = sample_rows(case)
     say(f"[gpu] c6: {len(rows)} sampled rows")
     _check(case, rows=rows, extra=0)
+
+
+def _run_kv(case, case_v, extra=3):
+    dc, t = W.device_decompress(case)
+    M, D = case.M, case.D_c
+    nblk = case.cache.scale_blocks
+    lat = torch.full((M + extra, D), 0x7F, dtype=torch.uint8, device="cuda")
+    lsc = torch.full((M + extra, nblk), float("nan"), dtype=torch.float32, device="cuda")
+    kout = torch.empty((M + extra, case.N), dtype=torch.bfloat16, device="cuda")
+    vout = torch.empty((M + extra, case_v.N), dtype=torch.bfloat16, device="cuda")
+    kout.view(torch.int16).fill_(POISON_OUT)
+    vout.view(torch.int16).fill_(POISON_OUT)
+    wv = torch.from_numpy(case_v.weight_q).cuda()
+    sv = torch.from_numpy(case_v.weight_scale).cuda()
+    cache = mp.PagedKVCache(dc.pool, dc.page_table, dc.cache_lengths, scales=dc.scales)
+    say(f"[gpu] {case.name} fp8 cache, K and V: M={M} N_k={case.N} N_v={case_v.N} K={case.K}")
+    mp.mla_decompress_kv_paged_fp8_cache(t["buffer_row_offsets"], t["cache_offsets"], M, t["weight_q"],
+                                         t["weight_scale"], wv, sv, cache, case.layer_idx, lat, lsc, kout, vout)
+    torch.cuda.synchronize()
+    return lat, lsc, kout, vout
+
+
+@pytest.mark.parametrize("seed,N,Nv", [(0, 512, 256), (1, 1024, 1024), (2, 256, 384)])
+def test_k_and_v_from_the_fp8_cache(seed, N, Nv):
+    case = _fp8_case(seed, N=N)
+    case_v = W.with_second_projection(case, seed=seed + 100, N=Nv)
+    lat, lsc, kout, vout = _run_kv(case, case_v)
+    M = case.M
+    codes, scales, k, v = oracle.decompress_kv_fp8_cache(case, case_v)
+    assert np.array_equal(to_bits(lat)[:M], codes), "gathered codes differ"
+    assert np.array_equal(lsc.cpu().numpy()[:M].view(np.uint32), scales.view(np.uint32)), "gathered scales differ"
+    check_close(kout[:M].double().cpu().numpy(), k, BF16_TOL, f"{case.name} k_buffer (fp8 cache, fused)")
+    check_close(vout[:M].double().cpu().numpy(), v, BF16_TOL, f"{case.name} v_buffer (fp8 cache, fused)")
+    assert np.all(to_bits(kout)[M:] == POISON_OUT) and np.all(to_bits(vout)[M:] == POISON_OUT)
+    # the K half equals the single-projection call bit for bit
+    single = run_decompress_fp8_cache(case)
+    assert torch.equal(single["out"][:M].view(torch.int16), kout[:M].view(torch.int16))
+
+
+def test_k_and_v_from_the_fp8_cache_at_full_size_sampled():
+    case = W.c6_fp8_cache()
+    case_v = W.with_second_projection(case, seed=606, N=case.N)
+    lat, lsc, kout, vout = _run_kv(case, case_v, extra=0)
+    rows = sample_rows(case)
+    codes, scales, k, v = oracle.decompress_kv_fp8_cache(case, case_v, rows)
+    M = case.M
+    assert np.array_equal(to_bits(lat)[:M], codes), "gathered codes differ"
+    check_close(rows_as_f64(kout, rows), k, BF16_TOL, "c6 k_buffer (fused, sampled rows)")
+    check_close(rows_as_f64(vout, rows), v, BF16_TOL, "c6 v_buffer (fused, sampled rows)")
