@@ -7,15 +7,17 @@
 // that an absorbed query head has the layout of a cache row (latent, then rope).
 //
 // Bound by HBM: at decode sizes the weight (num_heads * 512 * 128 bf16, 16 MiB)
-// and the output dominate.  One block of 4 waves per head and 128 latent
-// columns; the kv_latent_dim / 128 blocks of one head are dispatched to the
-// same XCD, next to each other, so they read that head's query rows from HBM
-// once and share them in the XCD's L2.  The weight tile (128 x 128, 32 KB) is
-// put into LDS once; query rows follow in chunks of 128 (32 KB), both by LDS
-// DMA from inline assembly with explicit waits.  v_mfma_f32_32x32x16_bf16 with
-// the weight as the row operand: wave w owns the tile's latent columns
-// 32 w .. 32 w + 31 for all 128 rows of a chunk and stores 4 consecutive
-// columns per lane.
+// and the output dominate.  One block of 4 waves per head and two 128-column
+// tiles of the latent columns (one when kv_latent_dim / 128 is odd); the
+// blocks of one head are dispatched to the same XCD, next to each other, so
+// they read that head's query rows from HBM once and share them in the XCD's
+// L2.  Query rows come in chunks of 128 (32 KB) and each weight tile
+// (128 x 128, 32 KB) once, all into LDS by loads issued from inline assembly
+// with explicit waits, in the order query chunk, tile 0, tile 1: tile 0 is
+// computed and stored while tile 1 is still arriving.  v_mfma_f32_32x32x16_bf16
+// with the weight as the row operand: wave w owns a tile's latent columns
+// 32 w .. 32 w + 31 for all 128 rows of a chunk; the results go through LDS so
+// that each store writes whole 256-byte row segments.
 #include "launch.hpp"
 
 namespace mla {
