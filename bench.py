@@ -17,6 +17,7 @@ The JSON line also carries the other rows of the path, each timed the same way:
   c6_fp8_cache the same shapes read from an e4m3 cache with per-128-column scales
   c4_kv_matmul write path, 128 lognormal requests, hidden 4096 -> 2 x 8 x 128
   c2_fused_kv  K and V decompression in one call, against two separate calls
+  c6_fused_kv_fp8_cache  the same from the e4m3 cache, against two calls
   c2_tp8_share one GPU's share of W_k when 8 GPUs split the heads (N = 2048)
   c5_latent_write  RMSNorm + rope rotation + scatter of 88994 new tokens'
                rows into the MLA pages (HBM-bound), and c5_latent_write_fp8
@@ -474,6 +475,38 @@ def main():
                                         "+ fp8 product on them (gemm_fp8_ring); no quantisation pass"}
         print(f"[bench] c6_fp8_cache: {t.avg_launch_ms:.3f} ms, {tf:.1f} TFLOP/s, {gbs:.0f} GB/s", file=sys.stderr,
               flush=True)
+        # K and V from the same e4m3 cache in one call, against two single-projection calls
+        cv8 = W.with_second_projection(c, seed=1006, N=c.N)
+        wv8 = torch.from_numpy(cv8.weight_q).cuda()
+        sv8 = torch.from_numpy(cv8.weight_scale).cuda()
+        f8vout = torch.empty((c.M, cv8.N), dtype=torch.bfloat16, device="cuda")
+
+        def f8kv_fn():
+            mp.mla_decompress_kv_paged_fp8_cache(tt["buffer_row_offsets"], tt["cache_offsets"], c.M, tt["weight_q"],
+                                                 tt["weight_scale"], wv8, sv8, f8cache, c.layer_idx, f8lat, f8sc,
+                                                 f8out, f8vout)
+
+        def f8kv_separate():
+            f8_fn()
+            mp.mla_decompress_k_paged_fp8_cache(tt["buffer_row_offsets"], tt["cache_offsets"], c.M, wv8, sv8, f8cache,
+                                                c.layer_idx, f8lat, f8sc, f8vout)
+        t = Timed(torch, f8kv_fn, steps, args.warmup)
+        t2 = Timed(torch, f8kv_separate, steps, args.warmup)
+        f = 2.0 * c.M * (c.N + cv8.N) * c.K
+        b = (c.M * (2 * (c.D_c + nblk * 4) + (c.N + cv8.N) * 2) + (c.N + cv8.N) * c.K + c.weight_scale.nbytes
+             + cv8.weight_scale.nbytes)
+        tf = f / (t.avg_launch_ms * 1e-3) / 1e12
+        gbs = b / (t.avg_launch_ms * 1e-3) / 1e9
+        rows["c6_fused_kv_fp8_cache"] = {
+            "rows": c.M, "ms": round(t.avg_launch_ms, 4), "separate_calls_ms": round(t2.avg_launch_ms, 4),
+            "tflops": round(tf, 2), "hbm_gbs_algorithmic": round(gbs, 1), "fp8_mfma_frac": round(tf / PEAK_FP8_TFLOPS, 4),
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s",
+                                 traffic_from_profile("gemm_fp8_ring", "c6_fused_kv_fp8_cache")),
+            "note": "one gather of codes and scales + one gemm_fp8_ring launch over W_k's and W_uv's N-tiles; "
+                    "separate_calls_ms: two mla_decompress_k_paged_fp8_cache calls (W_k, then W_uv)"}
+        print(f"[bench] c6_fused_kv_fp8_cache: {t.avg_launch_ms:.3f} ms, {gbs:.0f} GB/s; separate calls "
+              f"{t2.avg_launch_ms:.3f} ms", file=sys.stderr, flush=True)
+        del f8kv_fn, f8kv_separate, wv8, sv8, f8vout
         del f8_fn, f8lat, f8sc, f8out, f8cache, dc, tt
         torch.cuda.empty_cache()
         # fused K and V on the prefill batch (W_uv drawn like W_k), against the
