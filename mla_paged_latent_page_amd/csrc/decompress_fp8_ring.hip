@@ -89,6 +89,7 @@ __device__ inline Fp8Segment segment_of(const Fp8GemmParams& P, int tn)
         return Fp8Segment{P.W, P.SW, P.C, P.N, tn};
     return Fp8Segment{P.W2, P.SW2, P.C2, P.N2, tn - P.tiles_n1};
 }
+__device__ inline int first_projection_tiles(const Fp8GemmParams& P) { return P.tiles_n1; }
 
 struct Cursor {
     int tile, ks, tn, row0;     // tn: the tile's index within its projection
@@ -384,7 +385,14 @@ hipError_t launch_product_fp8_ring(const DecompressArgs& a, int cus, hipStream_t
     P.C2 = static_cast<uint16_t*>(a.out2);
     P.N2 = a.N2;
     P.tiles_n += a.N2 / BN;
-    P.xcd_map = (P.tiles_n % 8 == 0 && cus % 8 == 0) ? 1 : 0;
+    if (a.N2 > 0) {
+        // Two projections: both eighths of the weight at once would take half
+        // of an XCD's L2 and get evicted by the streaming rows, so each XCD
+        // walks the rows over its eighth of one projection, then the other's.
+        P.xcd_map = (P.tiles_n1 % 8 == 0 && (P.tiles_n - P.tiles_n1) % 8 == 0 && cus % 8 == 0) ? 3 : 0;
+    } else {
+        P.xcd_map = (P.tiles_n % 8 == 0 && cus % 8 == 0) ? 1 : 0;
+    }
     const int tiles = P.tiles_m * P.tiles_n;
     const int grid = P.xcd_map ? cus : (tiles < cus ? tiles : cus);
     hipLaunchKernelGGL(gemm_fp8_ring, dim3(grid), dim3(NT), 0, s, P);
