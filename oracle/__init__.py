@@ -294,8 +294,10 @@ def decompress_k_fp8_cache(case, rows=None):
 def decompress_kv_fp8_cache(case_k, case_v, rows=None):
     """(codes, scales, k_buffer rows, v_buffer rows): decompress_k_fp8_cache for
     W_k and for W_uv on the same gathered codes and scales (case_v is case_k
-    with the weight replaced by W_uv).  Pinned through its parts: the gather,
-    the scale gather and the block-scaled product each have their own pins."""
+    with the weight replaced by W_uv).  Pinned by: K and V each equal the
+    single-projection form on that projection's own weight, and a selection
+    W_uv (code 1.0, unit scales) returns the named latent columns dequantised
+    with their own block's scale, exactly."""
     assert case_v.cache is case_k.cache and case_v.K == case_k.K
     codes, scales, k = decompress_k_fp8_cache(case_k, rows)
     kb = -(-case_v.K // case_v.k_gran)

@@ -100,3 +100,52 @@ def test_preconditions():
     f8 = dataclasses.replace(f8, cache=dataclasses.replace(f8.cache, scale_gran=64))
     with pytest.raises(oracle.OracleError):
         oracle.decompress_k_fp8_cache(f8)            # scales per 64 columns do not fit 1x128 blocks
+
+
+# ---- the V leg of the fused K and V form on an fp8 cache (page
+# "mla_prefill_decode_graph_fp8", Args w_uv and w_uv_scale: the same latent
+# rows projected by a second weight)
+
+def _kv_cases(seed, N=256, Nv=384):
+    case = W.small_decompress(seed, batch=4, max_len=120, page_size=16, N=N, dtype="e4m3", fp8=True)
+    return case, W.with_second_projection(case, seed=seed + 100, N=Nv)
+
+
+def check_kv_each_projection_on_its_own_weight(orc, seed=21):
+    """K and V each equal the single-projection form run on that projection's
+    own weight and scales; V differs from K wherever the weights differ."""
+    case, case_v = _kv_cases(seed)
+    codes, scales, k, v = orc.decompress_kv_fp8_cache(case, case_v)
+    c1, s1, k1 = oracle.decompress_k_fp8_cache(case)
+    c2, s2, v1 = oracle.decompress_k_fp8_cache(case_v)
+    assert np.array_equal(codes, c1) and np.array_equal(scales, s1)
+    assert np.array_equal(k, k1)
+    assert v.shape == v1.shape and np.array_equal(v, v1)
+
+
+def check_kv_selection_w_uv(orc, seed=22):
+    """A selection W_uv (row n holds code 1.0 at column pi(n), zeros elsewhere;
+    unit block scales) returns the named latent columns, dequantised with the
+    cache's own scale of the block each column lies in, exactly: one non-zero
+    product per output, so no rounding is involved."""
+    case, case_v = _kv_cases(seed, Nv=256)
+    K, Nv = case.K, case_v.N
+    rng = np.random.default_rng(seed)
+    pi = rng.permutation(K)[:Nv]
+    wq = np.zeros((Nv, K), np.uint8)
+    wq[np.arange(Nv), pi] = 0x38                     # e4m3fn 1.0: exponent 7 (bias 7), mantissa 0
+    case_v = dataclasses.replace(case_v, weight_q=wq,
+                                 weight_scale=np.ones_like(case_v.weight_scale))
+    codes, scales, _, v = orc.decompress_kv_fp8_cache(case, case_v)
+    deq = oracle.e4m3_decode(codes[:, :K]).astype(np.float64) * \
+        np.repeat(scales[:, :K // 128].astype(np.float64), 128, axis=1)
+    assert len({int(p) // 128 for p in pi}) == K // 128    # columns from every scale block
+    assert np.array_equal(v, deq[:, pi])
+
+
+def test_kv_each_projection_on_its_own_weight():
+    check_kv_each_projection_on_its_own_weight(oracle)
+
+
+def test_kv_selection_w_uv_returns_the_named_dequantised_columns():
+    check_kv_selection_w_uv(oracle)

@@ -1,7 +1,12 @@
 """The oracle's pins are strong enough: plant one plausible mistake at a time
 in a copy of the oracle's C source (a wrong index, a dropped term, a flipped
 sign, a transposed operand, a wrong rounding tie), build it, run the pin
-tests against it, and require that every mutant fails at least one pin."""
+tests against it, and require that every mutant fails at least one pin.
+
+The arithmetic of the fused K and V form on an fp8 cache is put together in
+the oracle's Python layer, so its mutants are planted in a copy of that
+module's source and run against the two V-leg pins directly."""
+import importlib.util
 import os
 import subprocess
 import sys
@@ -68,3 +73,39 @@ def test_every_planted_mistake_fails_a_pin(tmp_path):
         results = list(ex.map(lambda n: _run_mutant(n, str(tmp_path)), MUTANTS))
     survivors = [n for n, rc in results if rc == 0]
     assert not survivors, f"mutants not caught by any pin: {survivors}"
+
+
+# mistakes in how the V leg of the fp8-cache fused form is assembled
+PY_SRC = os.path.join(ROOT, "oracle", "__init__.py")
+PY_MUTANTS = {
+    "v_reads_w_k": ("v = fp8_matmul_nt(codes[:, :case_v.K], scales[:, :kb], case_v.weight_q, case_v.weight_scale,",
+                    "v = fp8_matmul_nt(codes[:, :case_v.K], scales[:, :kb], case_k.weight_q, case_k.weight_scale,"),
+    "v_scale_slice_shifted": ("v = fp8_matmul_nt(codes[:, :case_v.K], scales[:, :kb],",
+                              "v = fp8_matmul_nt(codes[:, :case_v.K], scales[:, 1:kb + 1],"),
+}
+
+
+def _python_mutant(name):
+    import oracle
+    old, new = PY_MUTANTS[name]
+    src = open(PY_SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/found"
+    spec = importlib.util.spec_from_loader(f"oracle_mutant_{name}", loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    mod.__file__ = oracle.__file__      # loads the same built C library
+    exec(compile(src.replace(old, new), PY_SRC, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_v_leg_mistakes_fail_a_pin(name):
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import test_oracle_fp8_cache as pins
+    mod = _python_mutant(name)
+    caught = 0
+    for check in (pins.check_kv_each_projection_on_its_own_weight, pins.check_kv_selection_w_uv):
+        try:
+            check(mod)
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught, f"python mutant {name} passed every V-leg pin"
