@@ -203,18 +203,88 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _u32(t, what):
-    if t.element_size() != 4 or not t.is_contiguous():
-        raise ValueError(f"{what} must be a contiguous 32-bit tensor")
+def _on_device(t, what):
+    """Device pointer of a tensor that lives on the current GPU; anything else
+    (a host tensor, another GPU's tensor) is refused before any launch."""
+    import torch
+    if t is None or not isinstance(t, torch.Tensor) or not t.is_cuda or t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{what} must be a tensor on the current GPU")
     return t.data_ptr()
 
 
-def _check_outputs(M, desc, N, k_latent_buffer, k_buffer):
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _buf(t, what, nbytes, dtypes=None):
+    """Check a contiguous tensor of at least ``nbytes`` bytes (and, when given,
+    one of ``dtypes``); returns its pointer.  Where it lives is checked by
+    _gpu() once every shape, dtype and size check has passed."""
+    if t is None:
+        raise ValueError(f"{what} is required")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{what} must be of dtype {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if _nbytes(t) < nbytes:
+        raise ValueError(f"{what} holds {_nbytes(t)} bytes; the call reads or writes {nbytes}")
+    return t.data_ptr()
+
+
+def _u32(t, what, entries=0):
+    if t.element_size() != 4 or not t.is_contiguous() or t.dtype.is_floating_point:
+        raise ValueError(f"{what} must be a contiguous 32-bit integer tensor")
+    if t.numel() < entries:
+        raise ValueError(f"{what} must have at least {entries} entries")
+    return t.data_ptr()
+
+
+def _gpu(**tensors):
+    """Every tensor a call hands to the library must be on the current GPU."""
+    for name, t in tensors.items():
+        if t is not None:
+            _on_device(t, name)
+
+
+def _dtypes():
+    import torch
+    return {MLA_DTYPE_F32: (torch.float32,), MLA_DTYPE_BF16: (torch.bfloat16,),
+            MLA_DTYPE_F8E4M3FN: (torch.uint8, torch.float8_e4m3fn)}
+
+
+def _bytes_of(dtype_code):
+    return {MLA_DTYPE_F32: 4, MLA_DTYPE_BF16: 2, MLA_DTYPE_F8E4M3FN: 1}.get(dtype_code, 1)
+
+
+def _cache_desc(cache, scales=False):
+    """The cache's descriptor(s)."""
+    desc = cache.descriptor()
+    if not scales:
+        return desc
+    return desc, cache.scales_descriptor()
+
+
+def _cache_tensors(cache):
+    return {"cache.pool": cache.pool, "cache.page_table": cache.page_table,
+            "cache.cache_lengths": cache.cache_lengths, "cache.scales": cache.scales}
+
+
+def _index_args(buffer_row_offsets, cache_offsets, desc):
+    B = desc.batch_size
+    return (_u32(buffer_row_offsets, "buffer_row_offsets", B + 1), _u32(cache_offsets, "cache_offsets", B))
+
+
+def _check_outputs(M, desc, N, k_latent_buffer, k_buffer, out_dtype=None):
+    """k_latent_buffer holds M cache rows in the cache's dtype, k_buffer M rows of
+    N values of ``out_dtype`` (default: the cache's dtype)."""
+    dt = _dtypes()
     D = desc.num_heads * desc.head_dim
-    if k_latent_buffer.numel() < M * D or k_buffer.numel() < M * N:
-        raise ValueError(f"outputs must hold at least [{M}, {D}] and [{M}, {N}] elements")
-    if not (k_latent_buffer.is_contiguous() and k_buffer.is_contiguous()):
-        raise ValueError("outputs must be contiguous")
+    eb = _bytes_of(desc.dtype)
+    lat = _buf(k_latent_buffer, "k_latent_buffer", M * D * eb, dt.get(desc.dtype))
+    odt = dt.get(desc.dtype) if out_dtype is None else out_dtype
+    ob = _bytes_of(desc.dtype) if out_dtype is None else 2
+    out = _buf(k_buffer, "k_buffer", M * N * ob, odt)
+    return lat, out
 
 
 def _check(status, what):
@@ -227,32 +297,44 @@ def _check(status, what):
 # ---------------------------------------------------------------------------
 # operations
 # ---------------------------------------------------------------------------
+def _weight(w, name, dtypes):
+    if w is None or w.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D [N, K] tensor")
+    N, K = w.shape
+    return N, K, _buf(w, name, N * K * w.element_size(), dtypes)
+
+
+def _f32(t, name, count):
+    import torch
+    return _buf(t, name, count * 4, (torch.float32,))
+
+
 def mla_decompress_k_paged(buffer_row_offsets, cache_offsets, buffer_length: int, weight,
                            cache: PagedKVCache, layer_idx: int, k_latent_buffer, k_buffer,
                            stream=None) -> None:
     """k_latent_buffer[r] = paged cache row; k_buffer = k_latent_buffer[:, :K] @ weight.T."""
-    if weight.dim() != 2 or not weight.is_contiguous():
-        raise ValueError("weight must be a contiguous [N, K] tensor")
-    N, K = weight.shape
-    desc = cache.descriptor()
-    _check_outputs(buffer_length, desc, N, k_latent_buffer, k_buffer)
-    st = lib().mla_decompress_k_paged(_u32(buffer_row_offsets, "buffer_row_offsets"),
-                                      _u32(cache_offsets, "cache_offsets"), int(buffer_length),
-                                      weight.data_ptr(), N, K, ctypes.byref(desc), int(layer_idx),
-                                      k_latent_buffer.data_ptr(), k_buffer.data_ptr(), _stream(stream))
+    desc = _cache_desc(cache)
+    N, K, w = _weight(weight, "weight", _dtypes().get(desc.dtype))
+    lat, out = _check_outputs(buffer_length, desc, N, k_latent_buffer, k_buffer)
+    bro, co = _index_args(buffer_row_offsets, cache_offsets, desc)
+    _gpu(buffer_row_offsets=buffer_row_offsets, cache_offsets=cache_offsets, weight=weight,
+         k_latent_buffer=k_latent_buffer, k_buffer=k_buffer, **_cache_tensors(cache))
+    st = lib().mla_decompress_k_paged(bro, co, int(buffer_length), w, N, K, ctypes.byref(desc), int(layer_idx),
+                                      lat, out, _stream(stream))
     _check(st, "mla_decompress_k_paged")
 
 
 def mla_gather_latent_paged(buffer_row_offsets, cache_offsets, buffer_length: int, cache: PagedKVCache,
                             layer_idx: int, k_latent_buffer, stream=None) -> None:
     """k_latent_buffer[r] = paged cache row (the gather step alone)."""
-    desc = cache.descriptor()
+    desc = _cache_desc(cache)
     D = desc.num_heads * desc.head_dim
-    if k_latent_buffer.numel() < buffer_length * D or not k_latent_buffer.is_contiguous():
-        raise ValueError(f"k_latent_buffer must be contiguous and hold at least [{buffer_length}, {D}]")
-    st = lib().mla_gather_latent_paged(_u32(buffer_row_offsets, "buffer_row_offsets"),
-                                       _u32(cache_offsets, "cache_offsets"), int(buffer_length),
-                                       ctypes.byref(desc), int(layer_idx), k_latent_buffer.data_ptr(),
+    lat = _buf(k_latent_buffer, "k_latent_buffer", buffer_length * D * _bytes_of(desc.dtype),
+               _dtypes().get(desc.dtype))
+    bro, co = _index_args(buffer_row_offsets, cache_offsets, desc)
+    _gpu(buffer_row_offsets=buffer_row_offsets, cache_offsets=cache_offsets, k_latent_buffer=k_latent_buffer,
+         **_cache_tensors(cache))
+    st = lib().mla_gather_latent_paged(bro, co, int(buffer_length), ctypes.byref(desc), int(layer_idx), lat,
                                        _stream(stream))
     _check(st, "mla_gather_latent_paged")
 
@@ -261,28 +343,31 @@ def mla_latent_matmul(k_latent_buffer, buffer_length: int, weight, k_buffer, str
     """k_buffer[:M] = k_latent_buffer[:M, :K] @ weight.T (the up-projection step alone).
     k_latent_buffer is a 2-D tensor with unit column stride (its row stride is passed)."""
     import torch
-    if weight.dim() != 2 or not weight.is_contiguous():
-        raise ValueError("weight must be a contiguous [N, K] tensor")
-    N, K = weight.shape
-    if k_latent_buffer.dim() != 2 or k_latent_buffer.stride(1) != 1 or k_latent_buffer.shape[0] < buffer_length:
+    if weight is None or weight.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("weight must be a float32 or bfloat16 [N, K] tensor")
+    N, K, w = _weight(weight, "weight", (weight.dtype,))
+    M = int(buffer_length)
+    if k_latent_buffer.dim() != 2 or k_latent_buffer.stride(1) != 1 or k_latent_buffer.shape[0] < M:
         raise ValueError("k_latent_buffer must be a [>= M, >= K] tensor with unit column stride")
     if k_latent_buffer.shape[1] < K or k_latent_buffer.dtype != weight.dtype or k_buffer.dtype != weight.dtype:
         raise ValueError("k_latent_buffer, weight and k_buffer must share a dtype, and K <= latent width")
-    if k_buffer.numel() < buffer_length * N or not k_buffer.is_contiguous():
-        raise ValueError(f"k_buffer must be contiguous and hold at least [{buffer_length}, {N}]")
-    dt = {torch.float32: MLA_DTYPE_F32, torch.bfloat16: MLA_DTYPE_BF16}.get(weight.dtype, -1)
-    st = lib().mla_latent_matmul(k_latent_buffer.data_ptr(), k_latent_buffer.stride(0), int(buffer_length),
-                                 weight.data_ptr(), N, K, dt, k_buffer.data_ptr(), _stream(stream))
+    out = _buf(k_buffer, "k_buffer", M * N * weight.element_size(), (weight.dtype,))
+    _gpu(k_latent_buffer=k_latent_buffer, weight=weight, k_buffer=k_buffer)
+    lat = k_latent_buffer.data_ptr()
+    dt = {torch.float32: MLA_DTYPE_F32, torch.bfloat16: MLA_DTYPE_BF16}[weight.dtype]
+    st = lib().mla_latent_matmul(lat, k_latent_buffer.stride(0), M, w, N, K, dt, out, _stream(stream))
     _check(st, "mla_latent_matmul")
 
 
 def mla_check_indices(row_offsets, cache_offsets, rows: int, cache: PagedKVCache, stream=None):
     """Debug validation of a call's index arrays (synchronous).  Returns
     (status, first failing request or -1); never raises on a failed check."""
-    desc = cache.descriptor()
+    desc = _cache_desc(cache)
     bad = ctypes.c_int64(-1)
-    st = lib().mla_check_indices(_u32(row_offsets, "row_offsets"),
-                                 _u32(cache_offsets, "cache_offsets") if cache_offsets is not None else None,
+    _gpu(row_offsets=row_offsets, cache_offsets=cache_offsets, **_cache_tensors(cache))
+    st = lib().mla_check_indices(_u32(row_offsets, "row_offsets", desc.batch_size + 1),
+                                 _u32(cache_offsets, "cache_offsets", desc.batch_size)
+                                 if cache_offsets is not None else None,
                                  int(rows), ctypes.byref(desc), ctypes.byref(bad), _stream(stream))
     if st in (1, 7, 8):
         _check(st, "mla_check_indices")
@@ -293,53 +378,57 @@ def mla_decompress_k_paged_fp8_workspace_size(buffer_length: int, K: int, k_gran
     return int(lib().mla_decompress_k_paged_fp8_workspace_size(int(buffer_length), int(K), int(k_gran)))
 
 
+def _fp8_scale(sc, name, N, K, n_gran, k_gran):
+    return _f32(sc, name, -(-N // n_gran) * -(-K // k_gran))
+
+
+def _workspace(workspace):
+    if workspace is None:
+        raise ValueError("workspace is required")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return workspace.data_ptr(), _nbytes(workspace)
+
+
 def mla_decompress_k_paged_fp8(buffer_row_offsets, cache_offsets, buffer_length: int, weight_e4m3,
                                weight_scale, cache: PagedKVCache, layer_idx: int, k_latent_buffer,
                                k_buffer, workspace, m_gran: int = 1, n_gran: int = 128,
                                k_gran: int = 128, stream=None) -> None:
-    """The fp8 block-scaled form; ``workspace`` is a uint8 device tensor of at least
+    """The fp8 block-scaled form; ``workspace`` is a device tensor of at least
     mla_decompress_k_paged_fp8_workspace_size(M, K) bytes."""
-    if weight_e4m3.dim() != 2 or not weight_e4m3.is_contiguous():
-        raise ValueError("weight_e4m3 must be a contiguous [N, K] tensor")
-    N, K = weight_e4m3.shape
-    desc = cache.descriptor()
-    _check_outputs(buffer_length, desc, N, k_latent_buffer, k_buffer)
-    if weight_scale.numel() < -(-N // n_gran) * -(-K // k_gran) or weight_scale.element_size() != 4:
-        raise ValueError("weight_scale must hold float32 [N/n_gran, K/k_gran]")
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib().mla_decompress_k_paged_fp8(_u32(buffer_row_offsets, "buffer_row_offsets"),
-                                          _u32(cache_offsets, "cache_offsets"), int(buffer_length),
-                                          weight_e4m3.data_ptr(), weight_scale.data_ptr(), N, K,
-                                          m_gran, n_gran, k_gran, ctypes.byref(desc), int(layer_idx),
-                                          k_latent_buffer.data_ptr(), k_buffer.data_ptr(),
-                                          workspace.data_ptr() if workspace is not None else None,
-                                          ws_bytes, _stream(stream))
+    import torch
+    desc = _cache_desc(cache)
+    N, K, w = _weight(weight_e4m3, "weight_e4m3", _dtypes()[MLA_DTYPE_F8E4M3FN])
+    sw = _fp8_scale(weight_scale, "weight_scale", N, K, n_gran, k_gran)
+    lat, out = _check_outputs(buffer_length, desc, N, k_latent_buffer, k_buffer, (torch.bfloat16,))
+    bro, co = _index_args(buffer_row_offsets, cache_offsets, desc)
+    ws, ws_bytes = _workspace(workspace)
+    _gpu(buffer_row_offsets=buffer_row_offsets, cache_offsets=cache_offsets, weight_e4m3=weight_e4m3,
+         weight_scale=weight_scale, k_latent_buffer=k_latent_buffer, k_buffer=k_buffer, workspace=workspace,
+         **_cache_tensors(cache))
+    st = lib().mla_decompress_k_paged_fp8(bro, co, int(buffer_length), w, sw, N, K, m_gran, n_gran, k_gran,
+                                          ctypes.byref(desc), int(layer_idx), lat, out, ws, ws_bytes,
+                                          _stream(stream))
     _check(st, "mla_decompress_k_paged_fp8")
-
-
-def _weight_shape(w, name):
-    if w.dim() != 2 or not w.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous [N, K] tensor")
-    return w.shape
 
 
 def mla_decompress_kv_paged(buffer_row_offsets, cache_offsets, buffer_length: int, w_k, w_v,
                             cache: PagedKVCache, layer_idx: int, k_latent_buffer, k_buffer, v_buffer,
                             stream=None) -> None:
     """One gather, two up-projections: k_buffer = rows @ w_k.T, v_buffer = rows @ w_v.T."""
-    N_k, K = _weight_shape(w_k, "w_k")
-    N_v, K_v = _weight_shape(w_v, "w_v")
+    desc = _cache_desc(cache)
+    dt = _dtypes().get(desc.dtype)
+    N_k, K, wk = _weight(w_k, "w_k", dt)
+    N_v, K_v, wv = _weight(w_v, "w_v", dt)
     if K_v != K:
         raise ValueError("w_k and w_v must have the same K")
-    desc = cache.descriptor()
-    _check_outputs(buffer_length, desc, N_k, k_latent_buffer, k_buffer)
-    if v_buffer.numel() < buffer_length * N_v or not v_buffer.is_contiguous():
-        raise ValueError(f"v_buffer must be contiguous and hold at least [{buffer_length}, {N_v}]")
-    st = lib().mla_decompress_kv_paged(_u32(buffer_row_offsets, "buffer_row_offsets"),
-                                       _u32(cache_offsets, "cache_offsets"), int(buffer_length),
-                                       w_k.data_ptr(), N_k, w_v.data_ptr(), N_v, K, ctypes.byref(desc),
-                                       int(layer_idx), k_latent_buffer.data_ptr(), k_buffer.data_ptr(),
-                                       v_buffer.data_ptr(), _stream(stream))
+    lat, kout = _check_outputs(buffer_length, desc, N_k, k_latent_buffer, k_buffer)
+    vout = _buf(v_buffer, "v_buffer", buffer_length * N_v * _bytes_of(desc.dtype), dt)
+    bro, co = _index_args(buffer_row_offsets, cache_offsets, desc)
+    _gpu(buffer_row_offsets=buffer_row_offsets, cache_offsets=cache_offsets, w_k=w_k, w_v=w_v,
+         k_latent_buffer=k_latent_buffer, k_buffer=k_buffer, v_buffer=v_buffer, **_cache_tensors(cache))
+    st = lib().mla_decompress_kv_paged(bro, co, int(buffer_length), wk, N_k, wv, N_v, K, ctypes.byref(desc),
+                                       int(layer_idx), lat, kout, vout, _stream(stream))
     _check(st, "mla_decompress_kv_paged")
 
 
@@ -348,27 +437,35 @@ def mla_decompress_kv_paged_fp8(buffer_row_offsets, cache_offsets, buffer_length
                                 k_buffer, v_buffer, workspace, m_gran: int = 1, n_gran: int = 128,
                                 k_gran: int = 128, stream=None) -> None:
     """The fp8 block-scaled fused form (one gather and quantisation, two products)."""
-    N_k, K = _weight_shape(w_k_e4m3, "w_k_e4m3")
-    N_v, K_v = _weight_shape(w_v_e4m3, "w_v_e4m3")
+    import torch
+    desc = _cache_desc(cache)
+    f8 = _dtypes()[MLA_DTYPE_F8E4M3FN]
+    N_k, K, wk = _weight(w_k_e4m3, "w_k_e4m3", f8)
+    N_v, K_v, wv = _weight(w_v_e4m3, "w_v_e4m3", f8)
     if K_v != K:
         raise ValueError("w_k_e4m3 and w_v_e4m3 must have the same K")
-    desc = cache.descriptor()
-    _check_outputs(buffer_length, desc, N_k, k_latent_buffer, k_buffer)
-    if v_buffer.numel() < buffer_length * N_v or not v_buffer.is_contiguous():
-        raise ValueError(f"v_buffer must be contiguous and hold at least [{buffer_length}, {N_v}]")
-    for sc, n, nm in ((w_k_scale, N_k, "w_k_scale"), (w_v_scale, N_v, "w_v_scale")):
-        if sc.numel() < -(-n // n_gran) * -(-K // k_gran) or sc.element_size() != 4:
-            raise ValueError(f"{nm} must hold float32 [N/n_gran, K/k_gran]")
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib().mla_decompress_kv_paged_fp8(_u32(buffer_row_offsets, "buffer_row_offsets"),
-                                           _u32(cache_offsets, "cache_offsets"), int(buffer_length),
-                                           w_k_e4m3.data_ptr(), w_k_scale.data_ptr(), N_k,
-                                           w_v_e4m3.data_ptr(), w_v_scale.data_ptr(), N_v, K,
+    sk = _fp8_scale(w_k_scale, "w_k_scale", N_k, K, n_gran, k_gran)
+    sv = _fp8_scale(w_v_scale, "w_v_scale", N_v, K, n_gran, k_gran)
+    lat, kout = _check_outputs(buffer_length, desc, N_k, k_latent_buffer, k_buffer, (torch.bfloat16,))
+    vout = _buf(v_buffer, "v_buffer", buffer_length * N_v * 2, (torch.bfloat16,))
+    bro, co = _index_args(buffer_row_offsets, cache_offsets, desc)
+    ws, ws_bytes = _workspace(workspace)
+    _gpu(buffer_row_offsets=buffer_row_offsets, cache_offsets=cache_offsets, w_k_e4m3=w_k_e4m3,
+         w_k_scale=w_k_scale, w_v_e4m3=w_v_e4m3, w_v_scale=w_v_scale, k_latent_buffer=k_latent_buffer,
+         k_buffer=k_buffer, v_buffer=v_buffer, workspace=workspace, **_cache_tensors(cache))
+    st = lib().mla_decompress_kv_paged_fp8(bro, co, int(buffer_length), wk, sk, N_k, wv, sv, N_v, K,
                                            m_gran, n_gran, k_gran, ctypes.byref(desc), int(layer_idx),
-                                           k_latent_buffer.data_ptr(), k_buffer.data_ptr(), v_buffer.data_ptr(),
-                                           workspace.data_ptr() if workspace is not None else None,
-                                           ws_bytes, _stream(stream))
+                                           lat, kout, vout, ws, ws_bytes, _stream(stream))
     _check(st, "mla_decompress_kv_paged_fp8")
+
+
+def _fp8_cache_buffers(desc, buffer_length, k_latent_buffer, k_latent_scales):
+    import torch
+    D = desc.num_heads * desc.head_dim
+    nblk = -(-D // 128)
+    lat = _buf(k_latent_buffer, "k_latent_buffer", buffer_length * D, _dtypes()[MLA_DTYPE_F8E4M3FN])
+    lsc = _buf(k_latent_scales, "k_latent_scales", buffer_length * nblk * 4, (torch.float32,))
+    return lat, lsc
 
 
 def mla_decompress_k_paged_fp8_cache(buffer_row_offsets, cache_offsets, buffer_length: int, w_k_e4m3, w_k_scale,
@@ -376,26 +473,19 @@ def mla_decompress_k_paged_fp8_cache(buffer_row_offsets, cache_offsets, buffer_l
                                      stream=None) -> None:
     """Gather e4m3 rows and their scales from an fp8 cache (bit copies into
     k_latent_buffer / k_latent_scales), then k_buffer = block-scaled rows @ w_k.T."""
-    N, K = _weight_shape(w_k_e4m3, "w_k_e4m3")
-    desc = cache.descriptor()
-    sdesc = cache.scales_descriptor()
-    D = desc.num_heads * desc.head_dim
-    nblk = -(-D // 128)
-    if k_latent_buffer.numel() * k_latent_buffer.element_size() < buffer_length * D or \
-            not k_latent_buffer.is_contiguous() or k_latent_buffer.element_size() != 1:
-        raise ValueError(f"k_latent_buffer must be a contiguous 1-byte tensor of at least [{buffer_length}, {D}]")
-    if k_latent_scales.numel() < buffer_length * nblk or not k_latent_scales.is_contiguous() or \
-            k_latent_scales.element_size() != 4:
-        raise ValueError(f"k_latent_scales must be a contiguous float32 tensor of at least [{buffer_length}, {nblk}]")
-    if k_buffer.numel() < buffer_length * N or not k_buffer.is_contiguous():
-        raise ValueError(f"k_buffer must be contiguous and hold at least [{buffer_length}, {N}]")
-    if w_k_scale.numel() < -(-N // 128) * -(-K // 128) or w_k_scale.element_size() != 4:
-        raise ValueError("w_k_scale must hold float32 [N/128, K/128]")
-    st = lib().mla_decompress_k_paged_fp8_cache(_u32(buffer_row_offsets, "buffer_row_offsets"),
-                                                _u32(cache_offsets, "cache_offsets"), int(buffer_length),
-                                                w_k_e4m3.data_ptr(), w_k_scale.data_ptr(), N, K, ctypes.byref(desc),
-                                                ctypes.byref(sdesc), int(layer_idx), k_latent_buffer.data_ptr(),
-                                                k_latent_scales.data_ptr(), k_buffer.data_ptr(), _stream(stream))
+    import torch
+    desc, sdesc = _cache_desc(cache, scales=True)
+    N, K, w = _weight(w_k_e4m3, "w_k_e4m3", _dtypes()[MLA_DTYPE_F8E4M3FN])
+    sw = _fp8_scale(w_k_scale, "w_k_scale", N, K, 128, 128)
+    lat, lsc = _fp8_cache_buffers(desc, buffer_length, k_latent_buffer, k_latent_scales)
+    out = _buf(k_buffer, "k_buffer", buffer_length * N * 2, (torch.bfloat16,))
+    bro, co = _index_args(buffer_row_offsets, cache_offsets, desc)
+    _gpu(buffer_row_offsets=buffer_row_offsets, cache_offsets=cache_offsets, w_k_e4m3=w_k_e4m3,
+         w_k_scale=w_k_scale, k_latent_buffer=k_latent_buffer, k_latent_scales=k_latent_scales,
+         k_buffer=k_buffer, **_cache_tensors(cache))
+    st = lib().mla_decompress_k_paged_fp8_cache(bro, co, int(buffer_length), w, sw, N, K, ctypes.byref(desc),
+                                                ctypes.byref(sdesc), int(layer_idx), lat, lsc, out,
+                                                _stream(stream))
     _check(st, "mla_decompress_k_paged_fp8_cache")
 
 
@@ -404,53 +494,56 @@ def mla_decompress_kv_paged_fp8_cache(buffer_row_offsets, cache_offsets, buffer_
                                       k_latent_scales, k_buffer, v_buffer, stream=None) -> None:
     """mla_decompress_k_paged_fp8_cache for K and, from the same gathered codes and
     scales, v_buffer = block-scaled rows @ w_v.T, in one gather and one product launch."""
-    N, K = _weight_shape(w_k_e4m3, "w_k_e4m3")
-    Nv, Kv = _weight_shape(w_v_e4m3, "w_v_e4m3")
+    import torch
+    desc, sdesc = _cache_desc(cache, scales=True)
+    f8 = _dtypes()[MLA_DTYPE_F8E4M3FN]
+    N, K, wk = _weight(w_k_e4m3, "w_k_e4m3", f8)
+    Nv, Kv, wv = _weight(w_v_e4m3, "w_v_e4m3", f8)
     if Kv != K:
         raise ValueError("w_k_e4m3 and w_v_e4m3 must have the same K")
-    desc = cache.descriptor()
-    sdesc = cache.scales_descriptor()
-    D = desc.num_heads * desc.head_dim
-    nblk = -(-D // 128)
-    if k_latent_buffer.numel() * k_latent_buffer.element_size() < buffer_length * D or \
-            not k_latent_buffer.is_contiguous() or k_latent_buffer.element_size() != 1:
-        raise ValueError(f"k_latent_buffer must be a contiguous 1-byte tensor of at least [{buffer_length}, {D}]")
-    if k_latent_scales.numel() < buffer_length * nblk or not k_latent_scales.is_contiguous() or \
-            k_latent_scales.element_size() != 4:
-        raise ValueError(f"k_latent_scales must be a contiguous float32 tensor of at least [{buffer_length}, {nblk}]")
-    for name, buf, n in (("k_buffer", k_buffer, N), ("v_buffer", v_buffer, Nv)):
-        if buf.numel() < buffer_length * n or not buf.is_contiguous():
-            raise ValueError(f"{name} must be contiguous and hold at least [{buffer_length}, {n}]")
-    for name, sc, n in (("w_k_scale", w_k_scale, N), ("w_v_scale", w_v_scale, Nv)):
-        if sc.numel() < -(-n // 128) * -(-K // 128) or sc.element_size() != 4:
-            raise ValueError(f"{name} must hold float32 [{n}/128, K/128]")
-    st = lib().mla_decompress_kv_paged_fp8_cache(_u32(buffer_row_offsets, "buffer_row_offsets"),
-                                                 _u32(cache_offsets, "cache_offsets"), int(buffer_length),
-                                                 w_k_e4m3.data_ptr(), w_k_scale.data_ptr(), N,
-                                                 w_v_e4m3.data_ptr(), w_v_scale.data_ptr(), Nv, K,
+    sk = _fp8_scale(w_k_scale, "w_k_scale", N, K, 128, 128)
+    sv = _fp8_scale(w_v_scale, "w_v_scale", Nv, K, 128, 128)
+    lat, lsc = _fp8_cache_buffers(desc, buffer_length, k_latent_buffer, k_latent_scales)
+    kout = _buf(k_buffer, "k_buffer", buffer_length * N * 2, (torch.bfloat16,))
+    vout = _buf(v_buffer, "v_buffer", buffer_length * Nv * 2, (torch.bfloat16,))
+    bro, co = _index_args(buffer_row_offsets, cache_offsets, desc)
+    _gpu(buffer_row_offsets=buffer_row_offsets, cache_offsets=cache_offsets, w_k_e4m3=w_k_e4m3,
+         w_k_scale=w_k_scale, w_v_e4m3=w_v_e4m3, w_v_scale=w_v_scale, k_latent_buffer=k_latent_buffer,
+         k_latent_scales=k_latent_scales, k_buffer=k_buffer, v_buffer=v_buffer, **_cache_tensors(cache))
+    st = lib().mla_decompress_kv_paged_fp8_cache(bro, co, int(buffer_length), wk, sk, N, wv, sv, Nv, K,
                                                  ctypes.byref(desc), ctypes.byref(sdesc), int(layer_idx),
-                                                 k_latent_buffer.data_ptr(), k_latent_scales.data_ptr(),
-                                                 k_buffer.data_ptr(), v_buffer.data_ptr(), _stream(stream))
+                                                 lat, lsc, kout, vout, _stream(stream))
     _check(st, "mla_decompress_kv_paged_fp8_cache")
+
+
+def _absorb_shapes(q, w, name, d_nope, copy_rope, q_latent):
+    import torch
+    if q is None or q.dim() != 3:
+        raise ValueError("q must be a [T, H, d_nope + d_rope] tensor")
+    if w is None or w.dim() != 3:
+        raise ValueError(f"{name} must be a [H, kv_latent_dim, d_nope] tensor")
+    T, H, Dq = q.shape
+    if w.shape[0] != H or w.shape[2] != d_nope:
+        raise ValueError(f"{name} must be [{H}, kv_latent_dim, {d_nope}]")
+    L = w.shape[1]
+    d_rope = Dq - d_nope
+    Do = L + (d_rope if copy_rope else 0)
+    if q_latent is None or tuple(q_latent.shape) != (T, H, Do):
+        raise ValueError(f"q_latent must be a [{T}, {H}, {Do}] tensor")
+    qp = _buf(q, "q", T * H * Dq * 2, (torch.bfloat16,))
+    op = _buf(q_latent, "q_latent", T * H * Do * 2, (torch.bfloat16,))
+    return T, H, L, d_rope, qp, op
 
 
 def mla_absorb_q(q, w_uk, q_latent, d_nope: int = 128, copy_rope: bool = True, stream=None) -> None:
     """q_latent[t, h, :L] = q[t, h, :d_nope] @ w_uk[h].T per head (L = kv_latent_dim),
     then, with copy_rope, the rope columns q[t, h, d_nope:] after it."""
-    if q.dim() != 3 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous [T, H, d_nope + d_rope] tensor")
-    if w_uk.dim() != 3 or not w_uk.is_contiguous():
-        raise ValueError("w_uk must be a contiguous [H, kv_latent_dim, d_nope] tensor")
-    T, H, Dq = q.shape
-    if w_uk.shape[0] != H or w_uk.shape[2] != d_nope:
-        raise ValueError(f"w_uk must be [{H}, kv_latent_dim, {d_nope}]")
-    L = w_uk.shape[1]
-    d_rope = Dq - d_nope
-    Do = L + (d_rope if copy_rope else 0)
-    if tuple(q_latent.shape) != (T, H, Do) or not q_latent.is_contiguous():
-        raise ValueError(f"q_latent must be a contiguous [{T}, {H}, {Do}] tensor")
-    st = lib().mla_absorb_q(q.data_ptr(), T, H, int(d_nope), int(d_rope), w_uk.data_ptr(), int(L),
-                            1 if copy_rope else 0, q_latent.data_ptr(), _stream(stream))
+    import torch
+    T, H, L, d_rope, qp, op = _absorb_shapes(q, w_uk, "w_uk", d_nope, copy_rope, q_latent)
+    wp = _buf(w_uk, "w_uk", H * L * d_nope * 2, (torch.bfloat16,))
+    _gpu(q=q, w_uk=w_uk, q_latent=q_latent)
+    st = lib().mla_absorb_q(qp, T, H, int(d_nope), int(d_rope), wp, int(L), 1 if copy_rope else 0, op,
+                            _stream(stream))
     _check(st, "mla_absorb_q")
 
 
@@ -458,41 +551,45 @@ def mla_absorb_q_fp8(q, w_uk_e4m3, w_uk_scale, q_latent, d_nope: int = 128, copy
                      stream=None) -> None:
     """The fp8 form: each head's non-rope query part quantised per 1x128 block,
     times the e4m3 w_uk with its 128x128 block scales."""
-    if q.dim() != 3 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous [T, H, d_nope + d_rope] tensor")
-    if w_uk_e4m3.dim() != 3 or not w_uk_e4m3.is_contiguous() or w_uk_e4m3.element_size() != 1:
-        raise ValueError("w_uk_e4m3 must be a contiguous 1-byte [H, kv_latent_dim, d_nope] tensor")
-    T, H, Dq = q.shape
-    if w_uk_e4m3.shape[0] != H or w_uk_e4m3.shape[2] != d_nope:
-        raise ValueError(f"w_uk_e4m3 must be [{H}, kv_latent_dim, {d_nope}]")
-    L = w_uk_e4m3.shape[1]
-    if w_uk_scale.numel() < H * (-(-L // 128)) * (-(-d_nope // 128)) or w_uk_scale.element_size() != 4:
-        raise ValueError("w_uk_scale must hold float32 [H, kv_latent_dim / 128, d_nope / 128]")
-    d_rope = Dq - d_nope
-    Do = L + (d_rope if copy_rope else 0)
-    if tuple(q_latent.shape) != (T, H, Do) or not q_latent.is_contiguous():
-        raise ValueError(f"q_latent must be a contiguous [{T}, {H}, {Do}] tensor")
-    st = lib().mla_absorb_q_fp8(q.data_ptr(), T, H, int(d_nope), int(d_rope), w_uk_e4m3.data_ptr(),
-                                w_uk_scale.data_ptr(), int(L), 1, 128, 128, 1 if copy_rope else 0,
-                                q_latent.data_ptr(), _stream(stream))
+    T, H, L, d_rope, qp, op = _absorb_shapes(q, w_uk_e4m3, "w_uk_e4m3", d_nope, copy_rope, q_latent)
+    wp = _buf(w_uk_e4m3, "w_uk_e4m3", H * L * d_nope, _dtypes()[MLA_DTYPE_F8E4M3FN])
+    sp = _f32(w_uk_scale, "w_uk_scale", H * (-(-L // 128)) * (-(-d_nope // 128)))
+    _gpu(q=q, w_uk_e4m3=w_uk_e4m3, w_uk_scale=w_uk_scale, q_latent=q_latent)
+    st = lib().mla_absorb_q_fp8(qp, T, H, int(d_nope), int(d_rope), wp, sp, int(L), 1, 128, 128,
+                                1 if copy_rope else 0, op, _stream(stream))
     _check(st, "mla_absorb_q_fp8")
+
+
+def _latent_write_args(kv_input, input_row_offsets, kv_norm_gamma, freqs_cis, K, desc):
+    import torch
+    if kv_input is None or kv_input.dim() != 2:
+        raise ValueError("kv_input must be a [T, D_c] tensor")
+    T, D = kv_input.shape
+    if D != desc.num_heads * desc.head_dim:
+        raise ValueError("kv_input rows must be as wide as the cache rows")
+    x = _buf(kv_input, "kv_input", T * D * 2, (torch.bfloat16,))
+    g = _f32(kv_norm_gamma, "kv_norm_gamma", int(K))
+    if freqs_cis is not None:
+        if freqs_cis.dim() != 2:
+            raise ValueError("freqs_cis must be a [max_seq_len, qk_rope_head_dim] tensor")
+        fr = _f32(freqs_cis, "freqs_cis", freqs_cis.shape[0] * freqs_cis.shape[1])
+        max_seq = freqs_cis.shape[0]
+    else:
+        fr, max_seq = None, 0
+    iro = _u32(input_row_offsets, "input_row_offsets", desc.batch_size + 1)
+    return T, x, iro, g, fr, max_seq
 
 
 def mla_write_latent_paged(kv_input, input_row_offsets, kv_norm_gamma, epsilon: float, freqs_cis, K: int,
                            cache: PagedKVCache, layer_idx: int, stream=None) -> None:
     """Append new tokens' rows (RMSNorm of the first K columns with kv_norm_gamma,
     the rest rotated by freqs_cis at each token's position) into the cache pages."""
-    if kv_input.dim() != 2 or not kv_input.is_contiguous():
-        raise ValueError("kv_input must be a contiguous [T, D_c] tensor")
-    T = kv_input.shape[0]
-    desc = cache.descriptor()
-    if kv_input.shape[1] != desc.num_heads * desc.head_dim:
-        raise ValueError("kv_input rows must be as wide as the cache rows")
-    max_seq = freqs_cis.shape[0] if freqs_cis is not None else 0
-    st = lib().mla_write_latent_paged(kv_input.data_ptr(), _u32(input_row_offsets, "input_row_offsets"), T,
-                                      kv_norm_gamma.data_ptr(), float(epsilon),
-                                      freqs_cis.data_ptr() if freqs_cis is not None else None, int(max_seq),
-                                      int(K), ctypes.byref(desc), int(layer_idx), _stream(stream))
+    desc = _cache_desc(cache)
+    T, x, iro, g, fr, max_seq = _latent_write_args(kv_input, input_row_offsets, kv_norm_gamma, freqs_cis, K, desc)
+    _gpu(kv_input=kv_input, input_row_offsets=input_row_offsets, kv_norm_gamma=kv_norm_gamma,
+         freqs_cis=freqs_cis, **_cache_tensors(cache))
+    st = lib().mla_write_latent_paged(x, iro, T, g, float(epsilon), fr, int(max_seq), int(K), ctypes.byref(desc),
+                                      int(layer_idx), _stream(stream))
     _check(st, "mla_write_latent_paged")
 
 
@@ -500,37 +597,33 @@ def mla_write_latent_paged_fp8(kv_input, input_row_offsets, kv_norm_gamma, epsil
                                cache: PagedKVCache, layer_idx: int, stream=None) -> None:
     """mla_write_latent_paged into an e4m3 cache: the same fp32 rows, quantised
     per 128 columns (codes into the pool, fp32 scales into the cache's scale pool)."""
-    if kv_input.dim() != 2 or not kv_input.is_contiguous():
-        raise ValueError("kv_input must be a contiguous [T, D_c] tensor")
-    T = kv_input.shape[0]
-    desc = cache.descriptor()
-    sdesc = cache.scales_descriptor()
-    if kv_input.shape[1] != desc.num_heads * desc.head_dim:
-        raise ValueError("kv_input rows must be as wide as the cache rows")
-    max_seq = freqs_cis.shape[0] if freqs_cis is not None else 0
-    st = lib().mla_write_latent_paged_fp8(kv_input.data_ptr(), _u32(input_row_offsets, "input_row_offsets"), T,
-                                          kv_norm_gamma.data_ptr(), float(epsilon),
-                                          freqs_cis.data_ptr() if freqs_cis is not None else None, int(max_seq),
-                                          int(K), ctypes.byref(desc), ctypes.byref(sdesc), int(layer_idx),
-                                          _stream(stream))
+    desc, sdesc = _cache_desc(cache, scales=True)
+    T, x, iro, g, fr, max_seq = _latent_write_args(kv_input, input_row_offsets, kv_norm_gamma, freqs_cis, K, desc)
+    _gpu(kv_input=kv_input, input_row_offsets=input_row_offsets, kv_norm_gamma=kv_norm_gamma,
+         freqs_cis=freqs_cis, **_cache_tensors(cache))
+    st = lib().mla_write_latent_paged_fp8(x, iro, T, g, float(epsilon), fr, int(max_seq), int(K),
+                                          ctypes.byref(desc), ctypes.byref(sdesc), int(layer_idx), _stream(stream))
     _check(st, "mla_write_latent_paged_fp8")
 
 
 def kv_matmul_paged(hidden_state, input_row_offsets, weight, cache: PagedKVCache, layer_idx: int,
                     stream=None) -> None:
     """Append bf16(hidden_state @ weight) as K ([:HD]) and V ([HD:]) rows into the cache pages."""
-    if hidden_state.dim() != 2 or not hidden_state.is_contiguous():
-        raise ValueError("hidden_state must be a contiguous [T, hidden] tensor")
+    import torch
+    if hidden_state is None or hidden_state.dim() != 2:
+        raise ValueError("hidden_state must be a [T, hidden] tensor")
     T, Kd = hidden_state.shape
-    desc = cache.descriptor()
+    desc = _cache_desc(cache)
     hd = desc.num_heads * desc.head_dim
-    if tuple(weight.shape) != (Kd, 2 * hd) or not weight.is_contiguous():
-        raise ValueError(f"weight must be a contiguous [{Kd}, {2 * hd}] tensor")
+    if weight is None or tuple(weight.shape) != (Kd, 2 * hd):
+        raise ValueError(f"weight must be a [{Kd}, {2 * hd}] tensor")
+    h = _buf(hidden_state, "hidden_state", T * Kd * 2, (torch.bfloat16,))
+    w = _buf(weight, "weight", Kd * 2 * hd * 2, (torch.bfloat16,))
     if input_row_offsets.numel() != desc.batch_size + 1:
         raise ValueError("input_row_offsets must have batch_size + 1 entries")
-    st = lib().kv_matmul_paged(hidden_state.data_ptr(), _u32(input_row_offsets, "input_row_offsets"),
-                               T, Kd, weight.data_ptr(), ctypes.byref(desc), int(layer_idx),
-                               _stream(stream))
+    iro = _u32(input_row_offsets, "input_row_offsets", desc.batch_size + 1)
+    _gpu(hidden_state=hidden_state, input_row_offsets=input_row_offsets, weight=weight, **_cache_tensors(cache))
+    st = lib().kv_matmul_paged(h, iro, T, Kd, w, ctypes.byref(desc), int(layer_idx), _stream(stream))
     _check(st, "kv_matmul_paged")
 
 
