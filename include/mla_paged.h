@@ -30,10 +30,16 @@
  *     hipError_t).  A call with no rows to process returns MLA_OK after the host
  *     checks and enqueues nothing.
  *   - Index contents in device memory (offsets, page ids) are the caller's
- *     contract and are not validated on the host.  Kernels clamp every page id,
- *     page index and row to the buffers they were given, so a bad index yields
- *     unspecified values in the rows it affects but never an access outside
- *     the pool, the weight or the outputs.
+ *     contract and are not validated on the host.  Read paths clamp every page
+ *     id, page index and row to the buffers they were given, so a bad index
+ *     yields unspecified values in the output rows it affects but never an
+ *     access outside the pool, the weight or the outputs.  Write paths
+ *     (kv_matmul_paged, mla_write_latent_paged(_fp8)) store nothing for a token
+ *     whose position lies past its request's page table or whose page id lies
+ *     past the pool; every other byte of the pool keeps its value.
+ *   - Shapes whose 256-row tiles would need byte offsets of 2^31 or more (a
+ *     row of 2^22 bf16 elements in an output, a weight or the cache) return
+ *     MLA_ERR_INVALID_SHAPE.
  */
 #ifndef MLA_PAGED_H
 #define MLA_PAGED_H

@@ -97,6 +97,11 @@ mla::PagedLayer layer_view(const mla_paged_cache_t* c, uint32_t layer)
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The product kernels address one 256-row tile of their operands and outputs
+// through 32-bit byte offsets: a row of `width` elements of `eb` bytes times
+// 256 rows must stay below 2^31 bytes.
+bool tile_fits_32bit(int64_t width, int eb) { return width * eb * 256 < (int64_t(1) << 31); }
+
 }  // namespace
 
 MLA_API mla_status_t mla_paged_cache_default_strides(mla_paged_cache_t* c)
@@ -144,7 +149,8 @@ mla_status_t check_decompress(const uint32_t* bro, const uint32_t* co, int32_t M
     const int32_t N2 = v.present ? v.N : 64;
     if (cache->dtype == MLA_DTYPE_BF16) {
         if (K % 64 || N % 64 || N2 % 64 || (int64_t)N * K * 2 >= (int64_t(1) << 31) ||
-            (int64_t)N2 * K * 2 >= (int64_t(1) << 31))
+            (int64_t)N2 * K * 2 >= (int64_t(1) << 31) || !tile_fits_32bit(N, 2) || !tile_fits_32bit(N2, 2) ||
+            !tile_fits_32bit(D, 2))
             return MLA_ERR_INVALID_SHAPE;
     } else if (cache->dtype == MLA_DTYPE_F32) {
         if (K % 4 || N % 4 || N2 % 4)
@@ -289,7 +295,7 @@ MLA_API mla_status_t mla_latent_matmul(const void* k_latent_buffer, int64_t ld_l
         return MLA_ERR_INVALID_SHAPE;
     const int eb = elem_bytes(dtype);
     if (dtype == MLA_DTYPE_BF16) {
-        if (K % 64 || N % 64 || (int64_t)N * K * 2 >= (int64_t(1) << 31))
+        if (K % 64 || N % 64 || (int64_t)N * K * 2 >= (int64_t(1) << 31) || !tile_fits_32bit(N, 2))
             return MLA_ERR_INVALID_SHAPE;
     } else if (dtype == MLA_DTYPE_F32) {
         if (K % 4 || N % 4)
@@ -344,12 +350,13 @@ mla_status_t check_decompress_fp8(const uint32_t* bro, const uint32_t* co, int32
         return MLA_ERR_NULL_POINTER;
     const int32_t N2 = v.present ? v.N : 128;
     if (M < 0 || N <= 0 || K <= 0 || N2 <= 0 || m_gran != 1 || n_gran != 128 || k_gran != 128 || N % 128 ||
-        N2 % 128 || K % 128 || (int64_t)N * K >= (int64_t(1) << 31) || (int64_t)N2 * K >= (int64_t(1) << 31))
+        N2 % 128 || K % 128 || (int64_t)N * K >= (int64_t(1) << 31) || (int64_t)N2 * K >= (int64_t(1) << 31) ||
+        !tile_fits_32bit(N, 2) || !tile_fits_32bit(N2, 2) || (int64_t)M * (K / 128) * 4 >= (int64_t(1) << 31))
         return MLA_ERR_INVALID_SHAPE;
     if (mla_status_t st = check_cache_shape(cache, 1))
         return st;
     D = (int64_t)cache->num_heads * cache->head_dim;
-    if (K > D)
+    if (K > D || !tile_fits_32bit(D, 2))
         return MLA_ERR_INVALID_SHAPE;
     if (cache->dtype != MLA_DTYPE_BF16)
         return MLA_ERR_INVALID_DTYPE;
@@ -452,8 +459,8 @@ mla_status_t decompress_fp8_cache(const uint32_t* buffer_row_offsets, const uint
                  (v.present && (!v.w || !v.scale || !v.out))))
         return MLA_ERR_NULL_POINTER;
     if (M < 0 || N <= 0 || K <= 0 || N % 128 || K % 128 || (int64_t)N * K >= (int64_t(1) << 31) ||
-        cache_scales->granularity != 128 ||
-        (v.present && (v.N <= 0 || v.N % 128 || (int64_t)v.N * K >= (int64_t(1) << 31))))
+        !tile_fits_32bit(N, 2) || cache_scales->granularity != 128 ||
+        (v.present && (v.N <= 0 || v.N % 128 || (int64_t)v.N * K >= (int64_t(1) << 31) || !tile_fits_32bit(v.N, 2))))
         return MLA_ERR_INVALID_SHAPE;
     if (mla_status_t st = check_cache_shape(cache, 1))
         return st;
@@ -719,7 +726,7 @@ MLA_API mla_status_t kv_matmul_paged(const void* hidden_state, const uint32_t* i
     if (mla_status_t st = check_cache_shape(cache, 2))
         return st;
     const int64_t HD = (int64_t)cache->num_heads * cache->head_dim;
-    if (HD % 64 || (int64_t)hidden_dim * 2 * HD * 2 >= (int64_t(1) << 31))
+    if (HD % 64 || (int64_t)hidden_dim * 2 * HD * 2 >= (int64_t(1) << 31) || !tile_fits_32bit(hidden_dim, 2))
         return MLA_ERR_INVALID_SHAPE;
     if (cache->dtype != MLA_DTYPE_BF16)
         return MLA_ERR_INVALID_DTYPE;

@@ -77,6 +77,8 @@ struct TileList {
             tm = u / tiles_n;
             tn = u - tm * tiles_n;
         }
+        tm = __builtin_amdgcn_readfirstlane(tm);
+        tn = __builtin_amdgcn_readfirstlane(tn);
     }
 };
 
@@ -124,6 +126,15 @@ __device__ inline TileList make_tiles(const PT& P)
         total = P.tiles_m * P.tiles_n;
     }
     L.count = L.first < total ? (total - L.first + L.step - 1) / L.step : 0;
+    // Every field is wave-uniform; say so, so that the tile walk stays in
+    // scalar registers and its branches stay scalar branches.
+    L.first = __builtin_amdgcn_readfirstlane(L.first);
+    L.step = __builtin_amdgcn_readfirstlane(L.step);
+    L.count = __builtin_amdgcn_readfirstlane(L.count);
+    L.Gn = __builtin_amdgcn_readfirstlane(L.Gn);
+    L.x = __builtin_amdgcn_readfirstlane(L.x);
+    L.G2 = __builtin_amdgcn_readfirstlane(L.G2);
+    L.pass1 = __builtin_amdgcn_readfirstlane(L.pass1);
     return L;
 }
 

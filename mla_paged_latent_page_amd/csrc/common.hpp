@@ -57,6 +57,21 @@ __device__ inline int64_t token_offset(const PagedLayer& L, uint32_t b, uint32_t
     return (int64_t)pg * L.stride_page + (int64_t)slot * L.stride_token;
 }
 
+// Byte offset of the slot a write path stores token position p of request b
+// into, or -1 when the position lies past the request's page table or its page
+// id past the pool: the store is then skipped (clamping, as the read paths do,
+// would overwrite another token's cached row).
+__device__ inline int64_t store_offset(const PagedLayer& L, uint32_t b, uint32_t p)
+{
+    const uint32_t lp = p / L.page_size;
+    if (lp >= L.max_pages)
+        return -1;
+    const uint32_t pg = L.page_table[(size_t)b * L.max_pages + lp];
+    if (pg >= L.num_pages)
+        return -1;
+    return (int64_t)pg * L.stride_page + (int64_t)(p - lp * L.page_size) * L.stride_token;
+}
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 

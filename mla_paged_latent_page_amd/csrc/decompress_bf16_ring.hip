@@ -3,10 +3,9 @@
 // "mla_prefill_decode_graph_fp8", Args w_k), used when K is a multiple of 128.
 //
 //  * Same 256 x 256 tiles, epilogue, buffer resources and XCD-aware tile order
-//    as the register-staged kernel in decompress_bf16.hip.  Two wave layouts:
-//    4 waves of 128 x 128 (256 accumulators, one wave per SIMD) or 8 waves of
-//    128 x 64 (128 accumulators, two waves per SIMD, so one wave's LDS and
-//    memory stalls are covered by the other's MFMAs).
+//    as the register-staged kernel in decompress_bf16.hip; 8 waves of 128 x 64
+//    (128 accumulators, two waves per SIMD, so one wave's LDS and memory
+//    stalls are covered by the other's MFMAs).
 //  * K advances in 64-wide stages through two LDS slots of 64 KB (256 rows of
 //    128 bytes for each operand).  Operand tiles go from memory straight into
 //    LDS (buffer loads with an LDS destination, 16 bytes per lane, no VGPR
@@ -318,19 +317,10 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_bf16_ring(Gemm
 
 }  // namespace
 
-// MLA_PAGED_RING_WAVES=4|8 picks the wave layout (for tuning); the default is
-// the faster one measured on MI355X.
 hipError_t launch_product_bf16_ring(const DecompressArgs& a, int cus, hipStream_t s)
 {
-    static const int waves = [] {
-        const char* e = getenv("MLA_PAGED_RING_WAVES");
-        return e ? atoi(e) : 8;
-    }();
     GemmParams P = make_gemm_params(a, BM, BN, cus);
-    if (waves == 4)
-        hipLaunchKernelGGL((gemm_bf16_ring<2, 2>), dim3(gemm_grid(P, cus)), dim3(256), 0, s, P);
-    else
-        hipLaunchKernelGGL((gemm_bf16_ring<2, 4>), dim3(gemm_grid(P, cus)), dim3(512), 0, s, P);
+    hipLaunchKernelGGL((gemm_bf16_ring<2, 4>), dim3(gemm_grid(P, cus)), dim3(512), 0, s, P);
     return hipGetLastError();
 }
 

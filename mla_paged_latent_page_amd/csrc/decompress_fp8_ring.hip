@@ -24,7 +24,9 @@
 //    s_a per 32-row block) and a wave's 64 columns lie in one 128-wide weight
 //    block (s_w is uniform).  A zero s_w makes its stage add nothing: the MFMAs
 //    then run with E8M0 operand scales 2^-127 each, so every product underflows
-//    to zero, and the accumulators keep their scale.
+//    to zero, and the accumulators keep their scale.  A zero activation scale
+//    (an fp8 cache may hold one) does the same for its row alone, through that
+//    lane's own E8M0 scale.
 //  * Epilogue as in the bf16 ring kernel (bf16 pairs into a per-wave LDS strip,
 //    read back as 16-byte row pieces, non-temporal stores), 32 rows at a time;
 //    the strips live in the ring slot the tile's last stage consumed.
@@ -311,12 +313,20 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
         const bool skip = sw_c == 0.0f;
         const int e8 = skip ? 0 : 127;
         float rho[FM], ref_next[FM];
+        int e8a[FM];   // E8M0 scale of this lane's activation row in this stage
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
             const float sig = sa_c[j] * sw_c;
+            // A zero (or subnormal) activation scale: the row's block adds
+            // nothing.  Its codes go in with E8M0 scale 2^-127, so each of its
+            // products is below 2^-109 (exactly zero when nothing was added
+            // before: the accumulators stay in units of ref = 0), and the
+            // accumulators keep their scale, as for a zero weight scale.
+            const bool dead = skip || __builtin_fabsf(sig) < 1.17549435e-38f;
             const float r = ref[j] * __builtin_amdgcn_rcpf(sig);
-            rho[j] = skip ? 1.0f : (ref[j] == 0.0f ? 0.0f : r);
-            ref_next[j] = skip ? ref[j] : sig;
+            rho[j] = dead ? 1.0f : (ref[j] == 0.0f ? 0.0f : r);
+            ref_next[j] = dead ? ref[j] : sig;
+            e8a[j] = dead ? 0 : 127;
         }
 #pragma unroll
         for (int i = 0; i < FN; ++i)
@@ -326,14 +336,14 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
                 for (int e = 0; e < 16; ++e)
                     acc[i][j][e] *= rho[j];
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[0][i], fa[0][j], acc[i][j], 0, 0, 0, e8,
-                                                                            0, e8);
+                                                                            0, e8a[j]);
             }
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
             for (int j = 0; j < FM; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[1][i], fa[1][j], acc[i][j], 0, 0, 0, e8,
-                                                                            0, e8);
+                                                                            0, e8a[j]);
         // Order: the scales and the first k step's fragments first, then per
         // block its 16 rescale multiplies (run under the previous block's
         // MFMA), its first MFMA and a share of the second k step's fragment

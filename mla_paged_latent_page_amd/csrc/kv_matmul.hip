@@ -90,7 +90,7 @@ kv_matmul_kernel(KvParams P)
         if (t < a.T) {
             const uint32_t b = find_request(a.iro, a.L.batch, (uint32_t)t);
             const uint32_t p = a.cache_len[b] + ((uint32_t)t - a.iro[b]);
-            off = token_offset(a.L, b, p);
+            off = store_offset(a.L, b, p);
         }
         rowoff[r] = off;
     }
@@ -240,19 +240,13 @@ hipError_t launch_cfg(const KvMatmulArgs& a, hipStream_t s)
 
 }  // namespace
 
+// The LDS-ring kernel when the shapes fit its tiling (hidden_dim % 128 == 0,
+// HD % 256 == 0); the general tiled kernel above otherwise.
 hipError_t launch_kv_matmul(const KvMatmulArgs& a, hipStream_t s)
 {
-    static const int cfg = [] {
-        const char* e = getenv("MLA_PAGED_KV_TILE");
-        return e ? atoi(e) : 0;
-    }();
-    if (cfg == 0 && a.Kd % 128 == 0 && a.HD % 256 == 0)
+    if (a.Kd % 128 == 0 && a.HD % 256 == 0)
         return launch_kv_matmul_ring(a, num_cus(), s);
-    switch (cfg) {
-    case 1: return launch_cfg<256, 256, 2, 2>(a, s);
-    case 2: return launch_cfg<128, 256, 2, 2>(a, s);
-    default: return launch_cfg<256, 256, 2, 4>(a, s);
-    }
+    return launch_cfg<256, 256, 2, 4>(a, s);
 }
 
 }  // namespace mla

@@ -192,7 +192,7 @@ __global__ void __launch_bounds__(NT, 1) kv_matmul_ring(KvRingParams P)
             if (t < a.T) {
                 const uint32_t b = find_request(a.iro, a.L.batch, (uint32_t)t);
                 const uint32_t p = a.cache_len[b] + ((uint32_t)t - a.iro[b]);
-                off = token_offset(a.L, b, p);
+                off = store_offset(a.L, b, p);
             }
             rowoff[r] = off;
         }
@@ -320,13 +320,7 @@ hipError_t launch_kv_matmul_ring(const KvMatmulArgs& a, int cus, hipStream_t s)
     P.tiles_n = a.N / BN;
     // Hidden rows are 8 KB and T is large: keep each activation tile in one
     // XCD's L2 and re-read the (small) weight from the last-level cache.
-    static const int order = [] {
-        const char* e = getenv("MLA_PAGED_KV_ORDER");
-        return e ? atoi(e) : 2;
-    }();
-    P.xcd_map = (cus % 8 == 0 && P.tiles_m >= 8) ? order : 0;
-    if (P.xcd_map == 1 && P.tiles_n % 8 != 0)
-        P.xcd_map = 0;
+    P.xcd_map = (cus % 8 == 0 && P.tiles_m >= 8) ? 2 : 0;
     const int tiles = P.tiles_m * P.tiles_n;
     const int grid = P.xcd_map ? cus : (tiles < cus ? tiles : cus);
     hipLaunchKernelGGL(kv_matmul_ring, dim3(grid), dim3(NT), 0, s, P);

@@ -125,8 +125,8 @@ __global__ void __launch_bounds__(64 * WRITE_WAVES) latent_write_kernel(LatentWr
         const uint32_t b = cnt[k] == 0 ? 0u : min(cnt[k], a.L.batch) - 1;
         const uint32_t p = a.cache_len[b] + (t - a.iro[b]);
         const uint32_t pf = p < (uint32_t)a.max_seq ? p : (uint32_t)a.max_seq - 1;   // freqs row, clamped
-        off[k] = token_offset(a.L, b, p);
-        soff[k] = FP8 ? token_offset(a.Ls, b, p) : 0;
+        off[k] = store_offset(a.L, b, p);   // -1: no slot for this position, nothing is stored
+        soff[k] = FP8 ? store_offset(a.Ls, b, p) : 0;
         const float* f = a.freqs + (int64_t)pf * a.R + lane * 8;
         fr0[k] = rot ? *reinterpret_cast<const f32x4*>(f) : f32x4{0.f, 0.f, 0.f, 0.f};
         fr1[k] = rot ? *reinterpret_cast<const f32x4*>(f + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -142,6 +142,8 @@ __global__ void __launch_bounds__(64 * WRITE_WAVES) latent_write_kernel(LatentWr
     for (int k = 0; k < TW; ++k) {
         if (t0 + k >= a.T)
             break;
+        if (off[k] < 0)
+            continue;
         char* dst = const_cast<char*>(a.L.base) + off[k];
 
         // Latent part: RMS over the K latent values, scaled by gamma.

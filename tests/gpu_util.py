@@ -100,7 +100,11 @@ def workspace_views(ws, M, K):
     return q, s
 
 
-def rows_as_f64(t, rows):
+def rows_as_f64(t, rows, M):
+    """The sampled rows as binary64, after a scan on the GPU that every one of
+    the first M rows was written (no poison left, nothing non-finite): a tile
+    order that skipped or misplaced a tile shows even where no row was sampled."""
+    assert bool(torch.isfinite(t[:M]).all()), "an output row was not written (poison or non-finite values)"
     idx = torch.as_tensor(np.asarray(rows, np.int64), device=t.device)
     return t.index_select(0, idx).double().cpu().numpy()
 

@@ -446,3 +446,21 @@ def test_fp8_cache_kv_error_paths(lib):
     assert fp8_cache_kv(lib, d, s, layer=2) == RANGE
     assert fp8_cache_kv(lib, d, s, M=0) == OK
     assert fp8_cache_kv(lib, d, s) == DEV
+
+
+def test_tile_offsets_that_overflow_32_bits_are_refused(lib):
+    """The product kernels address a 256-row tile with 32-bit byte offsets, so a
+    row of 2^22 bf16 elements (256 rows = 2^31 bytes) is refused before any
+    launch, even where the weight itself (N x K) stays under 2^31 bytes."""
+    big = 1 << 22
+    d = cache_desc()
+    assert decompress(lib, d, N=big, K=64) == SHAPE
+    assert decompress(lib, d, N=big - 64, K=64) == DEV          # the largest accepted width
+    assert fp8(lib, d, N=big, K=128) == SHAPE
+    assert fp8(lib, d, N=big - 128, K=128) == DEV
+    assert lib.mla_latent_matmul(FAKE, 576, 100, FAKE, big, 64, 1, FAKE, None) == SHAPE
+    dk = cache_desc(num_kv=2, heads=1, head_dim=64, with_lengths=True)
+    assert kv(lib, dk, Kd=big) == SHAPE
+    assert kv(lib, dk, Kd=big - 64) == DEV
+    wide = cache_desc(head_dim=big, page_size=1, pages=2, maxp=2)   # a cache row of 2^22 bf16
+    assert decompress(lib, wide, N=512, K=512) == SHAPE

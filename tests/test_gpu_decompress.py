@@ -102,7 +102,7 @@ def _check_sampled(case, tol=BF16_TOL):
     rows = sample_rows(case)
     say(f"[gpu] {case.name}: comparing {len(rows)} sampled rows")
     ref = oracle.matmul_nt(ref_lat, case.cache.dtype, case.weight, case.weight_dtype, case.K, rows)
-    got = rows_as_f64(res["out"], rows)
+    got = rows_as_f64(res["out"], rows, M)
     check_close(got, ref, tol, f"{case.name} k_buffer (sampled)")
     tail = res["out"][M:].view(torch.int16)
     assert bool((tail == POISON_OUT).all())

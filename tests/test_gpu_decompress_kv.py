@@ -28,7 +28,7 @@ def _check(case, case_v, rows=None, single=True):
     assert np.array_equal(to_bits(res["lat"])[:M], lat), "gathered rows differ"
     tol = FP8_TOL if case.weight_dtype == "e4m3" else BF16_TOL
     for name, out, ref in (("k_buffer", res["k"], ref_k), ("v_buffer", res["v"], ref_v)):
-        got = out[:M].double().cpu().numpy() if rows is None else rows_as_f64(out, rows)
+        got = out[:M].double().cpu().numpy() if rows is None else rows_as_f64(out, rows, M)
         check_close(got, ref, tol, f"{case.name} fused {name}")
         assert _poisoned(out, M), f"{name}: rows past M were written"
     assert _poisoned(res["lat"], M)

@@ -37,7 +37,7 @@ def _check(case, rows=None):
     assert np.array_equal(s_got.view(np.uint32), s_ref.view(np.uint32)), "activation scales differ"
     assert _same_codes(q_got, q_ref), "activation codes differ"
     ref = oracle.fp8_matmul_nt(q_ref, s_ref, case.weight_q, case.weight_scale, 128, 128, rows)
-    got = res["out"][:M].double().cpu().numpy() if rows is None else rows_as_f64(res["out"], rows)
+    got = res["out"][:M].double().cpu().numpy() if rows is None else rows_as_f64(res["out"], rows, M)
     check_close(got, ref, FP8_TOL, f"{case.name} k_buffer fp8")
     assert np.all(to_bits(res["out"])[M:] == POISON_OUT)
     return res, ref_lat

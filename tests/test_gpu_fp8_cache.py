@@ -37,7 +37,7 @@ def _check(case, rows=None, extra=5):
     sc = res["scales"].cpu().numpy()
     assert np.array_equal(sc[:M].view(np.uint32), scales.view(np.uint32)), "gathered scales differ"
     assert np.all(np.isnan(sc[M:]))
-    got = res["out"][:M].double().cpu().numpy() if rows is None else rows_as_f64(res["out"], rows)
+    got = res["out"][:M].double().cpu().numpy() if rows is None else rows_as_f64(res["out"], rows, M)
     check_close(got, ref, BF16_TOL, f"{case.name} k_buffer (fp8 cache)")
     assert np.all(to_bits(res["out"])[M:] == POISON_OUT)
     return res
@@ -144,5 +144,29 @@ def test_k_and_v_from_the_fp8_cache_at_full_size_sampled():
     codes, scales, k, v = oracle.decompress_kv_fp8_cache(case, case_v, rows)
     M = case.M
     assert np.array_equal(to_bits(lat)[:M], codes), "gathered codes differ"
-    check_close(rows_as_f64(kout, rows), k, BF16_TOL, "c6 k_buffer (fused, sampled rows)")
-    check_close(rows_as_f64(vout, rows), v, BF16_TOL, "c6 v_buffer (fused, sampled rows)")
+    check_close(rows_as_f64(kout, rows, M), k, BF16_TOL, "c6 k_buffer (fused, sampled rows)")
+    check_close(rows_as_f64(vout, rows, M), v, BF16_TOL, "c6 v_buffer (fused, sampled rows)")
+
+
+def test_zero_activation_scales():
+    """Scale blocks of 0 in the cache (a writer may store s = 0 for an all-zero
+    block): a zero block after a non-zero one, a zero first block, and a row
+    whose every block is zero.  The oracle's value for such a block is exactly
+    0 * (its code sum); the product must stay finite and within the bound, and
+    the all-zero row must come out as zeros."""
+    case = _fp8_case(31, batch=4, max_len=300, page_size=16, K=512, rope=64, N=512)
+    c = case.cache
+    rng = np.random.default_rng(31)
+    sc = c.scales.copy()
+    layer = sc[:, case.layer_idx]
+    kb = case.K // 128
+    kill = rng.random(layer[..., :kb].shape) < 0.3
+    layer[..., :kb][kill] = 0.0
+    # the first row of request 0 loses every block
+    b0_pos = int(case.cache_offsets[0])
+    pg = int(c.page_table[0, b0_pos // c.page_size])
+    layer[pg, 0, b0_pos % c.page_size, :kb] = 0.0
+    case = dataclasses.replace(case, cache=dataclasses.replace(c, scales=sc))
+    res = _check(case)
+    out0 = res["out"][0].float().cpu().numpy()
+    assert np.all(out0 == 0.0), "a row whose every scale block is zero must give zeros"

@@ -92,3 +92,36 @@ def test_written_rows_decompress_back():
 def test_c5_full_size():
     case = W.c5_latent_write()
     _check(case)
+
+
+def test_tokens_without_a_slot_are_not_written():
+    """The last request's page-table entries name pages past the pool, and the
+    second-to-last request's last tokens lie past its page table: those tokens
+    are skipped, the others are written as the oracle says, and no other byte
+    of the pool changes."""
+    import dataclasses
+    case = W.latent_write_case("lw_noslot", seed=9, seq_lens=[20, 35, 9], start_lengths=[3, 0, 5], page_size=16)
+    c = case.cache
+    pt = c.page_table.copy()
+    pt[2, :] = c.num_pages + 7
+    bad = dataclasses.replace(case, cache=dataclasses.replace(c, page_table=pt))
+    # request 1: shrink its table so its tokens from position 16 on have no page
+    keep = 16
+    before, after = run_write(dataclasses.replace(bad, cache=dataclasses.replace(
+        bad.cache, page_table=np.where(np.arange(pt.shape[1])[None, :] >= keep // 16,
+                                       np.where(np.arange(pt.shape[0])[:, None] == 1, np.uint32(0xFFFFFFFF), pt),
+                                       pt).astype(np.uint32))))
+    # valid tokens: all of request 0, the first 16 positions of request 1
+    iro = case.input_row_offsets.astype(np.int64)
+    valid = np.concatenate([np.arange(iro[0], iro[1]), np.arange(iro[1], iro[1] + keep)])
+    ref, dst = oracle.latent_write(case)
+    ref, dst = ref[valid], dst[valid]
+    D = ref.shape[1]
+    flat = after.reshape(-1)
+    idx = torch.as_tensor(dst, device=after.device)[:, None] + torch.arange(D, device=after.device)[None, :]
+    got_rows = flat[idx.reshape(-1)].reshape(len(valid), D)
+    expect = before.clone().reshape(-1)
+    expect[idx.reshape(-1)] = got_rows.reshape(-1)
+    assert torch.equal(expect.view(torch.int16), flat.view(torch.int16)), "bytes outside the valid rows changed"
+    got = got_rows.double().cpu().numpy()
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 2.0 ** -24)
