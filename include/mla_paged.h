@@ -266,6 +266,35 @@ mla_status_t mla_decompress_kv_paged(const uint32_t* buffer_row_offsets,
                                      void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * mla_decompress_k_paged_fp8 without the workspace argument.  The activation
+ * codes and scales go to a fixed array of MLA_FP8_NOALLOC_SCRATCH_BYTES in
+ * device memory that the library holds on each GPU it runs on until the
+ * process ends; nothing is allocated per call.
+ *
+ *   Same arguments, arithmetic and results as mla_decompress_k_paged_fp8 (the
+ *   same kernels run).  Calls whose workspace would exceed the array
+ *   (mla_decompress_k_paged_fp8_workspace_size(M, K, k_gran) >
+ *   MLA_FP8_NOALLOC_SCRATCH_BYTES: more than 65536 rows at K = 512) return
+ *   MLA_ERR_WORKSPACE before anything is enqueued.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (other streams, other host threads) race on it and must be ordered by
+ *   the caller.  Nothing in the array has to start at zero: each call writes
+ *   every code and scale it reads.
+ *   The first call on a device looks up the array's address there
+ *   (MLA_ERR_HIP if that fails).
+ */
+#define MLA_FP8_NOALLOC_SCRATCH_BYTES (33u << 20)   /* the workspace of 65536 rows at K = 512 */
+mla_status_t mla_decompress_k_paged_fp8_noalloc(const uint32_t* buffer_row_offsets,
+                                                const uint32_t* cache_offsets, int32_t buffer_length,
+                                                const void* weight_e4m3, const float* weight_scale,
+                                                int32_t N, int32_t K, int32_t m_gran, int32_t n_gran,
+                                                int32_t k_gran, const mla_paged_cache_t* cache,
+                                                uint32_t layer_idx, void* k_latent_buffer, void* k_buffer,
+                                                void* stream);
+
+/*
  * The fp8 block-scaled form of mla_decompress_kv_paged (page
  * "mla_prefill_decode_graph_fp8": Args w_k, w_k_scale, w_uv, w_uv_scale; the
  * quantisation of the gathered rows as in mla_decompress_k_paged_fp8, done once

@@ -8,6 +8,7 @@ There is no fallback: if the library has not been built, every call raises.
 Entry points (same names as the C ABI):
   mla_decompress_k_paged       gather latent rows from a paged cache, up-project them
   mla_decompress_k_paged_fp8   the fp8 block-scaled form (1x128 activation, 128x128 weight scales)
+  mla_decompress_k_paged_fp8_noalloc  the same without a workspace (for callers that cannot allocate)
   mla_decompress_kv_paged(_fp8)  one gather, K and V up-projections
   mla_decompress_k_paged_fp8_cache  the fp8 form on an e4m3 cache with per-128-column scales
   mla_write_latent_paged       RMSNorm + rope rotation of new tokens' rows into the cache pages
@@ -37,7 +38,9 @@ EXPORTS = ("mla_paged_cache_default_strides", "mla_decompress_k_paged", "mla_gat
            "kv_matmul_paged", "mla_check_indices", "mla_status_string", "mla_last_hip_error",
            "mla_abi_version", "mla_decompress_kv_paged", "mla_decompress_kv_paged_fp8",
            "mla_write_latent_paged", "mla_decompress_k_paged_fp8_cache", "mla_absorb_q", "mla_absorb_q_fp8",
-           "mla_write_latent_paged_fp8", "mla_decompress_kv_paged_fp8_cache")
+           "mla_write_latent_paged_fp8", "mla_decompress_kv_paged_fp8_cache", "mla_decompress_k_paged_fp8_noalloc")
+# mla_decompress_k_paged_fp8_noalloc's fixed device array (include/mla_paged.h)
+MLA_FP8_NOALLOC_SCRATCH_BYTES = 33 << 20
 
 
 class MlaError(RuntimeError):
@@ -93,6 +96,9 @@ def lib():
             L.mla_decompress_k_paged_fp8.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                                      ctypes.POINTER(CacheDesc), u32, vp, vp, vp, sz, vp]
             L.mla_decompress_k_paged_fp8.restype = i32
+            L.mla_decompress_k_paged_fp8_noalloc.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                                             ctypes.POINTER(CacheDesc), u32, vp, vp, vp]
+            L.mla_decompress_k_paged_fp8_noalloc.restype = i32
             L.mla_decompress_kv_paged.argtypes = [vp, vp, i32, vp, i32, vp, i32, i32, ctypes.POINTER(CacheDesc),
                                                   u32, vp, vp, vp, vp]
             L.mla_decompress_kv_paged.restype = i32
@@ -410,6 +416,27 @@ def mla_decompress_k_paged_fp8(buffer_row_offsets, cache_offsets, buffer_length:
                                           ctypes.byref(desc), int(layer_idx), lat, out, ws, ws_bytes,
                                           _stream(stream))
     _check(st, "mla_decompress_k_paged_fp8")
+
+
+def mla_decompress_k_paged_fp8_noalloc(buffer_row_offsets, cache_offsets, buffer_length: int, weight_e4m3,
+                                       weight_scale, cache: PagedKVCache, layer_idx: int, k_latent_buffer,
+                                       k_buffer, m_gran: int = 1, n_gran: int = 128, k_gran: int = 128,
+                                       stream=None) -> None:
+    """mla_decompress_k_paged_fp8 without a workspace: the library's fixed device
+    array (MLA_FP8_NOALLOC_SCRATCH_BYTES per GPU) holds the activation codes and
+    scales.  Calls that overlap on one GPU race on that array."""
+    import torch
+    desc = _cache_desc(cache)
+    N, K, w = _weight(weight_e4m3, "weight_e4m3", _dtypes()[MLA_DTYPE_F8E4M3FN])
+    sw = _fp8_scale(weight_scale, "weight_scale", N, K, n_gran, k_gran)
+    lat, out = _check_outputs(buffer_length, desc, N, k_latent_buffer, k_buffer, (torch.bfloat16,))
+    bro, co = _index_args(buffer_row_offsets, cache_offsets, desc)
+    _gpu(buffer_row_offsets=buffer_row_offsets, cache_offsets=cache_offsets, weight_e4m3=weight_e4m3,
+         weight_scale=weight_scale, k_latent_buffer=k_latent_buffer, k_buffer=k_buffer, **_cache_tensors(cache))
+    st = lib().mla_decompress_k_paged_fp8_noalloc(bro, co, int(buffer_length), w, sw, N, K, m_gran, n_gran,
+                                                  k_gran, ctypes.byref(desc), int(layer_idx), lat, out,
+                                                  _stream(stream))
+    _check(st, "mla_decompress_k_paged_fp8_noalloc")
 
 
 def mla_decompress_kv_paged(buffer_row_offsets, cache_offsets, buffer_length: int, w_k, w_v,

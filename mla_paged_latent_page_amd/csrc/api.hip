@@ -3,6 +3,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "mla_paged.h"
@@ -404,6 +405,86 @@ MLA_API mla_status_t mla_decompress_k_paged_fp8(const uint32_t* buffer_row_offse
                                             cache, layer_idx, k_latent_buffer, k_buffer, D, none);
     set_fp8_workspace(a, weight_scale, workspace);
     const hipError_t e = mla::launch_decompress_fp8(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MLA_OK : hip_failed(e);
+}
+
+// ---------------------------------------------------------------------------
+// The fp8 call without a workspace argument, for callers that cannot allocate.
+// Its activation codes and scales go to a fixed array in device memory
+// (`scratch`, MLA_FP8_NOALLOC_SCRATCH_BYTES per GPU, held from the library's
+// load until the process ends).  Host code never passes the array's name to a
+// kernel: the name is a host-side stand-in, not a device address.  The device
+// address is looked up once per device, with that device current, and kept.
+// ---------------------------------------------------------------------------
+namespace {
+
+__device__ __align__(256) unsigned char scratch[MLA_FP8_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch` (null on failure; `e` tells why).
+void* scratch_on_current_device(hipError_t& e)
+{
+    e = hipSuccess;
+    int dev = -1;
+    if ((e = hipGetDevice(&dev)) != hipSuccess)
+        return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        e = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    if (void* p = g_scratch[dev].load(std::memory_order_acquire))
+        return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (void* p = g_scratch[dev].load(std::memory_order_relaxed))
+        return p;
+    void* ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess || !ptr) {
+        if (e == hipSuccess)
+            e = hipErrorInvalidSymbol;
+        return nullptr;
+    }
+    g_scratch[dev].store(ptr, std::memory_order_release);
+    return ptr;
+}
+
+}  // namespace
+
+MLA_API mla_status_t mla_decompress_k_paged_fp8_noalloc(const uint32_t* buffer_row_offsets,
+                                                        const uint32_t* cache_offsets, int32_t buffer_length,
+                                                        const void* weight_e4m3, const float* weight_scale,
+                                                        int32_t N, int32_t K, int32_t m_gran, int32_t n_gran,
+                                                        int32_t k_gran, const mla_paged_cache_t* cache,
+                                                        uint32_t layer_idx, void* k_latent_buffer, void* k_buffer,
+                                                        void* stream)
+{
+    int64_t D = 0;
+    const Second none;
+    // The scratch array stands in for the workspace: the usual checks run with
+    // a placeholder that passes the pointer and alignment tests, and a size
+    // beyond the array is refused first.
+    const size_t need = mla_decompress_k_paged_fp8_workspace_size(buffer_length > 0 ? buffer_length : 0, K, k_gran);
+    if (buffer_length > 0 && need > (size_t)MLA_FP8_NOALLOC_SCRATCH_BYTES)
+        return MLA_ERR_WORKSPACE;
+    void* const placeholder = reinterpret_cast<void*>(uintptr_t(256));
+    if (mla_status_t st = check_decompress_fp8(buffer_row_offsets, cache_offsets, buffer_length, weight_e4m3,
+                                               weight_scale, N, K, m_gran, n_gran, k_gran, cache, layer_idx,
+                                               k_latent_buffer, k_buffer, placeholder, need, none, D))
+        return st;
+    if (buffer_length == 0)
+        return MLA_OK;
+    if (mla_status_t st = check_device())
+        return st;
+    hipError_t e;
+    void* ws = scratch_on_current_device(e);
+    if (!ws)
+        return hip_failed(e);
+    mla::DecompressArgs a = decompress_args(buffer_row_offsets, cache_offsets, buffer_length, weight_e4m3, N, K,
+                                            cache, layer_idx, k_latent_buffer, k_buffer, D, none);
+    set_fp8_workspace(a, weight_scale, ws);
+    e = mla::launch_decompress_fp8(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MLA_OK : hip_failed(e);
 }
 

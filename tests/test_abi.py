@@ -464,3 +464,24 @@ def test_tile_offsets_that_overflow_32_bits_are_refused(lib):
     assert kv(lib, dk, Kd=big - 64) == DEV
     wide = cache_desc(head_dim=big, page_size=1, pages=2, maxp=2)   # a cache row of 2^22 bf16
     assert decompress(lib, wide, N=512, K=512) == SHAPE
+
+
+def test_noalloc_fp8_error_paths(lib):
+    """The fp8 call without a workspace: the usual checks, and a call whose
+    workspace would exceed the library's fixed array is refused."""
+    d = cache_desc()
+
+    def call(M=100, N=512, K=512, grans=(1, 128, 128), **ptrs):
+        p = dict(bro=FAKE, co=FAKE, w=FAKE, sw=FAKE, lat=FAKE, out=FAKE)
+        p.update(ptrs)
+        return lib.mla_decompress_k_paged_fp8_noalloc(p["bro"], p["co"], M, p["w"], p["sw"], N, K, *grans,
+                                                      ctypes.byref(d), 1, p["lat"], p["out"], None)
+    limit = mp.MLA_FP8_NOALLOC_SCRATCH_BYTES
+    assert lib.mla_decompress_k_paged_fp8_workspace_size(65536, 512, 128) == limit
+    assert call(M=65536) == DEV                 # exactly fills the array
+    assert call(M=65537) == WS                  # one row more does not fit
+    for k in ("bro", "co", "w", "sw", "lat", "out"):
+        assert call(**{k: None}) == NULLP
+    assert call(grans=(1, 128, 64)) == SHAPE
+    assert call(M=0, bro=None, co=None, w=None, sw=None, lat=None, out=None) == OK
+    assert call() == DEV
