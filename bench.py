@@ -653,17 +653,31 @@ def write_traffic_record(row_name, fetch_csv, write_csv, commands, alg_bytes):
     print(json.dumps({"record": os.path.relpath(path, ROOT), **{k: rec[k] for k in rec if k.endswith("launch")}}))
 
 
+def _durations_ns(path, kernel):
+    """Duration of each dispatch of the kernel in a counter CSV (its start and
+    end timestamps, ns)."""
+    d = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if kernel in r["Kernel_Name"]:
+                d[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return list(d.values())
+
+
 def write_counter_record(row_name, csvs, commands):
     kernel = _kernel_of(row_name)
     vals = {}
+    durs = []
     for p in csvs:
         for c, v in _dispatches(p, kernel).items():
             vals[c] = float(np.mean(v))
+        durs += _durations_ns(p, kernel)
     rec = {"kernel": kernel, "workload": row_name, "source_hash": source_hash(kernel),
            "counters_mean_per_dispatch": {c: v for c, v in sorted(vals.items())}, "commands": commands,
            "setup": "MI355X, ROCm 7.2; cd /tmp && export TMPDIR=/tmp, then the commands from the repository root"}
-    # GRBM_GUI_ACTIVE counts GPU-busy cycles on each of the 8 XCDs; the MFMA
-    # busy count is summed over every SIMD (4 per CU).
+    # GRBM_GUI_ACTIVE counts GPU-busy cycles on each of the 8 XCDs (summed);
+    # the MFMA busy count is summed over every SIMD (4 per CU), the TA busy
+    # count over the 256 TA instances (one per CU).
     gui = vals.get("GRBM_GUI_ACTIVE")
     if gui:
         cycles = gui / 8
@@ -675,11 +689,17 @@ def write_counter_record(row_name, csvs, commands):
             rec["ta_busy_frac"] = round(vals["TA_TA_BUSY_sum"] / 256 / cycles, 4)
         if "SQ_BUSY_CU_CYCLES" in vals:
             rec["cu_busy_frac"] = round(vals["SQ_BUSY_CU_CYCLES"] / 256 / cycles, 4)
+        if durs:
+            rec["dispatch_ns_mean"] = round(float(np.mean(durs)))
+            # the busy-cycle count over the dispatch time: meaningful for long
+            # dispatches only (counter set-up cycles swamp a few microseconds)
+            if np.mean(durs) > 1e5:
+                rec["clock_ghz"] = round(cycles / float(np.mean(durs)), 3)
     path = os.path.join(ROOT, "profiles", f"{kernel}_{row_name}_counters.json")
     with open(path, "w") as fo:
         json.dump(rec, fo, indent=1)
     print(json.dumps({"record": os.path.relpath(path, ROOT),
-                      **{k: rec[k] for k in ("mfma_busy_frac", "ta_busy_frac", "cycles_per_xcd") if k in rec}}))
+                      **{k: rec[k] for k in ("mfma_busy_frac", "ta_busy_frac", "clock_ghz", "cycles_per_xcd") if k in rec}}))
 
 
 def main():
@@ -731,12 +751,21 @@ def main():
     torch.cuda.set_device(0)
     print(f"[bench] device {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
     if args.profile:
+        # the same warm-up as a timed row (at least W calls and 0.2 s of GPU
+        # work, so the clock has ramped up), then exactly K calls
         row = build_row(args.profile, torch, mp, W)
         n = max(1, row.copies)
-        for i in range(args.warmup + args.steps):
+        w0, i = time.perf_counter(), 0
+        while i < args.warmup or time.perf_counter() - w0 < Timed.warm_seconds:
             row.fn(i % n)
+            i += 1
+            if i % 8 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
-        print(f"[bench] profiled {args.profile}: {args.warmup} + {args.steps} calls of {row.kernel}",
+        for j in range(args.steps):
+            row.fn((i + j) % n)
+        torch.cuda.synchronize()
+        print(f"[bench] profiled {args.profile}: {i} warm-up + {args.steps} calls of {row.kernel}",
               file=sys.stderr, flush=True)
         return
 
@@ -816,29 +845,29 @@ def main():
 
 
 def _alg_bytes_host(row_name, W):
-    """Algorithmic HBM bytes of one launch of a row's dominant kernel, from the
-    workload's shapes alone (no GPU)."""
-    if row_name in ("c1_product",):
-        c = W.c1_decode()
-        return c.M * (c.K * 2 + c.N * 2) + c.N * c.K * 2
-    if row_name in ("c1_gather",):
+    """Algorithmic HBM bytes of one launch of a row's dominant kernel alone,
+    from the workload's shapes (no GPU): for the products, the activation
+    columns they read (K of each row), their outputs and the weight once."""
+    def bf16_product(c, n):
+        return c.M * (c.K * 2 + n * 2) + n * c.K * 2
+
+    def fp8_product(c, n):
+        return c.M * (c.K + (c.K // 128) * 4 + n * 2) + n * c.K + (n // 128) * (c.K // 128) * 4
+    if row_name == "c1_product":
+        return bf16_product(W.c1_decode(), 16384)
+    if row_name == "c1_gather":
         c = W.c1_decode()
         return c.M * c.D_c * 2 * 2
-    if row_name in ("c1_decode", "c2_prefill", "c3_fp8"):
-        c = {"c1_decode": W.c1_decode, "c2_prefill": W.c2_prefill, "c3_fp8": W.c3_fp8}[row_name]()
-        return decompress_costs(c)[1]
-    if row_name == "c2_tp8_share":
-        c = W.c2_prefill()
-        c = dataclasses.replace(c, N=2048, weight=np.ascontiguousarray(c.weight[:2048]))
-        return decompress_costs(c)[1]
+    if row_name == "c2_prefill":
+        return bf16_product(W.c2_prefill(), 16384)
     if row_name == "c2_fused_kv":
-        c = W.c2_prefill()
-        return c.M * (2 * c.D_c * 2 + 2 * c.N * 2) + 2 * c.N * c.K * 2
+        return bf16_product(W.c2_prefill(), 2 * 16384)
+    if row_name == "c2_tp8_share":
+        return bf16_product(W.c2_prefill(), 2048)
+    if row_name == "c3_fp8":
+        return fp8_product(W.c3_fp8(), 16384)
     if row_name in ("c6_fp8_cache", "c6_fused_kv_fp8_cache"):
-        c = W.c6_fp8_cache()
-        nblk = c.cache.scale_blocks
-        n = c.N if row_name == "c6_fp8_cache" else 2 * c.N
-        return c.M * (2 * (c.D_c + nblk * 4) + n * 2) + n * c.K + (n // 128) * (c.K // 128) * 4
+        return fp8_product(W.c6_fp8_cache(), 16384 if row_name == "c6_fp8_cache" else 2 * 16384)
     if row_name == "c4_kv_matmul":
         k = W.c4_kv_matmul()
         return k.T * (k.hidden_dim * 2 + k.N * 2) + k.weight.nbytes
