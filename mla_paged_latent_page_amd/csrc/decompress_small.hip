@@ -10,16 +10,17 @@
 // one per CU).  The block's 64 x 512 weight tile (64 KB) and the rows' first
 // 512 columns go into LDS in K order, in chunks of 64 columns (128-byte row
 // pieces; weight chunk q is 8 KB):
-//  * at kernel start waves 5..7 put weight chunk 0 in flight while
-//    wave 4 resolves the rows' cache addresses (one lane per request reads its
-//    offsets, then one lane per row its page-table entry) into a table in LDS;
-//  * then waves 4..7 each issue, chunk after chunk, their share of row chunk c
-//    and of weight chunk c + 1, so rows and weight arrive together in K order.
-//    A CU serves the vector loads of its waves in issue order: rows queued
-//    behind the whole weight tile would start the product only after the
-//    weight had streamed in, and a tile queued behind slow index loads would
-//    leave HBM idle.  Row chunks that do not fit in LDS at once go through a
-//    ring of slots refilled as chunks are consumed;
+//  * at kernel start the compute waves 0..3 put the whole weight tile in
+//    flight, chunk after chunk, while wave 4 resolves the rows' cache
+//    addresses (one lane per request reads its offsets, then one lane per row
+//    its page-table entry; a small page table is copied into LDS in the same
+//    round of loads as the offsets) into a table in LDS.  The weight is the
+//    one HBM stream of the call: it starts at once and is not held up by the
+//    index loads' round trip;
+//  * then waves 4..7 each issue, chunk after chunk, their share of the row
+//    chunks (the rows are read by every block, so mostly from L2).  Row
+//    chunks that do not fit in LDS at once go through a ring of slots
+//    refilled as chunks are consumed;
 //  * waves 0..3 run v_mfma_f32_32x32x16_bf16 on chunk q as soon as its pieces
 //    have landed, with the weight as the row operand: up to 160 rows, wave w
 //    owns weight rows 32 (w % 2) .. +32 and the 32-row blocks w/2, w/2 + 2, ...
@@ -29,8 +30,9 @@
 //    cache rows r with r % grid == block) in flight into registers early and
 //    stores it at the end.
 // The accumulators go through LDS so that every k_buffer store writes whole
-// 128-byte row segments.  Loader waves order their loads against the compute
-// waves' LDS reads with explicit vmcnt waits and one barrier per chunk; the
+// 128-byte row segments.  Every wave that issued loads of chunk q (the
+// compute waves its weight pieces, the loader waves its row pieces) waits for
+// them with an explicit vmcnt wait before the chunk's barrier; the
 // loads into LDS are issued from inline assembly, so the compiler adds no
 // waits of its own for them.
 #include "launch.hpp"
@@ -44,14 +46,13 @@ constexpr int W_BYTES = SBN * SK * 2;            // 64 KB weight tile
 constexpr int CHUNK_K = 64, CHUNKS = SK / CHUNK_K, CROWB = CHUNK_K * 2;
 constexpr int W_CHUNK_BYTES = SBN * CROWB;       // 8 KB: one chunk of the weight tile
 constexpr int A_AREA = 96 * 1024;                // row chunks (first the row table, last the output staging)
-constexpr int W_LOADS = W_BYTES / 1024;          // 64 loads of 1 KB
-constexpr int W_WAVES = 3;
-// Weight chunks put in flight before the rows are: each CU serves its vector
-// loads in issue order, so the row wave's index and row loads wait behind
-// every weight load issued before them.
-constexpr int W_EARLY_CHUNKS = 1;
+constexpr int W_PIECES = W_CHUNK_BYTES / 1024;   // 1 KB loads per weight chunk
+constexpr int COMPUTE_WAVES = 4, LOADER_WAVES = 4;
+constexpr int W_PER_WAVE = W_PIECES / COMPUTE_WAVES;   // weight loads per chunk per wave (either role)
 constexpr int EARLY_COPY_ROWS = 2;               // k_latent_buffer rows per block copied through registers
 constexpr int EARLY_COPY_GRANULES = 128;         // up to 2048-byte cache rows
+constexpr int PT_STAGE_MAX = 16384;              // page tables up to 64 KB are copied into LDS whole
+constexpr int ROW_TABLE = A_AREA - SMAX_M * 16;  // row table: rowaddr, row_req, row_pos (4 KB)
 
 // vmcnt is a 6-bit counter: a wave never has more than 63 vector memory
 // operations outstanding (issue waits instead), so a wait for at most 63
@@ -80,29 +81,49 @@ struct SmallCfg {
     static constexpr int INITIAL = RING ? SLOTS - 1 : CHUNKS;    // chunks issued before the loop
     static_assert(SLOTS >= 2 && ROWS % 32 == 0, "chunk ring");
     static_assert(W_BYTES + A_AREA <= 163840 && ROWS * CROWB <= A_AREA, "LDS budget");
-    static_assert(SMAX_M * 16 <= W_CHUNK_BYTES, "row table fits in one weight chunk");
-    static_assert(W_EARLY_CHUNKS < CHUNKS, "the row table's chunk is loaded after the table is read");
 };
 
-// Loader wave (each issues, per chunk c, MB row loads and then, from chunk
-// W_EARLY_CHUNKS on, two weight loads of chunk c + W_EARLY_CHUNKS): chunk q's
-// row loads and weight loads must have landed.  The weight loads of chunk q
-// went out before its row loads, so the loads still allowed in flight are the
-// ones issued after chunk q's row loads.
-template <int MB>
+// Weight chunks put in flight at kernel start; the later ones go out one per
+// row chunk, after it.  Gathering, the rows' addresses are known only after
+// the index round trip: enough weight to keep HBM busy over it goes first
+// (more for many rows, whose product takes longer to catch up).  Reading
+// k_latent_buffer, the rows can go out at once, in K order with the weight.
+template <int MB, bool GATHER>
+constexpr int w_early()
+{
+    return GATHER ? (MB <= 3 ? 3 : 5) : 1;
+}
+static_assert(PT_STAGE_MAX * 4 <= ROW_TABLE, "the staged page table and the row table do not overlap");
+static_assert(W_PIECES % COMPUTE_WAVES == 0 && COMPUTE_WAVES == LOADER_WAVES, "weight loads split evenly");
+
+// Loader wave (each issues, per chunk c, MB row loads and then its share of
+// weight chunk c + E): chunk q's row loads and (q >= E) weight loads must
+// have landed.  The weight loads of chunk q went out before its
+// row loads, so the loads still allowed in flight are the ones issued after
+// chunk q's row loads.
+template <int MB, int E>
 constexpr int loads_after(int q)
 {
     using C = SmallCfg<MB>;
     const int issued = C::RING ? (C::INITIAL + q < CHUNKS ? C::INITIAL + q : CHUNKS) : CHUNKS;
-    int n = q + W_EARLY_CHUNKS < CHUNKS ? 2 : 0;
+    int n = q + E < CHUNKS ? W_PER_WAVE : 0;
     for (int c = q + 1; c < issued; ++c)
-        n += MB + (c + W_EARLY_CHUNKS < CHUNKS ? 2 : 0);
+        n += MB + (c + E < CHUNKS ? W_PER_WAVE : 0);
     return n;
 }
-template <int MB, int Q>
+template <int MB, int E, int Q>
 __device__ inline void wait_loads()
 {
-    vm_wait<loads_after<MB>(Q)>();
+    vm_wait<loads_after<MB, E>(Q)>();
+}
+
+// Compute wave (issued W_PER_WAVE weight loads per chunk of the first E
+// chunks, in K order, at kernel start): its share of weight chunk q has
+// landed (chunks from E on are the loader waves').
+template <int E, int Q>
+__device__ inline void wait_weight()
+{
+    vm_wait<(Q < E ? W_PER_WAVE * (E - 1 - Q) : 0)>();
 }
 
 // Waves 0..3: the product, chunk by chunk as the pieces land, then the
@@ -110,7 +131,7 @@ __device__ inline void wait_loads()
 // starting at block nb0 and the 32-row blocks MB0, MB0 + MSTEP, ... of the M
 // rows; every weight fragment it reads serves all its M blocks and every row
 // fragment all its weight blocks.
-template <int MB, int MB0, int MSTEP, int NBW>
+template <int MB, int E, int MB0, int MSTEP, int NBW>
 __device__ inline void compute_waves(const char* wt, char* at, int nb0, int lane)
 {
     using C = SmallCfg<MB>;
@@ -133,6 +154,16 @@ __device__ inline void compute_waves(const char* wt, char* at, int nb0, int lane
                 acc[s][j][i] = f32x16{};
 #pragma unroll
     for (int q = 0; q < CHUNKS; ++q) {
+        switch (q) {
+        case 0: wait_weight<E, 0>(); break;
+        case 1: wait_weight<E, 1>(); break;
+        case 2: wait_weight<E, 2>(); break;
+        case 3: wait_weight<E, 3>(); break;
+        case 4: wait_weight<E, 4>(); break;
+        case 5: wait_weight<E, 5>(); break;
+        case 6: wait_weight<E, 6>(); break;
+        default: wait_weight<E, 7>(); break;
+        }
         lds_barrier();
         const char* ws = wt + q * W_CHUNK_BYTES + (nb0 * 32 + frow) * CROWB;
         const char* as = at + (q % SLOTS) * C::CHUNK_BYTES + frow * CROWB;
@@ -179,10 +210,12 @@ __device__ inline void compute_waves(const char* wt, char* at, int nb0, int lane
         }
 }
 
-template <int MB>
-__global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a, int gather)
+template <int MB, bool GATHER>
+__global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a)
 {
     using C = SmallCfg<MB>;
+    constexpr bool gather = GATHER;
+    constexpr int E = w_early<MB, GATHER>();
     constexpr int SLOTS = C::SLOTS;
     __shared__ __attribute__((aligned(1024))) char wt[W_BYTES];
     __shared__ __attribute__((aligned(1024))) char at[A_AREA];
@@ -197,9 +230,9 @@ __global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a
     const bool early_copy = gather && gpr <= EARLY_COPY_GRANULES;
     const int lrow = lane >> 3, lpos = lane & 7;
     // The row table (first columns of row r at rowaddr[r]; rows M .. ROWS-1
-    // repeat row M-1, loaded and never stored) lives where weight chunk 7
-    // lands, until every loader wave has read its rows' addresses.
-    char* tbl = wt + (CHUNKS - 1) * W_CHUNK_BYTES;
+    // repeat row M-1, loaded and never stored) lives at the end of the row
+    // chunks' area until every loader wave has read its rows' addresses.
+    char* tbl = at + ROW_TABLE;
     uint64_t* rowaddr = reinterpret_cast<uint64_t*>(tbl);
 
     // Weight load (c, p): chunk c, tile rows 8 p .. 8 p + 7, one 128-byte row
@@ -212,36 +245,69 @@ __global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a
         asm_ld16_lds(wr, wt_lds + c * W_CHUNK_BYTES + p * 1024, voff, (uint32_t)(n0 * SK * 2 + c * CROWB));
     };
 
-    // 1. The first weight chunks (waves 5..7) while wave 4 builds the row table.
-    if (wave >= 5) {
-        for (int j = wave - 5; j < 8 * W_EARLY_CHUNKS; j += W_WAVES)
-            issue_w(j >> 3, j & 7);
-    } else if (wave == 4) {
+    // 1. Wave 4 resolves the rows' cache addresses into a table in LDS: one
+    //    lane per request reads its offsets and writes each of its rows'
+    //    request and token position into LDS; then one lane per row looks up
+    //    the page-table entry of its row.  A page table of at most
+    //    PT_STAGE_MAX entries is copied whole into LDS (the row chunks' area,
+    //    unused until the table is built) in the same round of loads as the
+    //    offsets, so the lookups are LDS reads: one round of memory latency
+    //    instead of two.  Rows no request covers (buffer_row_offsets ending
+    //    short of M) read the pool's first row.  The compute waves put the
+    //    whole weight tile in flight, chunk after chunk (wave v: pieces
+    //    W_PER_WAVE v .. of every chunk), only once the first round of index
+    //    loads has been issued: a CU serves its waves' vector loads in issue
+    //    order, and the index loads must not wait behind 64 KB of weight.
+    uint32_t* row_req = reinterpret_cast<uint32_t*>(tbl + SMAX_M * 8);
+    uint32_t* row_pos = row_req + SMAX_M;
+    const uint32_t pt_entries = a.L.batch * a.L.max_pages;
+    const bool pt_staged = pt_entries <= (uint32_t)PT_STAGE_MAX;
+    // Lane b of a round reads buffer_row_offsets[b] and cache_offsets[b]; a
+    // request's end is its neighbour lane's start (the last lane's comes from
+    // one more, wave-uniform, load).  Every load of a round is issued before
+    // any of them is used (indices clamped into the arrays instead of
+    // branching around the loads; batch >= 1), so each round costs one memory
+    // latency.
+    uint32_t lo = 0, c0 = 0, last = 0;
+    auto load_round = [&](uint32_t b0) __attribute__((always_inline)) {
+        const uint32_t b = b0 + lane;
+        const uint32_t bc = b < a.L.batch ? b : a.L.batch - 1;
+        const uint32_t bend = b0 + 64 < a.L.batch ? b0 + 64 : a.L.batch;
+        lo = a.bro[bc];
+        c0 = a.co[bc];
+        last = a.bro[bend];
+    };
+    // The barrier (with no wait before it) only orders the issue of the
+    // loads; each side has its own copy so that the compiler's wait pass sees
+    // the index loads pending on wave 4's path alone.
+    if (wave != 4) {
+        asm volatile("s_barrier" ::: "memory");
+        if (wave < COMPUTE_WAVES) {
+#pragma unroll
+            for (int c = 0; c < E; ++c)
+#pragma unroll
+                for (int j = 0; j < W_PER_WAVE; ++j)
+                    issue_w(c, W_PER_WAVE * wave + j);
+        }
+    } else {
         if (gather) {
-            // Two rounds of loads whatever the rows per request: one lane per
-            // request reads its offsets and writes each of its rows' request and
-            // token position into LDS; then one lane per row reads the page-table
-            // entry of its row.  Rows no request covers (buffer_row_offsets
-            // ending short of M) read the pool's first row.
-            uint32_t* row_req = reinterpret_cast<uint32_t*>(tbl + SMAX_M * 8);
-            uint32_t* row_pos = row_req + SMAX_M;
+            if (pt_staged) {
+                const i32x4 ptr = make_srd(a.L.page_table, pt_entries * 4);
+                for (uint32_t c = 0; c < (pt_entries * 4 + 1023) / 1024; ++c)
+                    asm_ld16_lds(ptr, at_lds + c * 1024, (uint32_t)lane * 16, c * 1024);
+            }
+            load_round(0);
+        }
+        asm volatile("s_barrier" ::: "memory");
+        if (gather) {
             for (int r = lane; r < C::ROWS; r += 64)
                 row_req[r] = ~0u;
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            // Every load of a round is issued before any of them is used
-            // (indices clamped into the arrays instead of branching around
-            // the loads), so each round costs one memory latency.
-            for (uint32_t b0 = 0; b0 < a.L.batch; b0 += 64) {
-                // Lane b reads buffer_row_offsets[b] and cache_offsets[b]; a
-                // request's end is its neighbour lane's start (the last lane's
-                // comes from one more, wave-uniform, load).
-                const uint32_t b = b0 + lane;
-                const uint32_t bc = b < a.L.batch ? b : a.L.batch - 1;
-                const uint32_t bend = b0 + 64 < a.L.batch ? b0 + 64 : a.L.batch;
-                uint32_t lo = a.bro[bc], c0 = a.co[bc], last = a.bro[bend];
+            for (uint32_t b0 = 0;;) {
                 // One use of all three here keeps the compiler from sinking a
                 // load into the branch that needs it (a second round trip).
                 asm volatile("" : "+v"(lo), "+v"(c0), "+v"(last));
+                const uint32_t b = b0 + lane;
                 const uint32_t next = (uint32_t)__shfl_down((int)lo, 1);
                 const uint32_t hi0 = lane == 63 || b + 1 >= a.L.batch ? last : next;
                 const uint32_t hi = b >= a.L.batch ? lo : hi0 < (uint32_t)M ? hi0 : (uint32_t)M;
@@ -249,10 +315,17 @@ __global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a
                     row_req[r] = b;
                     row_pos[r] = c0 + (r - lo);
                 }
+                b0 += 64;
+                if (b0 >= a.L.batch)
+                    break;
+                load_round(b0);
             }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            // The page table's copy (loads older than the offsets' ones, so
+            // landed once those have) and the row entries are in LDS.
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
             constexpr int RPL = (C::ROWS + 63) / 64;
             const PagedLayer& L = a.L;
+            const uint32_t* pt_lds = reinterpret_cast<const uint32_t*>(at);
             uint32_t pgv[RPL], slot[RPL];
             bool valid[RPL];
 #pragma unroll
@@ -264,7 +337,8 @@ __global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a
                 uint32_t lp = pos / L.page_size;
                 slot[k] = pos - lp * L.page_size;
                 lp = lp < L.max_pages ? lp : L.max_pages - 1;
-                pgv[k] = L.page_table[(size_t)bb * L.max_pages + lp];
+                const size_t e = (size_t)bb * L.max_pages + lp;
+                pgv[k] = pt_staged ? pt_lds[e] : L.page_table[e];
             }
 #pragma unroll
             for (int k = 0; k < RPL; ++k) {
@@ -290,8 +364,7 @@ __global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a
 
     // 2. Loader waves 4..7 (w = wave - 4) take the row loads i = w, w + 4, ...
     //    of every chunk (lane l: row 8 i + l / 8, granule position l % 8 with
-    //    logical granule (l % 8) ^ ((row / 2) % 8)) and the weight loads
-    //    p = 2 w, 2 w + 1 of every chunk from W_EARLY_CHUNKS on.
+    //    logical granule (l % 8) ^ ((row / 2) % 8)).
     const int w = wave - 4;
     const char* src_row[MB];
     u32x4 cp[EARLY_COPY_ROWS][2];
@@ -314,20 +387,20 @@ __global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a
             }
         }
     }
-    lds_barrier();              // row table read: weight chunk 7 may land on it
+    lds_barrier();              // row table read: row chunks may land on it
 
     if (wave >= 4) {
         // Chunk c: this wave's row loads, then its share of weight chunk
-        // c + W_EARLY_CHUNKS, so rows and weight arrive in K order.
+        // c + W_EARLY, so rows and the rest of the weight arrive in K order.
         auto issue_chunk = [&](int c) __attribute__((always_inline)) {
             const int slot = c % SLOTS;
 #pragma unroll
             for (int k = 0; k < MB; ++k)
                 asm_gld16_lds(src_row[k] + c * CROWB, at_lds + slot * C::CHUNK_BYTES + (w + 4 * k) * 1024);
-            if (c + W_EARLY_CHUNKS < CHUNKS) {
-                issue_w(c + W_EARLY_CHUNKS, 2 * w);
-                issue_w(c + W_EARLY_CHUNKS, 2 * w + 1);
-            }
+            if (c + E < CHUNKS)
+#pragma unroll
+                for (int j = 0; j < W_PER_WAVE; ++j)
+                    issue_w(c + E, W_PER_WAVE * w + j);
         };
 #pragma unroll
         for (int c = 0; c < C::INITIAL; ++c)
@@ -335,14 +408,14 @@ __global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a
 #pragma unroll
         for (int q = 0; q < CHUNKS; ++q) {
             switch (q) {
-            case 0: wait_loads<MB, 0>(); break;
-            case 1: wait_loads<MB, 1>(); break;
-            case 2: wait_loads<MB, 2>(); break;
-            case 3: wait_loads<MB, 3>(); break;
-            case 4: wait_loads<MB, 4>(); break;
-            case 5: wait_loads<MB, 5>(); break;
-            case 6: wait_loads<MB, 6>(); break;
-            default: wait_loads<MB, 7>(); break;
+            case 0: wait_loads<MB, E, 0>(); break;
+            case 1: wait_loads<MB, E, 1>(); break;
+            case 2: wait_loads<MB, E, 2>(); break;
+            case 3: wait_loads<MB, E, 3>(); break;
+            case 4: wait_loads<MB, E, 4>(); break;
+            case 5: wait_loads<MB, E, 5>(); break;
+            case 6: wait_loads<MB, E, 6>(); break;
+            default: wait_loads<MB, E, 7>(); break;
             }
             lds_barrier();
             // Every wave is done with chunk q-1: refill its slot.
@@ -385,16 +458,16 @@ __global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a
         // 3. The product.  Many rows: wave v owns both weight blocks and M
         //    blocks v, v + 4 (one LDS fragment read per MFMA).
         switch (wave) {
-        case 0: compute_waves<MB, 0, 4, 2>(wt, at, 0, lane); break;
-        case 1: compute_waves<MB, 1, 4, 2>(wt, at, 0, lane); break;
-        case 2: compute_waves<MB, 2, 4, 2>(wt, at, 0, lane); break;
-        default: compute_waves<MB, 3, 4, 2>(wt, at, 0, lane); break;
+        case 0: compute_waves<MB, E, 0, 4, 2>(wt, at, 0, lane); break;
+        case 1: compute_waves<MB, E, 1, 4, 2>(wt, at, 0, lane); break;
+        case 2: compute_waves<MB, E, 2, 4, 2>(wt, at, 0, lane); break;
+        default: compute_waves<MB, E, 3, 4, 2>(wt, at, 0, lane); break;
         }
     } else if (wave < 2) {
         // Few rows: wave v owns weight block v % 2 and M blocks v / 2, v / 2 + 2, ...
-        compute_waves<MB, 0, 2, 1>(wt, at, wave & 1, lane);
+        compute_waves<MB, E, 0, 2, 1>(wt, at, wave & 1, lane);
     } else {
-        compute_waves<MB, 1, 2, 1>(wt, at, wave & 1, lane);
+        compute_waves<MB, E, 1, 2, 1>(wt, at, wave & 1, lane);
     }
     lds_barrier();              // outputs staged
 
@@ -411,6 +484,22 @@ __global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a
     }
 }
 
+template <bool GATHER>
+void launch_small(const DecompressArgs& a, hipStream_t s)
+{
+    const dim3 grid(a.N / SBN), block(SNT);
+    switch ((a.M + 31) / 32) {
+    case 1: hipLaunchKernelGGL((decompress_small_bf16<1, GATHER>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decompress_small_bf16<2, GATHER>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((decompress_small_bf16<3, GATHER>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decompress_small_bf16<4, GATHER>), grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL((decompress_small_bf16<5, GATHER>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((decompress_small_bf16<6, GATHER>), grid, block, 0, s, a); break;
+    case 7: hipLaunchKernelGGL((decompress_small_bf16<7, GATHER>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((decompress_small_bf16<8, GATHER>), grid, block, 0, s, a); break;
+    }
+}
+
 }  // namespace
 
 bool small_bf16_fits(const DecompressArgs& a)
@@ -422,17 +511,10 @@ bool small_bf16_fits(const DecompressArgs& a)
 // k_latent_buffer; gather == 0: rows are read from k_latent_buffer.
 hipError_t launch_small_bf16(const DecompressArgs& a, int gather, hipStream_t s)
 {
-    const dim3 grid(a.N / SBN), block(SNT);
-    switch ((a.M + 31) / 32) {
-    case 1: hipLaunchKernelGGL(decompress_small_bf16<1>, grid, block, 0, s, a, gather); break;
-    case 2: hipLaunchKernelGGL(decompress_small_bf16<2>, grid, block, 0, s, a, gather); break;
-    case 3: hipLaunchKernelGGL(decompress_small_bf16<3>, grid, block, 0, s, a, gather); break;
-    case 4: hipLaunchKernelGGL(decompress_small_bf16<4>, grid, block, 0, s, a, gather); break;
-    case 5: hipLaunchKernelGGL(decompress_small_bf16<5>, grid, block, 0, s, a, gather); break;
-    case 6: hipLaunchKernelGGL(decompress_small_bf16<6>, grid, block, 0, s, a, gather); break;
-    case 7: hipLaunchKernelGGL(decompress_small_bf16<7>, grid, block, 0, s, a, gather); break;
-    default: hipLaunchKernelGGL(decompress_small_bf16<8>, grid, block, 0, s, a, gather); break;
-    }
+    if (gather)
+        launch_small<true>(a, s);
+    else
+        launch_small<false>(a, s);
     return hipGetLastError();
 }
 
