@@ -17,20 +17,18 @@ PEAKS_PATH = os.path.join(BUILD_DIR, "libmla_peaks.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
 
 
-def sources():
-    return sorted(glob.glob(os.path.join(SRC_DIR, "*.hip")))
+def sources(src_dir=SRC_DIR):
+    return sorted(glob.glob(os.path.join(src_dir, "*.hip")))
 
 
-def _hipcc(out, srcs, verbose):
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *srcs]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -40,6 +38,23 @@ def _hipcc(out, srcs, verbose):
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build_library(out, srcs, include_dir, verbose=False, jobs=8):
+    """Compile each source to an object, in parallel, then link the objects
+    into the shared library `out`."""
+    from concurrent.futures import ThreadPoolExecutor
+    obj_dir = out + ".objs"
+    os.makedirs(obj_dir, exist_ok=True)
+    objs = [os.path.join(obj_dir, os.path.basename(s) + ".o") for s in srcs]
+
+    def compile_one(i):
+        _run([HIPCC, *FLAGS, "-I", include_dir, "-c", "-o", objs[i], srcs[i]], verbose)
+
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(compile_one, range(len(srcs))))
+    tmp = out + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, out)
 
 
@@ -47,8 +62,9 @@ def build(verbose: bool = False) -> str:
     """Compile every source into the shared library, and the measurement
     kernels into their own (always recompiles)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    _hipcc(LIB_PATH, sources(), verbose)
-    _hipcc(PEAKS_PATH, sorted(glob.glob(os.path.join(SRC_DIR, "peaks", "*.hip"))), verbose)
+    inc = os.path.join(ROOT, "include")
+    build_library(LIB_PATH, sources(), inc, verbose)
+    build_library(PEAKS_PATH, sorted(glob.glob(os.path.join(SRC_DIR, "peaks", "*.hip"))), inc, verbose)
     return LIB_PATH
 
 
