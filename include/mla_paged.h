@@ -222,6 +222,12 @@ size_t mla_decompress_k_paged_fp8_workspace_size(int32_t buffer_length, int32_t 
  *                  codes [M][K] followed (at offset align256(M*K)) by the scales
  *                  float [M][K / k_gran]
  * other arguments  as in mla_decompress_k_paged; k_latent_buffer and k_buffer are BF16
+ *
+ * The workspace argument is an addition to the page's signature: the codes and
+ * scales go through device memory between the quantising gather and the product
+ * (the product reads codes, half the bytes of the bf16 rows, in a loop bound by
+ * its operand loads).  Callers that cannot pass one use
+ * mla_decompress_k_paged_fp8_noalloc.
  */
 mla_status_t mla_decompress_k_paged_fp8(const uint32_t* buffer_row_offsets,
                                         const uint32_t* cache_offsets,
