@@ -167,22 +167,43 @@ __device__ inline void compute_waves(const char* wt, char* at, int nb0, int lane
         lds_barrier();
         const char* ws = wt + q * W_CHUNK_BYTES + (nb0 * 32 + frow) * CROWB;
         const char* as = at + (q % SLOTS) * C::CHUNK_BYTES + frow * CROWB;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        // Fragments of k step kk + 1 are read before step kk's MFMAs go out,
+        // so the LDS latency is exposed once per chunk (after its barrier),
+        // not once per k step.
+        bf16x8 wf[2][NBW], af[2][NBLK > 0 ? NBLK : 1];
+        auto read_step = [&](int kk, int b) __attribute__((always_inline)) {
             const int g = (2 * kk + half) ^ rsw;
-            bf16x8 wf[NBW], af[NBLK > 0 ? NBLK : 1];
 #pragma unroll
             for (int j = 0; j < NBW; ++j)
-                wf[j] = as_bf16x8(lds_ld16(ws + j * 32 * CROWB + g * 16));
+                wf[b][j] = as_bf16x8(lds_ld16(ws + j * 32 * CROWB + g * 16));
 #pragma unroll
             for (int i = 0; i < NBLK; ++i)
-                af[i] = as_bf16x8(lds_ld16(as + (MB0 + MSTEP * i) * 32 * CROWB + g * 16));
+                af[b][i] = as_bf16x8(lds_ld16(as + (MB0 + MSTEP * i) * 32 * CROWB + g * 16));
+        };
+        read_step(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int b = kk & 1;
+            if (kk < 3)
+                read_step(kk + 1, b ^ 1);
 #pragma unroll
             for (int j = 0; j < NBW; ++j)
 #pragma unroll
                 for (int i = 0; i < NBLK; ++i)
                     acc[kk % KSPLIT][j][i] =
-                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], af[i], acc[kk % KSPLIT][j][i], 0, 0, 0);
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[b][j], af[b][i], acc[kk % KSPLIT][j][i], 0, 0, 0);
+        }
+        // Keep that order (the scheduler would otherwise put each read right
+        // before the MFMA that needs it).
+        constexpr int NRD = NBW + (NBLK > 0 ? NBLK : 0), NMF = NBW * NBLK;
+        if constexpr (NMF > 0) {
+            __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+#pragma unroll
+            for (int kk = 0; kk < 3; ++kk) {
+                __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
         }
     }
     // Every wave is past its last LDS read of the chunks: stage the outputs.
