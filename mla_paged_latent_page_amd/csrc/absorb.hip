@@ -154,17 +154,36 @@ __global__ void __launch_bounds__(AB_NT, 1) absorb_bf16(AbsorbArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 acc[i] = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < AB_K / 16; ++kk) {
+            // The fragments of k step kk + 1 are read before step kk's MFMAs
+            // go out (order pinned below), so the LDS latency is exposed once
+            // per tile, not once per MFMA.
+            bf16x8 wf[2], af[2][4];
+            auto read_step = [&](int kk, int b) __attribute__((always_inline)) {
                 const int g = 2 * kk + half;   // lane's 8 k values: granule g of the row
-                const bf16x8 wf = as_bf16x8(lds_ld16(wrow + ((g ^ (frow & 15)) * 16)));
+                wf[b] = as_bf16x8(lds_ld16(wrow + ((g ^ (frow & 15)) * 16)));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 32 * i + frow;
-                    const bf16x8 af = as_bf16x8(lds_ld16(at + r * AB_ROWB + ((g ^ (r & 15)) * 16)));
-                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, af, acc[i], 0, 0, 0);
+                    af[b][i] = as_bf16x8(lds_ld16(at + r * AB_ROWB + ((g ^ (r & 15)) * 16)));
                 }
+            };
+            read_step(0, 0);
+#pragma unroll
+            for (int kk = 0; kk < AB_K / 16; ++kk) {
+                const int b = kk & 1;
+                if (kk + 1 < AB_K / 16)
+                    read_step(kk + 1, b ^ 1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[b], af[b][i], acc[i], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+#pragma unroll
+            for (int kk = 0; kk + 1 < AB_K / 16; ++kk) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             // Stage: lane holds rows 32 i + frow, tile columns 32 wave + 8 q + 4 half + 0..3.
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -367,19 +386,32 @@ __global__ void __launch_bounds__(AB_NT, 1) absorb_fp8(AbsorbArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 acc[i] = f32x16{};
+            // Both k steps' fragments are read before the first MFMA goes out
+            // (order pinned below), so the second step's reads run under the
+            // first step's MFMAs.
+            i32x8 wf[2], af[2][4];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const int g0 = 4 * kk + 2 * half;   // lane's 32 codes: granules g0, g0 + 1
-                const i32x8 wf = join16(lds_ld16(wt[tt] + wrow * AF_ROWB + f8_granule(wrow, g0)),
-                                        lds_ld16(wt[tt] + wrow * AF_ROWB + f8_granule(wrow, g0 + 1)));
+                wf[kk] = join16(lds_ld16(wt[tt] + wrow * AF_ROWB + f8_granule(wrow, g0)),
+                                lds_ld16(wt[tt] + wrow * AF_ROWB + f8_granule(wrow, g0 + 1)));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 32 * i + frow;
-                    const i32x8 af = join16(lds_ld16(qt + r * AF_ROWB + f8_granule(r, g0)),
-                                            lds_ld16(qt + r * AF_ROWB + f8_granule(r, g0 + 1)));
-                    acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, af, acc[i], 0, 0, 0, 127, 0, 127);
+                    af[kk][i] = join16(lds_ld16(qt + r * AF_ROWB + f8_granule(r, g0)),
+                                       lds_ld16(qt + r * AF_ROWB + f8_granule(r, g0 + 1)));
                 }
             }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[kk], af[kk][i], acc[i], 0, 0, 0, 127,
+                                                                             0, 127);
+            __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             const float sw = a.wscale[(int64_t)h * tpn + u * TPB + tt];
             // Stage: lane holds rows 32 i + frow, tile columns 32 wave + 8 q + 4 half + 0..3.
 #pragma unroll
