@@ -13,8 +13,37 @@ FP8_TOL = 3e-2    # same form, fp8 block-scaled outputs
 POISON_OUT = 0x7FC3  # NaN bf16 pattern pre-filled into outputs to catch stray writes
 
 
+GUARD_BYTES = 4096   # canary bytes before and after every output buffer
+GUARD_BYTE = 0xA5
+
+
 def say(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+_guarded = []
+
+
+def guarded_empty(shape, dtype):
+    """A contiguous device tensor with GUARD_BYTES of canary bytes right before
+    and after it in the same allocation (its start stays 256-byte aligned).
+    check_guards() asserts that every canary of every such tensor made since
+    the last check is intact: a write before the start or past the end of an
+    output shows even where it lands outside the rows a test compares."""
+    nbytes = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+    raw = torch.full((GUARD_BYTES + nbytes + GUARD_BYTES,), GUARD_BYTE, dtype=torch.uint8, device="cuda")
+    t = raw[GUARD_BYTES:GUARD_BYTES + nbytes].view(dtype).view(shape)
+    _guarded.append(raw)
+    return t
+
+
+def check_guards(what=""):
+    torch.cuda.synchronize()
+    raws = list(_guarded)
+    _guarded.clear()
+    for raw in raws:
+        g = torch.cat([raw[:GUARD_BYTES], raw[-GUARD_BYTES:]])
+        assert bool((g == GUARD_BYTE).all()), f"{what}: a canary byte next to an output changed"
 
 
 def to_bits(t):
@@ -34,8 +63,8 @@ def run_decompress(case, extra_rows=0, fp8=None):
     dc, t = W.device_decompress(case)
     M, D, N = case.M, case.D_c, case.N
     dt = torch.float32 if case.cache.dtype == "f32" else torch.bfloat16
-    lat = torch.empty((M + extra_rows, D), dtype=dt, device="cuda")
-    out = torch.empty((M + extra_rows, N), dtype=dt, device="cuda")
+    lat = guarded_empty((M + extra_rows, D), dt)
+    out = guarded_empty((M + extra_rows, N), dt)
     if dt == torch.bfloat16:
         lat.view(torch.int16).fill_(POISON_OUT)
         out.view(torch.int16).fill_(POISON_OUT)
@@ -54,7 +83,7 @@ def run_decompress(case, extra_rows=0, fp8=None):
     else:
         mp.mla_decompress_k_paged(t["buffer_row_offsets"], t["cache_offsets"], M, t["weight"], cache,
                                   case.layer_idx, lat, out)
-    torch.cuda.synchronize()
+    check_guards(case.name)
     return res
 
 
@@ -66,9 +95,9 @@ def run_decompress_kv(case, case_v, extra_rows=0):
     _, tv = W.device_decompress(case_v)
     M, D = case.M, case.D_c
     dt = torch.float32 if case.cache.dtype == "f32" else torch.bfloat16
-    lat = torch.empty((M + extra_rows, D), dtype=dt, device="cuda")
-    kout = torch.empty((M + extra_rows, case.N), dtype=dt, device="cuda")
-    vout = torch.empty((M + extra_rows, case_v.N), dtype=dt, device="cuda")
+    lat = guarded_empty((M + extra_rows, D), dt)
+    kout = guarded_empty((M + extra_rows, case.N), dt)
+    vout = guarded_empty((M + extra_rows, case_v.N), dt)
     for x in (lat, kout, vout):
         if dt == torch.bfloat16:
             x.view(torch.int16).fill_(POISON_OUT)
@@ -87,7 +116,7 @@ def run_decompress_kv(case, case_v, extra_rows=0):
     else:
         mp.mla_decompress_kv_paged(t["buffer_row_offsets"], t["cache_offsets"], M, t["weight"], tv["weight"],
                                    cache, case.layer_idx, lat, kout, vout)
-    torch.cuda.synchronize()
+    check_guards(case.name + " fused K+V")
     return res
 
 
@@ -148,13 +177,15 @@ def run_decompress_fp8_cache(case, extra_rows=0):
     dc, t = W.device_decompress(case)
     M, D, N = case.M, case.D_c, case.N
     nblk = case.cache.scale_blocks
-    lat = torch.full((M + extra_rows, D), 0x7F, dtype=torch.uint8, device="cuda")
-    lsc = torch.full((M + extra_rows, nblk), float("nan"), dtype=torch.float32, device="cuda")
-    out = torch.empty((M + extra_rows, N), dtype=torch.bfloat16, device="cuda")
+    lat = guarded_empty((M + extra_rows, D), torch.uint8)
+    lat.fill_(0x7F)
+    lsc = guarded_empty((M + extra_rows, nblk), torch.float32)
+    lsc.fill_(float("nan"))
+    out = guarded_empty((M + extra_rows, N), torch.bfloat16)
     out.view(torch.int16).fill_(POISON_OUT)
     cache = mp.PagedKVCache(dc.pool, dc.page_table, dc.cache_lengths, scales=dc.scales)
     say(f"[gpu] {case.name} fp8 cache: M={M} N={N} K={case.K} D={D} nblk={nblk}")
     mp.mla_decompress_k_paged_fp8_cache(t["buffer_row_offsets"], t["cache_offsets"], M, t["weight_q"],
                                         t["weight_scale"], cache, case.layer_idx, lat, lsc, out)
-    torch.cuda.synchronize()
+    check_guards(case.name + " fp8 cache")
     return {"lat": lat, "scales": lsc, "out": out}

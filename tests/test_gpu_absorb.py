@@ -13,7 +13,7 @@ import torch
 import mla_paged_latent_page_amd as mp
 import oracle
 import workloads as W
-from gpu_util import BF16_TOL, POISON_OUT, check_close, say, to_bits
+from gpu_util import BF16_TOL, POISON_OUT, check_close, check_guards, guarded_empty, say, to_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -21,11 +21,11 @@ pytestmark = pytest.mark.gpu
 def _run(case, extra=3):
     t = W.device_absorb(case)
     T, H = case.T, case.H
-    buf = torch.empty((T + extra, H, case.out_dim), dtype=torch.bfloat16, device="cuda")
+    buf = guarded_empty((T + extra, H, case.out_dim), torch.bfloat16)
     buf.view(torch.int16).fill_(POISON_OUT)
     say(f"[gpu] {case.name}: T={T} H={H} L={case.kv_latent_dim} rope={case.d_rope} copy={case.copy_rope}")
     mp.mla_absorb_q(t["q"], t["w_uk"], buf[:T], d_nope=case.d_nope, copy_rope=case.copy_rope)
-    torch.cuda.synchronize()
+    check_guards(case.name)
     return buf
 
 
@@ -78,12 +78,12 @@ def test_c7_decode_batch():
 def _check_fp8(case, extra=3):
     t = W.device_absorb(case)
     T, H, NL = case.T, case.H, case.kv_latent_dim
-    buf = torch.empty((T + extra, H, case.out_dim), dtype=torch.bfloat16, device="cuda")
+    buf = guarded_empty((T + extra, H, case.out_dim), torch.bfloat16)
     buf.view(torch.int16).fill_(POISON_OUT)
     say(f"[gpu] {case.name} fp8: T={T} H={H} L={NL} rope={case.d_rope} copy={case.copy_rope}")
     mp.mla_absorb_q_fp8(t["q"], t["w_uk_e4m3"], t["w_uk_scale"], buf[:T], d_nope=case.d_nope,
                         copy_rope=case.copy_rope)
-    torch.cuda.synchronize()
+    check_guards(case.name + " fp8")
     lat, rope, _, _ = oracle.absorb_q_fp8(case)
     got = buf[:T, :, :NL].double().cpu().numpy()
     check_close(got.reshape(T, -1), lat.reshape(T, -1), BF16_TOL, f"{case.name} q_latent fp8")

@@ -17,8 +17,8 @@ import torch
 import mla_paged_latent_page_amd as mp
 import oracle
 import workloads as W
-from gpu_util import BF16_TOL, POISON_OUT, check_close, rows_as_f64, run_decompress, run_decompress_fp8_cache, \
-    sample_rows, say, to_bits
+from gpu_util import BF16_TOL, POISON_OUT, check_close, check_guards, guarded_empty, rows_as_f64, run_decompress, \
+    run_decompress_fp8_cache, sample_rows, say, to_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -103,10 +103,12 @@ def _run_kv(case, case_v, extra=3):
     dc, t = W.device_decompress(case)
     M, D = case.M, case.D_c
     nblk = case.cache.scale_blocks
-    lat = torch.full((M + extra, D), 0x7F, dtype=torch.uint8, device="cuda")
-    lsc = torch.full((M + extra, nblk), float("nan"), dtype=torch.float32, device="cuda")
-    kout = torch.empty((M + extra, case.N), dtype=torch.bfloat16, device="cuda")
-    vout = torch.empty((M + extra, case_v.N), dtype=torch.bfloat16, device="cuda")
+    lat = guarded_empty((M + extra, D), torch.uint8)
+    lat.fill_(0x7F)
+    lsc = guarded_empty((M + extra, nblk), torch.float32)
+    lsc.fill_(float("nan"))
+    kout = guarded_empty((M + extra, case.N), torch.bfloat16)
+    vout = guarded_empty((M + extra, case_v.N), torch.bfloat16)
     kout.view(torch.int16).fill_(POISON_OUT)
     vout.view(torch.int16).fill_(POISON_OUT)
     wv = torch.from_numpy(case_v.weight_q).cuda()
@@ -115,7 +117,7 @@ def _run_kv(case, case_v, extra=3):
     say(f"[gpu] {case.name} fp8 cache, K and V: M={M} N_k={case.N} N_v={case_v.N} K={case.K}")
     mp.mla_decompress_kv_paged_fp8_cache(t["buffer_row_offsets"], t["cache_offsets"], M, t["weight_q"],
                                          t["weight_scale"], wv, sv, cache, case.layer_idx, lat, lsc, kout, vout)
-    torch.cuda.synchronize()
+    check_guards(case.name + " fp8 cache K and V")
     return lat, lsc, kout, vout
 
 

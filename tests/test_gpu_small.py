@@ -11,7 +11,7 @@ import torch
 import mla_paged_latent_page_amd as mp
 import oracle
 import workloads as W
-from gpu_util import BF16_TOL, POISON_OUT, check_close, run_decompress, say, to_bits
+from gpu_util import BF16_TOL, POISON_OUT, check_close, check_guards, guarded_empty, run_decompress, say, to_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -92,11 +92,11 @@ def test_latent_matmul_few_rows(M):
     a_bits[:, K:] = W.POISON_BF16
     A = torch.from_numpy(a_bits.view(np.int16)).cuda().view(torch.bfloat16)
     Wt = torch.from_numpy(w_bits.view(np.int16)).cuda().view(torch.bfloat16)
-    out = torch.empty((M + 2, N), dtype=torch.bfloat16, device="cuda")
+    out = guarded_empty((M + 2, N), torch.bfloat16)
     out.view(torch.int16).fill_(POISON_OUT)
     say(f"[gpu] latent_matmul few rows M={M}")
     mp.mla_latent_matmul(A, M, Wt, out)
-    torch.cuda.synchronize()
+    check_guards(f"latent_matmul few rows M={M}")
     ref = oracle.matmul_nt(a_bits, "bf16", w_bits, "bf16", K)
     check_close(out[:M].double().cpu().numpy(), ref, BF16_TOL, f"latent_matmul M={M}")
     assert np.all(to_bits(out)[M:] == POISON_OUT)

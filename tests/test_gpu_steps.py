@@ -12,7 +12,7 @@ import torch
 import mla_paged_latent_page_amd as mp
 import oracle
 import workloads as W
-from gpu_util import BF16_TOL, POISON_OUT, check_close, run_decompress, say, to_bits
+from gpu_util import BF16_TOL, POISON_OUT, check_close, check_guards, guarded_empty, run_decompress, say, to_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -22,12 +22,12 @@ OK, SHAPE, RANGE = 0, 2, 5
 def _gather(case, extra_rows=5):
     dc, t = W.device_decompress(case)
     dt = torch.float32 if case.cache.dtype == "f32" else torch.bfloat16
-    lat = torch.empty((case.M + extra_rows, case.D_c), dtype=dt, device="cuda")
+    lat = guarded_empty((case.M + extra_rows, case.D_c), dt)
     lat.view(torch.int16 if dt == torch.bfloat16 else torch.int32).fill_(POISON_OUT)
     cache = mp.PagedKVCache(dc.pool, dc.page_table, dc.cache_lengths)
     say(f"[gpu] gather {case.name}: M={case.M} D={case.D_c} ps={case.cache.page_size}")
     mp.mla_gather_latent_paged(t["buffer_row_offsets"], t["cache_offsets"], case.M, cache, case.layer_idx, lat)
-    torch.cuda.synchronize()
+    check_guards("gather " + case.name)
     return lat, dc, t
 
 
@@ -62,11 +62,11 @@ def test_latent_matmul_alone(ld_extra):
     a_bits[:, K:] = W.POISON_BF16
     A = torch.from_numpy(a_bits.view(np.int16)).cuda().view(torch.bfloat16)
     Wt = torch.from_numpy(w_bits.view(np.int16)).cuda().view(torch.bfloat16)
-    out = torch.empty((M + 3, N), dtype=torch.bfloat16, device="cuda")
+    out = guarded_empty((M + 3, N), torch.bfloat16)
     out.view(torch.int16).fill_(POISON_OUT)
     say(f"[gpu] latent_matmul M={M} N={N} K={K} ld={K + ld_extra}")
     mp.mla_latent_matmul(A, M, Wt, out)
-    torch.cuda.synchronize()
+    check_guards(f"latent_matmul M={M}")
     ref = oracle.matmul_nt(a_bits, "bf16", w_bits, "bf16", K)
     check_close(out[:M].double().cpu().numpy(), ref, BF16_TOL, f"latent_matmul ld={K + ld_extra}")
     assert np.all(to_bits(out)[M:] == POISON_OUT)
@@ -139,3 +139,17 @@ def test_check_indices_append_mode():
     st, bad = mp.mla_check_indices(t["input_row_offsets"], None, case.T, over)
     iro = case.input_row_offsets
     assert (st, bad) == ((RANGE, 0) if iro[1] > iro[0] else (OK, -1))
+
+
+def test_guard_canaries_catch_a_write_next_to_an_output():
+    """The canaries around the tests' outputs: a byte changed right before or
+    right after an output buffer (written here from the host) is reported."""
+    import gpu_util
+    for where in (gpu_util.GUARD_BYTES - 1, -gpu_util.GUARD_BYTES):
+        guarded_empty((4, 64), torch.bfloat16).zero_()
+        gpu_util._guarded[-1][where] = 0
+        with pytest.raises(AssertionError, match="canary"):
+            check_guards("planted")
+    guarded_empty((4, 64), torch.bfloat16).zero_()
+    check_guards("untouched")
+
