@@ -44,6 +44,7 @@ constexpr int SBN = 64, SK = 512, SMAX_M = 256;
 constexpr int SNT = 512;                         // 8 waves
 constexpr int W_BYTES = SBN * SK * 2;            // 64 KB weight tile
 constexpr int CHUNK_K = 64, CHUNKS = SK / CHUNK_K, CROWB = CHUNK_K * 2;
+constexpr int SLOTS_MAX = 6;                      // row chunks in LDS at once (ring slots)
 constexpr int W_CHUNK_BYTES = SBN * CROWB;       // 8 KB: one chunk of the weight tile
 constexpr int A_AREA = 96 * 1024;                // row chunks (first the row table, last the output staging)
 constexpr int W_PIECES = W_CHUNK_BYTES / 1024;   // 1 KB loads per weight chunk
@@ -75,7 +76,9 @@ template <int MB>
 struct SmallCfg {
     static constexpr int ROWS = 32 * MB;                         // rows loaded (M rounded up)
     static constexpr int CHUNK_BYTES = ROWS * CROWB;
-    static constexpr int FIT = A_AREA / CHUNK_BYTES;
+    // At most SLOTS_MAX chunks of rows in LDS: with fewer rows in flight at
+    // the start, the first chunks' rows and the weight land sooner.
+    static constexpr int FIT = A_AREA / CHUNK_BYTES < SLOTS_MAX ? A_AREA / CHUNK_BYTES : SLOTS_MAX;
     static constexpr bool RING = FIT < CHUNKS;
     static constexpr int SLOTS = RING ? FIT : CHUNKS;
     static constexpr int INITIAL = RING ? SLOTS - 1 : CHUNKS;    // chunks issued before the loop
