@@ -20,7 +20,8 @@
 //  * then waves 4..7 each issue, chunk after chunk, their share of the row
 //    chunks (the rows are read by every block, so mostly from L2).  Row
 //    chunks that do not fit in LDS at once go through a ring of slots
-//    refilled as chunks are consumed;
+//    refilled as chunks are consumed (for 129..192 rows the weight chunks
+//    after the first few go through the same slots, beside their rows);
 //  * waves 0..3 run v_mfma_f32_32x32x16_bf16 on chunk q as soon as its pieces
 //    have landed, with the weight as the row operand: up to 160 rows, wave w
 //    owns weight rows 32 (w % 2) .. +32 and the 32-row blocks w/2, w/2 + 2, ...
@@ -54,6 +55,7 @@ constexpr int EARLY_COPY_ROWS = 2;               // k_latent_buffer rows per blo
 constexpr int EARLY_COPY_GRANULES = 128;         // up to 2048-byte cache rows
 constexpr int PT_STAGE_MAX = 16384;              // page tables up to 64 KB are copied into LDS whole
 constexpr int ROW_TABLE = A_AREA - SMAX_M * 16;  // row table: rowaddr, row_req, row_pos (4 KB)
+constexpr int LDS_BYTES = 160 * 1024;
 
 // vmcnt is a 6-bit counter: a wave never has more than 63 vector memory
 // operations outstanding (issue waits instead), so a wait for at most 63
@@ -72,18 +74,38 @@ typedef __attribute__((address_space(1))) u32x4 g_u32x4;
 __device__ inline u32x4 gld16(const void* p) { return *(const g_u32x4*)p; }
 __device__ inline void gst16(void* p, u32x4 v) { *(g_u32x4*)p = v; }
 
+constexpr int cmin(int x, int y) { return x < y ? x : y; }
+
+// LDS layout.  The whole 64 KB weight tile stays in LDS and the row chunks go
+// through the remaining 96 KB (at most SLOTS_MAX chunks of rows at once: with
+// fewer rows in flight at the start, the first chunks' rows and the weight
+// land sooner); or, where that leaves room for fewer chunks of rows than
+// LDS could hold with the weight streamed beside them (160 or 192 rows), each
+// ring slot holds a chunk of rows and the same chunk of the weight (WRING).
+// The rows then have one more chunk in flight: with every block reading the
+// same rows, their loads take long to land, and chunks in flight set the
+// pace.  Only weight chunks with a free slot can go early, so the streamed
+// layout is used only where at least four can (five slots): with three, the
+// weight stream starts too thin to cover the index round trip of many rows
+// (224 and 256 rows ran 2 % slower streamed than resident).
 template <int MB>
 struct SmallCfg {
     static constexpr int ROWS = 32 * MB;                         // rows loaded (M rounded up)
     static constexpr int CHUNK_BYTES = ROWS * CROWB;
-    // At most SLOTS_MAX chunks of rows in LDS: with fewer rows in flight at
-    // the start, the first chunks' rows and the weight land sooner.
-    static constexpr int FIT = A_AREA / CHUNK_BYTES < SLOTS_MAX ? A_AREA / CHUNK_BYTES : SLOTS_MAX;
+    static constexpr int FIT_RESIDENT = cmin(A_AREA / CHUNK_BYTES, SLOTS_MAX);
+    static constexpr int FIT_STREAMED = cmin(LDS_BYTES / (CHUNK_BYTES + W_CHUNK_BYTES), SLOTS_MAX);
+    static constexpr bool WRING = FIT_RESIDENT < CHUNKS && FIT_STREAMED > FIT_RESIDENT && FIT_STREAMED >= 5;
+    static constexpr int FIT = WRING ? FIT_STREAMED : FIT_RESIDENT;
     static constexpr bool RING = FIT < CHUNKS;
     static constexpr int SLOTS = RING ? FIT : CHUNKS;
     static constexpr int INITIAL = RING ? SLOTS - 1 : CHUNKS;    // chunks issued before the loop
+    static constexpr int WT_BYTES = WRING ? SLOTS * W_CHUNK_BYTES : W_BYTES;
+    static constexpr int AT_BYTES = WRING ? SLOTS * CHUNK_BYTES : A_AREA;
+    // LDS slot of weight chunk c.
+    static constexpr int wslot(int c) { return WRING ? c % SLOTS : c; }
     static_assert(SLOTS >= 2 && ROWS % 32 == 0, "chunk ring");
-    static_assert(W_BYTES + A_AREA <= 163840 && ROWS * CROWB <= A_AREA, "LDS budget");
+    static_assert(WT_BYTES + AT_BYTES <= LDS_BYTES && CHUNK_BYTES <= AT_BYTES, "LDS budget");
+    static_assert(AT_BYTES >= A_AREA, "the row table and the staged page table fit in the rows' area");
 };
 
 // Weight chunks put in flight at kernel start; the later ones go out one per
@@ -91,24 +113,34 @@ struct SmallCfg {
 // the index round trip: enough weight to keep HBM busy over it goes first
 // (more for many rows, whose product takes longer to catch up).  Reading
 // k_latent_buffer, the rows can go out at once, in K order with the weight.
+// With the weight streamed through the ring, only chunks with a free slot
+// can go early.
 template <int MB, bool GATHER>
 constexpr int w_early()
 {
-    return GATHER ? (MB <= 3 ? 3 : 5) : 1;
+    return cmin(GATHER ? (MB <= 3 ? 3 : 5) : 1, SmallCfg<MB>::WRING ? SmallCfg<MB>::INITIAL : CHUNKS);
 }
 static_assert(PT_STAGE_MAX * 4 <= ROW_TABLE, "the staged page table and the row table do not overlap");
 static_assert(W_PIECES % COMPUTE_WAVES == 0 && COMPUTE_WAVES == LOADER_WAVES, "weight loads split evenly");
 
 // Loader wave (each issues, per chunk c, MB row loads and then its share of
-// weight chunk c + E): chunk q's row loads and (q >= E) weight loads must
-// have landed.  The weight loads of chunk q went out before its
-// row loads, so the loads still allowed in flight are the ones issued after
-// chunk q's row loads.
+// weight chunk c + E; with the weight streamed, of weight chunk c itself when
+// c >= E): chunk q's row loads and (q >= E) weight loads must have landed.
+// Resident weight: the weight loads of chunk q went out before its row
+// loads, so the loads still allowed in flight are the ones issued after
+// chunk q's row loads.  Streamed weight: the ones issued after chunk q's
+// weight loads.
 template <int MB, int E>
 constexpr int loads_after(int q)
 {
     using C = SmallCfg<MB>;
     const int issued = C::RING ? (C::INITIAL + q < CHUNKS ? C::INITIAL + q : CHUNKS) : CHUNKS;
+    if (C::WRING) {
+        int n = 0;
+        for (int c = q + 1; c < issued; ++c)
+            n += MB + (c >= E ? W_PER_WAVE : 0);
+        return n;
+    }
     int n = q + E < CHUNKS ? W_PER_WAVE : 0;
     for (int c = q + 1; c < issued; ++c)
         n += MB + (c + E < CHUNKS ? W_PER_WAVE : 0);
@@ -168,7 +200,7 @@ __device__ inline void compute_waves(const char* wt, char* at, int nb0, int lane
         default: wait_weight<E, 7>(); break;
         }
         lds_barrier();
-        const char* ws = wt + q * W_CHUNK_BYTES + (nb0 * 32 + frow) * CROWB;
+        const char* ws = wt + C::wslot(q) * W_CHUNK_BYTES + (nb0 * 32 + frow) * CROWB;
         const char* as = at + (q % SLOTS) * C::CHUNK_BYTES + frow * CROWB;
         // Fragments of k step kk + 1 are read before step kk's MFMAs go out,
         // so the LDS latency is exposed once per chunk (after its barrier),
@@ -241,8 +273,8 @@ __global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a
     constexpr bool gather = GATHER;
     constexpr int E = w_early<MB, GATHER>();
     constexpr int SLOTS = C::SLOTS;
-    __shared__ __attribute__((aligned(1024))) char wt[W_BYTES];
-    __shared__ __attribute__((aligned(1024))) char at[A_AREA];
+    __shared__ __attribute__((aligned(1024))) char wt[C::WT_BYTES];
+    __shared__ __attribute__((aligned(1024))) char at[C::AT_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -266,7 +298,7 @@ __global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a
     auto issue_w = [&](int c, int p) __attribute__((always_inline)) {
         const int row = 8 * p + lrow;
         const uint32_t voff = (uint32_t)(row * SK * 2 + ((lpos ^ ((row >> 1) & 7)) * 16));
-        asm_ld16_lds(wr, wt_lds + c * W_CHUNK_BYTES + p * 1024, voff, (uint32_t)(n0 * SK * 2 + c * CROWB));
+        asm_ld16_lds(wr, wt_lds + C::wslot(c) * W_CHUNK_BYTES + p * 1024, voff, (uint32_t)(n0 * SK * 2 + c * CROWB));
     };
 
     // 1. Wave 4 resolves the rows' cache addresses into a table in LDS: one
@@ -415,16 +447,18 @@ __global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a
 
     if (wave >= 4) {
         // Chunk c: this wave's row loads, then its share of weight chunk
-        // c + W_EARLY, so rows and the rest of the weight arrive in K order.
+        // c + E (streamed weight: of chunk c, in the same slot), so rows and
+        // the rest of the weight arrive in K order.
         auto issue_chunk = [&](int c) __attribute__((always_inline)) {
             const int slot = c % SLOTS;
 #pragma unroll
             for (int k = 0; k < MB; ++k)
                 asm_gld16_lds(src_row[k] + c * CROWB, at_lds + slot * C::CHUNK_BYTES + (w + 4 * k) * 1024);
-            if (c + E < CHUNKS)
+            const int cw = C::WRING ? c : c + E;
+            if (cw >= E && cw < CHUNKS)
 #pragma unroll
                 for (int j = 0; j < W_PER_WAVE; ++j)
-                    issue_w(c + E, W_PER_WAVE * w + j);
+                    issue_w(cw, W_PER_WAVE * w + j);
         };
 #pragma unroll
         for (int c = 0; c < C::INITIAL; ++c)
