@@ -13,8 +13,8 @@
 //  * at kernel start the compute waves 0..3 put the whole weight tile in
 //    flight, chunk after chunk, while wave 4 resolves the rows' cache
 //    addresses (one lane per request reads its offsets, then one lane per row
-//    its page-table entry; a small page table is copied into LDS in the same
-//    round of loads as the offsets) into a table in LDS.  The weight is the
+//    of waves 4..7 its page-table entry; a small page table is copied into
+//    LDS in the same round of loads as the offsets) into a table in LDS.  The weight is the
 //    one HBM stream of the call: it starts at once and is not held up by the
 //    index loads' round trip;
 //  * then waves 4..7 each issue, chunk after chunk, their share of the row
@@ -303,8 +303,8 @@ __global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a
 
     // 1. Wave 4 resolves the rows' cache addresses into a table in LDS: one
     //    lane per request reads its offsets and writes each of its rows'
-    //    request and token position into LDS; then one lane per row looks up
-    //    the page-table entry of its row.  A page table of at most
+    //    request and token position into LDS; then one lane per row (on
+    //    waves 4..7) looks up the page-table entry of its row.  A page table of at most
     //    PT_STAGE_MAX entries is copied whole into LDS (the row chunks' area,
     //    unused until the table is built) in the same round of loads as the
     //    offsets, so the lookups are LDS reads: one round of memory latency
@@ -376,45 +376,46 @@ __global__ void __launch_bounds__(SNT, 1) decompress_small_bf16(DecompressArgs a
                     break;
                 load_round(b0);
             }
-            // The page table's copy (loads older than the offsets' ones, so
-            // landed once those have) and the row entries are in LDS.
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-            constexpr int RPL = (C::ROWS + 63) / 64;
-            const PagedLayer& L = a.L;
-            const uint32_t* pt_lds = reinterpret_cast<const uint32_t*>(at);
-            uint32_t pgv[RPL], slot[RPL];
-            bool valid[RPL];
-#pragma unroll
-            for (int k = 0; k < RPL; ++k) {
-                const int r = lane + 64 * k;
-                const uint32_t b = r < C::ROWS ? row_req[r] : ~0u;
-                valid[k] = b != ~0u;
-                const uint32_t pos = valid[k] ? row_pos[r] : 0u, bb = valid[k] ? b : 0u;
-                uint32_t lp = pos / L.page_size;
-                slot[k] = pos - lp * L.page_size;
-                lp = lp < L.max_pages ? lp : L.max_pages - 1;
-                const size_t e = (size_t)bb * L.max_pages + lp;
-                pgv[k] = pt_staged ? pt_lds[e] : L.page_table[e];
-            }
-#pragma unroll
-            for (int k = 0; k < RPL; ++k) {
-                const uint32_t pg = pgv[k] < L.num_pages ? pgv[k] : L.num_pages - 1;
-                const int64_t off = valid[k] ? (int64_t)pg * L.stride_page + (int64_t)slot[k] * L.stride_token : 0;
-                if (lane + 64 * k < C::ROWS)
-                    rowaddr[lane + 64 * k] = (uint64_t)(L.base + off);
-            }
         } else {
             for (int r = lane; r < M; r += 64)
                 rowaddr[r] = (uint64_t)(static_cast<const char*>(a.lat) + (int64_t)r * a.D * 2);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            for (int r = M + lane; r < C::ROWS; r += 64)
+                rowaddr[r] = rowaddr[M - 1];
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        for (int r = M + lane; r < C::ROWS; r += 64)
-            rowaddr[r] = rowaddr[M - 1];
         // The compiler's own wait (vmcnt(0), known to its wait pass): no load
         // of this branch is left pending where the wave roles' code joins,
         // so no conservative wait lands on the weight waves, whose loads into
-        // LDS it cannot see and would wait for too.
+        // LDS it cannot see and would wait for too.  Gathering, the page
+        // table's copy (loads older than the offsets' ones) has then landed.
         __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+    if (gather) {
+        // Every row's request and position, and the page table's copy, are in
+        // LDS.  Waves 4..7 look the rows up, one per lane (row 64 (wave - 4) +
+        // lane; rows M .. ROWS-1 take row M-1's address), so the division and
+        // 64-bit address arithmetic of 256 rows run as one step on four waves
+        // instead of four steps on one.
+        lds_barrier();
+        if (wave >= 4) {
+            const int r = 64 * (wave - 4) + lane;
+            if (r < C::ROWS) {
+                const PagedLayer& L = a.L;
+                const int re = r < M ? r : M - 1;
+                const uint32_t b = row_req[re];
+                const bool valid = b != ~0u;
+                const uint32_t pos = valid ? row_pos[re] : 0u, bb = valid ? b : 0u;
+                uint32_t lp = pos / L.page_size;
+                const uint32_t slot = pos - lp * L.page_size;
+                lp = lp < L.max_pages ? lp : L.max_pages - 1;
+                const size_t e = (size_t)bb * L.max_pages + lp;
+                const uint32_t pgv = pt_staged ? reinterpret_cast<const uint32_t*>(at)[e] : L.page_table[e];
+                const uint32_t pg = pgv < L.num_pages ? pgv : L.num_pages - 1;
+                const int64_t off = valid ? (int64_t)pg * L.stride_page + (int64_t)slot * L.stride_token : 0;
+                rowaddr[r] = (uint64_t)(L.base + off);
+            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+        }
     }
     lds_barrier();              // row table written
 
