@@ -340,11 +340,20 @@ __global__ void __launch_bounds__(AB_NT, 1) absorb_fp8(AbsorbArgs a)
             ab_vm_wait<AB_M / 16>();
         lds_barrier();
         // Quantise the chunk: lanes 16 k .. 16 k + 15 hold row 16 p + 4 wave + k,
-        // 8 values each (one granule of the bf16 row).
+        // 8 values each (one granule of the bf16 row).  All of the lane's
+        // granules are read before the first is used (one LDS round trip, not
+        // one per row).
+        u32x4 qv[AB_M / 16];
 #pragma unroll
         for (int p = 0; p < AB_M / 16; ++p) {
             const int r = 16 * p + 4 * wave + lr;
-            const u32x4 v = lds_ld16(at + r * AB_ROWB + ((lg ^ (r & 15)) * 16));
+            qv[p] = lds_ld16(at + r * AB_ROWB + ((lg ^ (r & 15)) * 16));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < AB_M / 16; ++p) {
+            const int r = 16 * p + 4 * wave + lr;
+            const u32x4 v = qv[p];
             float x[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -355,10 +364,7 @@ __global__ void __launch_bounds__(AB_NT, 1) absorb_fp8(AbsorbArgs a)
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 am = fmaxf(am, fabsf(x[i]));
-            am = fmaxf(am, __shfl_xor(am, 1));
-            am = fmaxf(am, __shfl_xor(am, 2));
-            am = fmaxf(am, __shfl_xor(am, 4));
-            am = fmaxf(am, __shfl_xor(am, 8));
+            am = max16(am);
             float sq = 1.0f, inv = 1.0f;
             if (am > 0.0f) {
                 sq = am / 448.0f;

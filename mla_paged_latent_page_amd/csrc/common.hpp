@@ -194,6 +194,25 @@ __device__ inline void buf_st16_nt(rsrc_t r, u32x4 v, uint32_t voff, uint32_t so
 // operand read touches over all LDS banks.
 __device__ inline int swz(int row, int g, int gpr) { return g ^ (row & (gpr - 1)); }
 
+// Maximum of v over each group of 16 lanes (lanes 16 k .. 16 k + 15), by DPP
+// moves inside the 16-lane rows: quad lanes xor 1, xor 2, then the other
+// quad of the half row (half-row mirror), then the other half (row mirror).
+// Plain VALU work, where shuffles through LDS (ds_bpermute) would each wait
+// an LDS round trip.  A maximum is exact in any order.
+template <int CTRL>
+__device__ inline float dpp_f32(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ inline float max16(float v)
+{
+    v = fmaxf(v, dpp_f32<0xB1>(v));    // quad_perm [1, 0, 3, 2]
+    v = fmaxf(v, dpp_f32<0x4E>(v));    // quad_perm [2, 3, 0, 1]
+    v = fmaxf(v, dpp_f32<0x141>(v));   // row_half_mirror
+    v = fmaxf(v, dpp_f32<0x140>(v));   // row_mirror
+    return v;
+}
+
 // Tile-to-block map.  Blocks are dispatched to the 8 XCDs round-robin
 // (block i runs on XCD i % 8).  When the N tiles split evenly over the XCDs,
 // XCD x takes N-tiles [x*G, (x+1)*G) for every M-tile, so its slice of the

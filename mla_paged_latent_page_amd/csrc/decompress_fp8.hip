@@ -48,10 +48,7 @@ __global__ void __launch_bounds__(256) gather_quant_fp8_kernel(DecompressArgs a)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             am = fmaxf(am, fabsf(x[i]));
-        am = fmaxf(am, __shfl_xor(am, 1));
-        am = fmaxf(am, __shfl_xor(am, 2));
-        am = fmaxf(am, __shfl_xor(am, 4));
-        am = fmaxf(am, __shfl_xor(am, 8));
+        am = max16(am);
         float s = 1.0f, inv = 1.0f;
         if (am > 0.0f) {
             s = am / 448.0f;

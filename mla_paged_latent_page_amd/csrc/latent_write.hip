@@ -44,14 +44,6 @@ __device__ inline float wave_sum(float v)
     return v;
 }
 
-// Max over the 16-lane group of this lane.
-__device__ inline float group16_max(float v)
-{
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1)
-        v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
-}
 
 // Eight fp32 values of one 128-column block, quantised with the block's scale:
 // the 8 codes (packed little-endian) and, returned, the scale.
@@ -61,7 +53,7 @@ __device__ inline float quantise8(const float (&y)[8], u32x2& codes)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         am = fmaxf(am, fabsf(y[i]));
-    am = group16_max(am);
+    am = max16(am);
     float s = 1.0f, to_codes = 1.0f;
     if (am > 0.0f) {
         s = am / 448.0f;
