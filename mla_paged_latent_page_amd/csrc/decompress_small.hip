@@ -126,16 +126,16 @@ static_assert(W_PIECES % COMPUTE_WAVES == 0 && COMPUTE_WAVES == LOADER_WAVES, "w
 // Loader wave (each issues, per chunk c, MB row loads and then its share of
 // weight chunk c + E; with the weight streamed, of weight chunk c itself when
 // c >= E): chunk q's row loads and (q >= E) weight loads must have landed.
-// Resident weight: the weight loads of chunk q went out before its row
-// loads, so the loads still allowed in flight are the ones issued after
-// chunk q's row loads.  Streamed weight: the ones issued after chunk q's
-// weight loads.
+// Resident weight with E >= 1: the weight loads of chunk q went out before
+// its row loads, so the loads still allowed in flight are the ones issued
+// after chunk q's row loads.  Streamed weight, or E = 0: the ones issued
+// after chunk q's weight loads.
 template <int MB, int E>
 constexpr int loads_after(int q)
 {
     using C = SmallCfg<MB>;
     const int issued = C::RING ? (C::INITIAL + q < CHUNKS ? C::INITIAL + q : CHUNKS) : CHUNKS;
-    if (C::WRING) {
+    if (C::WRING || E == 0) {
         int n = 0;
         for (int c = q + 1; c < issued; ++c)
             n += MB + (c >= E ? W_PER_WAVE : 0);
