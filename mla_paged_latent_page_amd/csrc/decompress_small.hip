@@ -4,19 +4,19 @@
 // "mla_prefill_decode_graph_fp8", Args w_k).
 //
 // With M <= 256 rows the call is bound by reading the weight (N x 512 bf16,
-// 16 MiB at N = 16384) once from HBM, so the whole weight must be in flight at
-// once, the product must run while it streams in, and the call must be one
+// 16 MiB at N = 16384) once from HBM, so the weight must stream in from the
+// start, the product must run while it streams in, and the call must be one
 // launch.  One block of 8 waves per 64 weight rows (256 blocks at N = 16384,
 // one per CU).  The block's 64 x 512 weight tile (64 KB) and the rows' first
 // 512 columns go into LDS in K order, in chunks of 64 columns (128-byte row
 // pieces; weight chunk q is 8 KB):
-//  * at kernel start the compute waves 0..3 put the whole weight tile in
+//  * at kernel start the compute waves 0..3 put the first weight chunks in
 //    flight, chunk after chunk, while wave 4 resolves the rows' cache
 //    addresses (one lane per request reads its offsets, then one lane per row
 //    of waves 4..7 its page-table entry; a small page table is copied into
-//    LDS in the same round of loads as the offsets) into a table in LDS.  The weight is the
-//    one HBM stream of the call: it starts at once and is not held up by the
-//    index loads' round trip;
+//    LDS in the same round of loads as the offsets) into a table in LDS.
+//    The weight is the one HBM stream of the call: it starts at once and is
+//    not held up by the index loads' round trip;
 //  * then waves 4..7 each issue, chunk after chunk, their share of the row
 //    chunks (the rows are read by every block, so mostly from L2).  Row
 //    chunks that do not fit in LDS at once go through a ring of slots
