@@ -172,21 +172,18 @@ __device__ inline void compute_waves(const char* wt, char* at, int nb0, int lane
     using C = SmallCfg<MB>;
     constexpr int SLOTS = C::SLOTS;
     constexpr int NBLK = MB > MB0 ? (MB - MB0 + MSTEP - 1) / MSTEP : 0;   // M blocks of this wave
-    // Independent accumulators per output block (k steps split round-robin,
-    // summed at the end), so a wave with one or two output blocks still keeps
-    // four MFMA chains in flight instead of waiting on each result.
-    constexpr int NACC = NBW * (NBLK > 0 ? NBLK : 1);
-    constexpr int KSPLIT = NACC >= 4 ? 1 : 4 / NACC;
+    // One accumulator per output block.  A wave with a single block runs its
+    // MFMAs as one dependent chain: each chunk's four arrive faster than the
+    // chunks do, and the chain ends with no partial sums to add (four
+    // independent chains summed at the end measured 1-2 % slower).
     const int frow = lane & 31, half = lane >> 5;
     const int rsw = (frow >> 1) & 7;          // granule swizzle of every row this lane reads
-    f32x16 acc[KSPLIT][NBW][NBLK > 0 ? NBLK : 1];
+    f32x16 acc[NBW][NBLK > 0 ? NBLK : 1];
 #pragma unroll
-    for (int s = 0; s < KSPLIT; ++s)
+    for (int j = 0; j < NBW; ++j)
 #pragma unroll
-        for (int j = 0; j < NBW; ++j)
-#pragma unroll
-            for (int i = 0; i < NBLK; ++i)
-                acc[s][j][i] = f32x16{};
+        for (int i = 0; i < NBLK; ++i)
+            acc[j][i] = f32x16{};
 #pragma unroll
     for (int q = 0; q < CHUNKS; ++q) {
         switch (q) {
@@ -225,8 +222,7 @@ __device__ inline void compute_waves(const char* wt, char* at, int nb0, int lane
             for (int j = 0; j < NBW; ++j)
 #pragma unroll
                 for (int i = 0; i < NBLK; ++i)
-                    acc[kk % KSPLIT][j][i] =
-                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[b][j], af[b][i], acc[kk % KSPLIT][j][i], 0, 0, 0);
+                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[b][j], af[b][i], acc[j][i], 0, 0, 0);
         }
         // Keep that order (the scheduler would otherwise put each read right
         // before the MFMA that needs it).
@@ -243,13 +239,6 @@ __device__ inline void compute_waves(const char* wt, char* at, int nb0, int lane
     }
     // Every wave is past its last LDS read of the chunks: stage the outputs.
     // Lane holds rows 32 mb + frow, columns 32 nb + 8 q + 4 half + 0..3 (q < 4).
-#pragma unroll
-    for (int s = 1; s < KSPLIT; ++s)
-#pragma unroll
-        for (int j = 0; j < NBW; ++j)
-#pragma unroll
-            for (int i = 0; i < NBLK; ++i)
-                acc[0][j][i] += acc[s][j][i];
     lds_barrier();
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
@@ -259,8 +248,8 @@ __device__ inline void compute_waves(const char* wt, char* at, int nb0, int lane
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int g = (nb0 + j) * 4 + q;
-                const u32x2 v = {pack_bf16x2(acc[0][j][i][4 * q], acc[0][j][i][4 * q + 1]),
-                                 pack_bf16x2(acc[0][j][i][4 * q + 2], acc[0][j][i][4 * q + 3])};
+                const u32x2 v = {pack_bf16x2(acc[j][i][4 * q], acc[j][i][4 * q + 1]),
+                                 pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3])};
                 lds_st8(at + m * CROWB + ((g ^ (m & 7)) * 16) + half * 8, v);
             }
         }
