@@ -350,6 +350,29 @@ __global__ void __launch_bounds__(AB_NT, 1) absorb_fp8(AbsorbArgs a)
             qv[p] = lds_ld16(at + r * AB_ROWB + ((lg ^ (r & 15)) * 16));
         }
         __builtin_amdgcn_sched_barrier(0);
+        // Row maxima first (the lane group's 8 rows), then one pair of
+        // divisions per lane for row lg % 8 of its group, whose results each
+        // row's lanes take from lane p of their 16-lane row (a DPP row
+        // broadcast): two divisions per lane instead of sixteen.
+        float amx[AB_M / 16];
+#pragma unroll
+        for (int p = 0; p < AB_M / 16; ++p) {
+            const u32x4 v = qv[p];
+            float am = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                am = fmaxf(am, fmaxf(fabsf(bf16_lo(v[i])), fabsf(bf16_hi(v[i]))));
+            amx[p] = max16(am);
+        }
+        float my_am = amx[0];
+#pragma unroll
+        for (int p = 1; p < AB_M / 16; ++p)
+            my_am = (lg & 7) == p ? amx[p] : my_am;
+        float my_sq = 1.0f, my_inv = 1.0f;
+        if (my_am > 0.0f) {
+            my_sq = my_am / 448.0f;
+            my_inv = 448.0f / my_am;
+        }
 #pragma unroll
         for (int p = 0; p < AB_M / 16; ++p) {
             const int r = 16 * p + 4 * wave + lr;
@@ -360,19 +383,11 @@ __global__ void __launch_bounds__(AB_NT, 1) absorb_fp8(AbsorbArgs a)
                 x[2 * i] = bf16_lo(v[i]);
                 x[2 * i + 1] = bf16_hi(v[i]);
             }
-            float am = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                am = fmaxf(am, fabsf(x[i]));
-            am = max16(am);
-            float sq = 1.0f, inv = 1.0f;
-            if (am > 0.0f) {
-                sq = am / 448.0f;
-                inv = 448.0f / am;
-            }
+            const float inv = row16_lane(my_inv, p);
             const u32x2 codes = {pack_e4m3x2(x[0] * inv, x[1] * inv) | (pack_e4m3x2(x[2] * inv, x[3] * inv) << 16),
                                  pack_e4m3x2(x[4] * inv, x[5] * inv) | (pack_e4m3x2(x[6] * inv, x[7] * inv) << 16)};
             lds_st8(qt + r * AF_ROWB + f8_granule(r, lg >> 1) + (lg & 1) * 8, codes);
+            const float sq = row16_lane(my_sq, p);
             if (lg == 0)
                 qsc[r] = sq;
         }

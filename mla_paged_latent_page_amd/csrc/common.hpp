@@ -212,6 +212,29 @@ __device__ inline float max16(float v)
     v = fmaxf(v, dpp_f32<0x140>(v));   // row_mirror
     return v;
 }
+// The value lane p (0..15, a constant once unrolled) of this lane's 16-lane
+// row holds (DPP row_newbcast).
+__device__ inline float row16_lane(float v, int p)
+{
+    switch (p & 15) {
+    case 0: return dpp_f32<0x150>(v);
+    case 1: return dpp_f32<0x151>(v);
+    case 2: return dpp_f32<0x152>(v);
+    case 3: return dpp_f32<0x153>(v);
+    case 4: return dpp_f32<0x154>(v);
+    case 5: return dpp_f32<0x155>(v);
+    case 6: return dpp_f32<0x156>(v);
+    case 7: return dpp_f32<0x157>(v);
+    case 8: return dpp_f32<0x158>(v);
+    case 9: return dpp_f32<0x159>(v);
+    case 10: return dpp_f32<0x15A>(v);
+    case 11: return dpp_f32<0x15B>(v);
+    case 12: return dpp_f32<0x15C>(v);
+    case 13: return dpp_f32<0x15D>(v);
+    case 14: return dpp_f32<0x15E>(v);
+    default: return dpp_f32<0x15F>(v);
+    }
+}
 
 // Tile-to-block map.  Blocks are dispatched to the 8 XCDs round-robin
 // (block i runs on XCD i % 8).  When the N tiles split evenly over the XCDs,
