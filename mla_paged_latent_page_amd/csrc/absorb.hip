@@ -498,20 +498,26 @@ __global__ void __launch_bounds__(AB_NT, 1) absorb_fp8(AbsorbArgs a)
 hipError_t launch_absorb_fp8(const AbsorbArgs& a, hipStream_t s)
 {
     const int heads8 = (a.H + 7) / 8 * 8, tiles = a.NL / AB_N;
-    if (tiles % 2 == 0)
+    if (tiles % 2 == 0) {
+        log_launch("absorb_fp8<2>", heads8 * (tiles / 2), AB_NT, "T=%d H=%d latent=%d", a.T, a.H, a.NL);
         hipLaunchKernelGGL(absorb_fp8<2>, dim3(heads8 * (tiles / 2)), dim3(AB_NT), 0, s, a);
-    else
+    } else {
+        log_launch("absorb_fp8<1>", heads8 * tiles, AB_NT, "T=%d H=%d latent=%d", a.T, a.H, a.NL);
         hipLaunchKernelGGL(absorb_fp8<1>, dim3(heads8 * tiles), dim3(AB_NT), 0, s, a);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_absorb_bf16(const AbsorbArgs& a, hipStream_t s)
 {
     const int heads8 = (a.H + 7) / 8 * 8, tiles = a.NL / AB_N;
-    if (tiles % 2 == 0)
+    if (tiles % 2 == 0) {
+        log_launch("absorb_bf16<2>", heads8 * (tiles / 2), AB_NT, "T=%d H=%d latent=%d", a.T, a.H, a.NL);
         hipLaunchKernelGGL(absorb_bf16<2>, dim3(heads8 * (tiles / 2)), dim3(AB_NT), 0, s, a);
-    else
+    } else {
+        log_launch("absorb_bf16<1>", heads8 * tiles, AB_NT, "T=%d H=%d latent=%d", a.T, a.H, a.NL);
         hipLaunchKernelGGL(absorb_bf16<1>, dim3(heads8 * tiles), dim3(AB_NT), 0, s, a);
+    }
     return hipGetLastError();
 }
 

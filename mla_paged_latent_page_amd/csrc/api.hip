@@ -6,8 +6,31 @@
 #include <mutex>
 #include <vector>
 
+#include <cstdarg>
+#include <cstdio>
+
 #include "mla_paged.h"
 #include "launch.hpp"
+
+namespace mla {
+
+void log_launch(const char* kernel, unsigned grid, unsigned block, const char* fmt, ...)
+{
+    static const bool on = [] {
+        const char* v = std::getenv("MLA_PAGED_LOG");
+        return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
+    }();
+    if (!on)
+        return;
+    char detail[256];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(detail, sizeof(detail), fmt, ap);
+    va_end(ap);
+    std::fprintf(stderr, "mla_paged: %s grid %u block %u %s\n", kernel, grid, block, detail);
+}
+
+}  // namespace mla
 
 #define MLA_API extern "C" __attribute__((visibility("default")))
 

@@ -251,6 +251,8 @@ hipError_t launch_product_bf16(const DecompressArgs& a, hipStream_t s)
     if (a.K % 128 == 0)
         return launch_product_bf16_ring(a, cus, s);
     GemmParams P = make_gemm_params(a, BM, BN, cus);
+    log_launch("gemm_bf16_persistent", gemm_grid(P, cus), NT, "M=%d N=%d K=%d tiles=%dx%d xcd_map=%d", P.M, P.N, P.K,
+               P.tiles_m, P.tiles_n, P.xcd_map);
     hipLaunchKernelGGL(gemm_bf16_persistent, dim3(gemm_grid(P, cus)), dim3(NT), 0, s, P);
     return hipGetLastError();
 }

@@ -320,6 +320,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_bf16_ring(Gemm
 hipError_t launch_product_bf16_ring(const DecompressArgs& a, int cus, hipStream_t s)
 {
     GemmParams P = make_gemm_params(a, BM, BN, cus);
+    log_launch("gemm_bf16_ring<2,4>", gemm_grid(P, cus), 512, "M=%d N=%d N2=%d K=%d tiles=%dx%d xcd_map=%d", P.M, P.N,
+               P.N2, P.K, P.tiles_m, P.tiles_n, P.xcd_map);
     hipLaunchKernelGGL((gemm_bf16_ring<2, 4>), dim3(gemm_grid(P, cus)), dim3(512), 0, s, P);
     return hipGetLastError();
 }

@@ -42,6 +42,7 @@ __global__ void __launch_bounds__(256) matmul_f32_kernel(DecompressArgs a, int t
 hipError_t launch_product_f32(const DecompressArgs& a, hipStream_t s)
 {
     const int tiles_n = (a.N + 15) / 16, tiles_m = (a.M + 15) / 16;
+    log_launch("matmul_f32_kernel", tiles_n * tiles_m, 256, "M=%d N=%d K=%d", a.M, a.N, a.K);
     hipLaunchKernelGGL(matmul_f32_kernel, dim3(tiles_n * tiles_m), dim3(256), 0, s, a, tiles_n);
     return hipGetLastError();
 }

@@ -110,6 +110,7 @@ inline int quant_blocks(int M) { return (M + 4 * QROWS - 1) / (4 * QROWS); }
 
 hipError_t launch_decompress_fp8(const DecompressArgs& a, hipStream_t s)
 {
+    log_launch("gather_quant_fp8_kernel", quant_blocks(a.M), 256, "M=%d K=%d D=%d", a.M, a.K, a.D);
     hipLaunchKernelGGL(gather_quant_fp8_kernel, dim3(quant_blocks(a.M)), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -138,6 +139,7 @@ hipError_t launch_decompress_fp8_cache(const DecompressArgs& a, hipStream_t s)
 // launch over both projections' N-tiles.
 hipError_t launch_decompress_kv_fp8(const DecompressArgs& a, hipStream_t s)
 {
+    log_launch("gather_quant_fp8_kernel", quant_blocks(a.M), 256, "M=%d K=%d D=%d", a.M, a.K, a.D);
     hipLaunchKernelGGL(gather_quant_fp8_kernel, dim3(quant_blocks(a.M)), dim3(256), 0, s, first_projection(a));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)

@@ -405,6 +405,8 @@ hipError_t launch_product_fp8_ring(const DecompressArgs& a, int cus, hipStream_t
     }
     const int tiles = P.tiles_m * P.tiles_n;
     const int grid = P.xcd_map ? cus : (tiles < cus ? tiles : cus);
+    log_launch("gemm_fp8_ring", grid, NT, "M=%d N=%d N2=%d K=%d tiles=%dx%d xcd_map=%d", P.M, P.N, P.N2, P.K, P.tiles_m,
+               P.tiles_n, P.xcd_map);
     hipLaunchKernelGGL(gemm_fp8_ring, dim3(grid), dim3(NT), 0, s, P);
     return hipGetLastError();
 }

@@ -536,6 +536,8 @@ template <bool GATHER>
 void launch_small(const DecompressArgs& a, hipStream_t s)
 {
     const dim3 grid(a.N / SBN), block(SNT);
+    log_launch(GATHER ? "decompress_small_bf16<gather>" : "decompress_small_bf16<rows>", grid.x, block.x,
+               "M=%d N=%d K=%d row_blocks=%d", a.M, a.N, a.K, (a.M + 31) / 32);
     switch ((a.M + 31) / 32) {
     case 1: hipLaunchKernelGGL((decompress_small_bf16<1, GATHER>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((decompress_small_bf16<2, GATHER>), grid, block, 0, s, a); break;

@@ -77,6 +77,7 @@ hipError_t launch_gather_rows(const DecompressArgs& a, int elem_bytes, hipStream
 {
     const int gpr = a.D * elem_bytes / 16;
     const int waves = (a.M + ROWS - 1) / ROWS;
+    log_launch("gather_rows_kernel", (waves + 3) / 4, 256, "M=%d row_bytes=%d", a.M, gpr * 16);
     hipLaunchKernelGGL(gather_rows_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, a, gpr);
     return hipGetLastError();
 }

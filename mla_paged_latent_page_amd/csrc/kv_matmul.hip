@@ -234,6 +234,8 @@ hipError_t launch_cfg(const KvMatmulArgs& a, hipStream_t s)
     P.tiles_m = (a.T + BM - 1) / BM;
     P.tiles_n = (a.N + BN - 1) / BN;
     P.xcd_map = (P.tiles_n % 8 == 0) ? 1 : 0;
+    log_launch("kv_matmul_kernel", P.tiles_m * P.tiles_n, 64 * WM * WN, "tiles=%dx%d tile=%dx%d", P.tiles_m, P.tiles_n, BM,
+               BN);
     hipLaunchKernelGGL((kv_matmul_kernel<BM, BN, WM, WN>), dim3(P.tiles_m * P.tiles_n), dim3(64 * WM * WN), 0, s, P);
     return hipGetLastError();
 }

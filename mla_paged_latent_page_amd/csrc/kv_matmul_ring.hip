@@ -323,6 +323,7 @@ hipError_t launch_kv_matmul_ring(const KvMatmulArgs& a, int cus, hipStream_t s)
     P.xcd_map = (cus % 8 == 0 && P.tiles_m >= 8) ? 2 : 0;
     const int tiles = P.tiles_m * P.tiles_n;
     const int grid = P.xcd_map ? cus : (tiles < cus ? tiles : cus);
+    log_launch("kv_matmul_ring", grid, NT, "tiles=%dx%d", P.tiles_m, P.tiles_n);
     hipLaunchKernelGGL(kv_matmul_ring, dim3(grid), dim3(NT), 0, s, P);
     return hipGetLastError();
 }

@@ -212,6 +212,7 @@ __global__ void __launch_bounds__(64 * WRITE_WAVES) latent_write_kernel(LatentWr
 hipError_t launch_latent_write(const LatentWriteArgs& a, hipStream_t s)
 {
     constexpr int per_block = WRITE_WAVES * TOKENS_PER_WAVE;
+    log_launch("latent_write_kernel<bf16>", (a.T + per_block - 1) / per_block, 64 * WRITE_WAVES, "T=%d K=%d R=%d", a.T, a.K, a.R);
     hipLaunchKernelGGL(latent_write_kernel<false>, dim3((a.T + per_block - 1) / per_block), dim3(64 * WRITE_WAVES), 0, s,
                        a);
     return hipGetLastError();
@@ -220,6 +221,7 @@ hipError_t launch_latent_write(const LatentWriteArgs& a, hipStream_t s)
 hipError_t launch_latent_write_fp8(const LatentWriteArgs& a, hipStream_t s)
 {
     constexpr int per_block = WRITE_WAVES * TOKENS_PER_WAVE;
+    log_launch("latent_write_kernel<e4m3>", (a.T + per_block - 1) / per_block, 64 * WRITE_WAVES, "T=%d K=%d R=%d", a.T, a.K, a.R);
     hipLaunchKernelGGL(latent_write_kernel<true>, dim3((a.T + per_block - 1) / per_block), dim3(64 * WRITE_WAVES), 0, s,
                        a);
     return hipGetLastError();

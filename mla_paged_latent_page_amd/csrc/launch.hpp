@@ -114,6 +114,12 @@ hipError_t launch_kv_matmul_ring(const KvMatmulArgs& a, int cus, hipStream_t s);
 constexpr int kRingTileN = 256;   // N-tile width of the bf16 ring kernel
 int num_cus();
 bool small_bf16_fits(const DecompressArgs& a);
+
+// With MLA_PAGED_LOG set in the environment (to anything but "0", read once),
+// every kernel launch prints one line to stderr: the kernel, its grid and
+// block sizes and its shape parameters (printf-style).  Otherwise nothing.
+void log_launch(const char* kernel, unsigned grid, unsigned block, const char* fmt, ...)
+    __attribute__((format(printf, 4, 5)));
 hipError_t launch_small_bf16(const DecompressArgs& a, int gather, hipStream_t s);
 
 }  // namespace mla
