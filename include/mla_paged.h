@@ -29,6 +29,9 @@
  *     it is a gfx950), then the launch (MLA_ERR_HIP; mla_last_hip_error() gives the
  *     hipError_t).  A call with no rows to process returns MLA_OK after the host
  *     checks and enqueues nothing.
+ *   - With MLA_PAGED_LOG set in the environment (to anything but "0"; read once
+ *     per process) every kernel launch prints one line to stderr naming the
+ *     kernel, its grid and block sizes and its shapes.
  *   - Index contents in device memory (offsets, page ids) are the caller's
  *     contract and are not validated on the host.  Read paths clamp every page
  *     id, page index and row to the buffers they were given, so a bad index
