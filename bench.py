@@ -37,7 +37,8 @@ Profiling and records (profiles/):
                            the calibration of both counters on a 1 GiB copy)
   --counters-from CSV...   with --row ROW: summarise counter CSVs of
                            `--profile ROW` runs (matrix-pipe busy cycles, clock,
-                           vector-memory unit busy) into
+                           vector-memory unit busy, LDS busy and bank-conflict
+                           stalls) into
                            profiles/<kernel>_<row>_counters.json
 """
 import argparse
@@ -106,7 +107,8 @@ def counters_from_profile(kernel, workload):
     rec = _record(kernel, workload, "counters")
     if not rec:
         return None
-    return {k: rec[k] for k in ("mfma_busy_frac", "clock_ghz", "ta_busy_frac") if k in rec}
+    return {k: rec[k] for k in ("mfma_busy_frac", "clock_ghz", "ta_busy_frac", "lds_busy_frac", "lds_bank_conflict_frac")
+            if k in rec}
 
 
 WARM_SECONDS = 0.2   # the GPU's clock ramps up over some tens of ms after host-side set-up
@@ -689,6 +691,12 @@ def write_counter_record(row_name, csvs, commands):
             rec["ta_busy_frac"] = round(vals["TA_TA_BUSY_sum"] / 256 / cycles, 4)
         if "SQ_BUSY_CU_CYCLES" in vals:
             rec["cu_busy_frac"] = round(vals["SQ_BUSY_CU_CYCLES"] / 256 / cycles, 4)
+        # LDS: cycles it serves indexed accesses (over every CU), and the share
+        # of those cycles stalled by bank conflicts
+        if "SQ_LDS_IDX_ACTIVE" in vals:
+            rec["lds_busy_frac"] = round(vals["SQ_LDS_IDX_ACTIVE"] / 256 / cycles, 4)
+            if "SQ_LDS_BANK_CONFLICT" in vals and vals["SQ_LDS_IDX_ACTIVE"] > 0:
+                rec["lds_bank_conflict_frac"] = round(vals["SQ_LDS_BANK_CONFLICT"] / vals["SQ_LDS_IDX_ACTIVE"], 4)
         if durs:
             rec["dispatch_ns_mean"] = round(float(np.mean(durs)))
             # the busy-cycle count over the dispatch time: meaningful for long
@@ -699,7 +707,8 @@ def write_counter_record(row_name, csvs, commands):
     with open(path, "w") as fo:
         json.dump(rec, fo, indent=1)
     print(json.dumps({"record": os.path.relpath(path, ROOT),
-                      **{k: rec[k] for k in ("mfma_busy_frac", "ta_busy_frac", "clock_ghz", "cycles_per_xcd") if k in rec}}))
+                      **{k: rec[k] for k in ("mfma_busy_frac", "ta_busy_frac", "lds_busy_frac", "lds_bank_conflict_frac",
+                                             "clock_ghz", "cycles_per_xcd") if k in rec}}))
 
 
 def main():
