@@ -19,7 +19,8 @@
 //    E8M0 scale inputs; instead the accumulators are kept in units of the
 //    current stage's scale sig = s_a * s_w: before a stage's MFMAs add its
 //    products, the accumulators are multiplied by ref / sig (ref: the previous
-//    stage's scale), and the epilogue multiplies by the last ref.  The weight is
+//    stage's scale), and the epilogue multiplies by the last ref.  A tile's
+//    first stage starts its accumulators from zero instead.  The weight is
 //    the MFMA's row operand, so a lane's 16 results lie in one output row (one
 //    s_a per 32-row block) and a wave's 64 columns lie in one 128-wide weight
 //    block (s_w is uniform).  A zero s_w makes its stage add nothing: the MFMAs
@@ -123,6 +124,12 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
     if (tl.count == 0)
         return;
     const int total = tl.count * KT;  // stages this block runs
+    // Waves w and w + 4 share a SIMD.  At equal priority the older wave wins
+    // the issue slots, and waves 4..7 reached each stage's barrier some 600
+    // cycles after waves 0..3 (per-stage timestamps); priority for the later
+    // waves evens that out (2-3 % on the whole call).
+    if (wave >= 4)
+        __builtin_amdgcn_s_setprio(1);
 
     // Loader lanes: in a 1 KB chunk (8 rows of 128 bytes) lane l fills row l/8 at
     // granule position l%8, i.e. logical granule (l%8) ^ ((row/2)%8); odd chunks
@@ -279,11 +286,6 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-            for (int j = 0; j < FM; ++j)
-                acc[i][j] = f32x16{};
-#pragma unroll
         for (int j = 0; j < FM; ++j)
             ref[j] = 0.0f;
     };
@@ -309,7 +311,6 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
         load_frags(slot, std::integral_constant<int, 0>{});
         const int after = slot == 0 ? 2 : slot - 1;
         issue(after, lc);
-        load_frags(slot, std::integral_constant<int, 1>{});
         const bool skip = sw_c == 0.0f;
         const int e8 = skip ? 0 : 127;
         float rho[FM], ref_next[FM];
@@ -328,34 +329,53 @@ __global__ void __launch_bounds__(NT, 1) gemm_fp8_ring(Fp8GemmParams P)
             ref_next[j] = dead ? ref[j] : sig;
             e8a[j] = dead ? 0 : 127;
         }
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-            for (int j = 0; j < FM; ++j) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    acc[i][j][e] *= rho[j];
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[0][i], fa[0][j], acc[i][j], 0, 0, 0, e8,
-                                                                            0, e8a[j]);
+        // Per block: its rescale (none in a tile's first stage: the
+        // accumulators start from zero there), its first-step MFMA and one of
+        // the second step's fragments read; then the second step.  Fences keep
+        // that order, so no MFMA waits for the one before it on the same block.
+        const char* sb = ring + slot * SLOT_BYTES;
+        auto read_k1 = [&](int b) __attribute__((always_inline)) {
+            if (b < FN) {
+                const char* p = sb + A_BYTES + (wn * WTN + b * 32) * ROWB;
+                fw[1][b] = join(lds_ld16(p + fr_off[1][0]), lds_ld16(p + fr_off[1][1]));
+            } else {
+                const char* p = sb + (wm * WTM + (b - FN) * 32) * ROWB;
+                fa[1][b - FN] = join(lds_ld16(p + fr_off[1][0]), lds_ld16(p + fr_off[1][1]));
             }
+        };
+        static_assert(FN + FM == FN * FM, "one second-step fragment read per block");
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks == 0) {
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) {
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[0][i], fa[0][j], f32x16{}, 0, 0, 0,
+                                                                                e8, 0, e8a[j]);
+                    read_k1(i * FM + j);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        acc[i][j][e] *= rho[j];
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[0][i], fa[0][j], acc[i][j], 0, 0, 0,
+                                                                                e8, 0, e8a[j]);
+                    read_k1(i * FM + j);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+        }
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
             for (int j = 0; j < FM; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[1][i], fa[1][j], acc[i][j], 0, 0, 0, e8,
                                                                             0, e8a[j]);
-        // Order: the scales and the first k step's fragments first, then per
-        // block its 16 rescale multiplies (run under the previous block's
-        // MFMA), its first MFMA and a share of the second k step's fragment
-        // reads, then the second k step.
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (FN + FM) + FM + 1, 0);
-#pragma unroll
-        for (int b = 0; b < FN * FM; ++b) {
-            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (FN + FM) / (FN * FM), 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, FN * FM, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < FM; ++j)
             ref[j] = ref_next[j];
