@@ -24,10 +24,10 @@
 // e4m3 cache (the collection's scale_dtype_ fp32 and quantization_granularity_
 // 128 of page "generic_flare_mla_decompress_k_cache_ragged_paged"): the same
 // fp32 values, quantised per 128-column block of the row (K % 128 == 0, so the
-// rope columns start a block): amax over the block by a 16-lane butterfly
-// (8 columns per lane), s = amax / 448 (1 for an all-zero block), codes
-// e4m3fn(y * (448 / amax)) rounded to nearest even; each lane stores its 8
-// codes, the first lane of a block stores s into the scale pool.
+// rope columns start a block): amax over the block by DPP exchanges within
+// 16 lanes (8 columns per lane), s = amax / 448 (1 for an all-zero block),
+// codes e4m3fn(y * (448 / amax)) rounded to nearest even; each lane stores
+// its 8 codes, the first lane of a block stores s into the scale pool.
 #include "launch.hpp"
 
 namespace mla {
@@ -36,32 +36,40 @@ namespace {
 constexpr int WRITE_WAVES = 4;
 constexpr int TOKENS_PER_WAVE = 2;
 
+// Sum over the 64 lanes: within each 16-lane row by DPP (the exchanges of
+// max16), then the four row sums read out of lanes 0, 16, 32 and 48.  Every
+// lane gets the same total.
 __device__ inline float wave_sum(float v)
 {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        v += __shfl_xor(v, m, 64);
-    return v;
+    v += dpp_f32<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+    v += dpp_f32<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    v += dpp_f32<0x141>(v);   // row_half_mirror
+    v += dpp_f32<0x140>(v);   // row_mirror
+    const int b = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 
-// Eight fp32 values of one 128-column block, quantised with the block's scale:
-// the 8 codes (packed little-endian) and, returned, the scale.
-__device__ inline float quantise8(const float (&y)[8], u32x2& codes)
+// Amax of one 128-column block: 8 values per lane, 16 lanes per block.
+__device__ inline float block_amax(const float (&y)[8])
 {
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         am = fmaxf(am, fabsf(y[i]));
-    am = max16(am);
-    float s = 1.0f, to_codes = 1.0f;
-    if (am > 0.0f) {
-        s = am / 448.0f;
-        to_codes = 448.0f / am;
-    }
-    codes = {pack_e4m3x2(y[0] * to_codes, y[1] * to_codes) | (pack_e4m3x2(y[2] * to_codes, y[3] * to_codes) << 16),
-             pack_e4m3x2(y[4] * to_codes, y[5] * to_codes) | (pack_e4m3x2(y[6] * to_codes, y[7] * to_codes) << 16)};
-    return s;
+    return max16(am);
+}
+
+// Eight fp32 values of a block as e4m3 codes (packed little-endian) with the
+// block's 448 / amax.
+__device__ inline u32x2 codes8(const float (&y)[8], float to_codes)
+{
+    return {pack_e4m3x2(y[0] * to_codes, y[1] * to_codes) | (pack_e4m3x2(y[2] * to_codes, y[3] * to_codes) << 16),
+            pack_e4m3x2(y[4] * to_codes, y[5] * to_codes) | (pack_e4m3x2(y[6] * to_codes, y[7] * to_codes) << 16)};
 }
 
 template <bool FP8>
@@ -190,9 +198,20 @@ __global__ void __launch_bounds__(64 * WRITE_WAVES) latent_write_kernel(LatentWr
             // K / 128 + j lanes 16 j .. of the rope part.  Lanes past the row
             // hold zeros, which leave every amax unchanged.
             float* sdst = reinterpret_cast<float*>(const_cast<char*>(a.Ls.base) + soff[k]);
-            u32x2 cl, cr;
-            const float sl = quantise8(yl, cl);
-            const float sr = quantise8(yr, cr);
+            // Scale s = amax / 448 (1 for an all-zero block) and 448 / amax of
+            // the lane's latent and rope blocks: even lanes divide for the
+            // latent block, odd lanes for the rope block, and every lane takes
+            // both results from lanes 0 and 1 of its 16-lane row (one pair of
+            // IEEE divisions per lane instead of two).
+            const float aml = block_amax(yl), amr = block_amax(yr);
+            const float am = (lane & 1) ? amr : aml;
+            float sc = 1.0f, to = 1.0f;
+            if (am > 0.0f) {
+                sc = am / 448.0f;
+                to = 448.0f / am;
+            }
+            const float sl = row16_lane(sc, 0), sr = row16_lane(sc, 1);
+            const u32x2 cl = codes8(yl, row16_lane(to, 0)), cr = codes8(yr, row16_lane(to, 1));
             if (lat) {
                 *reinterpret_cast<u32x2*>(dst + lane * 8) = cl;
                 if ((lane & 15) == 0)
