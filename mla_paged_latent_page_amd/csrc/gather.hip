@@ -8,8 +8,10 @@
 //
 // Each wave copies ROWS consecutive rows.  Lanes 0..ROWS-1 resolve one row each
 // (request by binary search, then page and slot), the offsets are broadcast
-// with readlane, and then every lane issues its 16-byte loads for all ROWS rows
-// before the first store, so ROWS loads per lane are in flight at once.
+// with readlane, and then the wave copies the rows as one flat run of 16-byte
+// granules (the destination rows are consecutive): every lane issues ROWS
+// loads before its first store, and every instruction but the last has all
+// 64 lanes busy (a row of 72 granules per lane pass would leave 56 idle).
 #include "launch.hpp"
 
 namespace mla {
@@ -58,16 +60,28 @@ __global__ void __launch_bounds__(256) gather_rows_kernel(DecompressArgs a, int 
     }
     const int64_t row_bytes = (int64_t)granules_per_row * 16;
     char* dst = static_cast<char*>(a.lat) + (int64_t)r0 * row_bytes;
-    for (int g = lane; g < granules_per_row; g += 64) {
+    // The wave's rows are consecutive in k_latent_buffer: granule f of the
+    // flat run is granule f % gpr of row f / gpr, and its destination is
+    // dst + 16 f.  Every lane has a granule in every step but the last.
+    const int total = nrows * granules_per_row;
+    for (int f0 = 0; f0 < total; f0 += 64 * ROWS) {
         u32x4 v[ROWS];
 #pragma unroll
-        for (int i = 0; i < ROWS; ++i)
-            if (i < nrows)
-                v[i] = ld16(src[i] + g * 16);
+        for (int u = 0; u < ROWS; ++u) {
+            const int f = f0 + u * 64 + lane;
+            const int i = f / granules_per_row, g = f - i * granules_per_row;
+            const char* sp = src[0];
 #pragma unroll
-        for (int i = 0; i < ROWS; ++i)
-            if (i < nrows)
-                st16(dst + i * row_bytes + g * 16, v[i]);
+            for (int k = 1; k < ROWS; ++k)
+                sp = i == k ? src[k] : sp;
+            v[u] = f < total ? ld16(sp + g * 16) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < ROWS; ++u) {
+            const int f = f0 + u * 64 + lane;
+            if (f < total)
+                st16(dst + (int64_t)f * 16, v[u]);
+        }
     }
 }
 
