@@ -46,10 +46,12 @@ def test_decode_probe_batches(newest):
 
 @pytest.mark.parametrize("lens,offs,ps", [([1], [0], 16), ([40, 1, 3], [9, 0, 2], 1), ([300, 200], [270, 199], 7),
                                           ([100, 90, 80, 70], [37, 30, 28, 11], 32), ([256], [0], 128),
-                                          ([100, 90], [5, 0], 16)])
+                                          ([100, 90], [5, 0], 16), ([50, 30], [3, 0], 16), ([97], [0], 16),
+                                          ([120, 100], [10, 0], 32), ([130, 70], [2, 5], 8)])
 def test_ragged_small_batches(lens, offs, ps):
-    """Row counts 1 .. 256, including 185 rows (the weight streamed through the
-    ring slots with the rows)."""
+    """Row counts 1 .. 256 over every row-block count (77 rows: 3 blocks of 32;
+    97: 4; 185: 6, the weight streamed through the ring slots with the rows;
+    210: 7; 193: 7 at its lower edge)."""
     case = W.decompress_case("small_m", seed=21, cache_lengths=lens, cache_offsets=offs, page_size=ps,
                              kv_lora_rank=512, rope_dim=64, N=1024)
     assert case.M <= 256
@@ -85,7 +87,7 @@ def test_selection_weight_small_exact():
     assert np.array_equal(to_bits(res["out"]), ref_lat[:, perm])
 
 
-@pytest.mark.parametrize("M", [1, 64, 150, 185, 200, 256])
+@pytest.mark.parametrize("M", [1, 33, 64, 96, 97, 128, 150, 160, 161, 185, 192, 193, 200, 224, 256])
 def test_latent_matmul_few_rows(M):
     rng = np.random.default_rng(24 + M)
     N, K, ld = 2048, 512, 576
