@@ -50,6 +50,16 @@ def test_small_bf16_full_compare(seed, ps, N):
     _check_full(case)
 
 
+@pytest.mark.parametrize("lens,offs,M", [([257], [0], 257), ([300, 256], [44, 0], 512), ([513], [0], 513)])
+def test_edges_of_the_gather_and_product_path(lens, offs, M):
+    """257 rows (the first count past the few-rows kernel), exactly 512 (two
+    whole 256-row tiles) and 513 (one row into a third tile)."""
+    case = W.decompress_case("edge_m", seed=31, cache_lengths=lens, cache_offsets=offs, page_size=16,
+                             kv_lora_rank=512, rope_dim=64, N=1024)
+    assert case.M == M
+    _check_full(case)
+
+
 def test_small_bf16_no_rope_k64_and_empty_requests():
     case = W.decompress_case("k64_empty", seed=9, cache_lengths=[40, 10, 77, 5, 300], cache_offsets=[40, 3, 0, 5, 17],
                              page_size=32, kv_lora_rank=64, rope_dim=0, N=64)
