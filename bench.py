@@ -67,6 +67,7 @@ KERNEL_SOURCES = {
     "gemm_fp8_ring": ("decompress_fp8_ring.hip", "decompress_fp8.hip", "bf16_tile_common.hpp"),
     "kv_matmul_ring": ("kv_matmul_ring.hip", "kv_matmul.hip", "bf16_tile_common.hpp"),
     "decompress_small_bf16": ("decompress_small.hip",),
+    "decompress_small_fp8": ("decompress_fp8_small.hip", "decompress_fp8.hip", "bf16_tile_common.hpp"),
     "latent_write_kernel": ("latent_write.hip",),
     "absorb_bf16": ("absorb.hip",),
     "absorb_fp8": ("absorb.hip",),
@@ -299,6 +300,35 @@ def probe_row(torch, mp, W, pc, copies=32):
                info={"rows": M, "kernel": "decompress_small_bf16 (gather + product in one launch)"})
 
 
+def fp8_probe_case(W, newest=16):
+    """C3's 4 requests, the newest `newest` tokens of each (64 rows by default),
+    against C3's e4m3 W_k: the decode-sized fp8 call."""
+    base = W.c3_fp8()
+    q = probe_case(W, base, newest)
+    return dataclasses.replace(base, name=f"p{q.M}_fp8", buffer_row_offsets=q.buffer_row_offsets,
+                               cache_offsets=q.cache_offsets)
+
+
+def probe_row_fp8(torch, mp, W, pc, copies=32):
+    """Few-rows fp8 call (the quantising gather, then the few-rows fp8 product):
+    each launch on its own copy of the 8 MiB weight."""
+    dc, t = W.device_decompress(pc)
+    M, D, N = pc.M, pc.D_c, pc.N
+    lat = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    cache = mp.PagedKVCache(dc.pool, dc.page_table, dc.cache_lengths)
+    ws = torch.empty(mp.mla_decompress_k_paged_fp8_workspace_size(M, pc.K), dtype=torch.uint8, device="cuda")
+    weights = [t["weight_q"].clone() for _ in range(copies)]
+
+    def fn(i=0):
+        mp.mla_decompress_k_paged_fp8(t["buffer_row_offsets"], t["cache_offsets"], M, weights[i % copies],
+                                      t["weight_scale"], cache, pc.layer_idx, lat, out, ws)
+    f, b = decompress_costs(pc)
+    return Row(fn, "decompress_small_fp8", f, b, "hbm", PEAK_HBM_GBS, copies=copies,
+               check=lambda: out.view(torch.int16).clone(),
+               info={"rows": M, "kernel": "gather_quant_fp8_kernel, then decompress_small_fp8 (two launches)"})
+
+
 def absorb_row(torch, mp, W, fp8, copies=32):
     c = W.c7_absorb_fp8() if fp8 else W.c7_absorb()
     t = W.device_absorb(c)
@@ -468,12 +498,14 @@ def build_row(name, torch, mp, W):
         return absorb_row(torch, mp, W, name.endswith("fp8"))
     if name in ("p64", "p256"):
         return probe_row(torch, mp, W, probe_case(W, W.c1_decode(), 1 if name == "p64" else 4))
+    if name == "p64_fp8":
+        return probe_row_fp8(torch, mp, W, fp8_probe_case(W))
     if name == "copy":
         return copy_row(torch)
     raise SystemExit(f"unknown row {name}")
 
 
-OTHER_ROWS = ("p64", "p256", "c2_prefill", "c3_fp8", "c6_fp8_cache", "c6_fused_kv_fp8_cache", "c2_fused_kv",
+OTHER_ROWS = ("p64", "p256", "p64_fp8", "c2_prefill", "c3_fp8", "c6_fp8_cache", "c6_fused_kv_fp8_cache", "c2_fused_kv",
               "c2_tp8_share", "c4_kv_matmul", "c5_latent_write", "c5_latent_write_fp8", "c7_absorb", "c7_absorb_fp8")
 PROFILE_ROWS = ("c1_decode", "c1_product", "c1_gather") + OTHER_ROWS + ("copy",)
 
@@ -618,7 +650,7 @@ def _kernel_of(row_name):
             "c3_fp8": "gemm_fp8_ring", "c6_fp8_cache": "gemm_fp8_ring", "c6_fused_kv_fp8_cache": "gemm_fp8_ring",
             "c4_kv_matmul": "kv_matmul_ring", "c5_latent_write": "latent_write_kernel",
             "c5_latent_write_fp8": "latent_write_kernel", "c7_absorb": "absorb_bf16", "c7_absorb_fp8": "absorb_fp8",
-            "p64": "decompress_small_bf16", "p256": "decompress_small_bf16",
+            "p64": "decompress_small_bf16", "p256": "decompress_small_bf16", "p64_fp8": "decompress_small_fp8",
             "copy": "__amd_rocclr_copyBuffer"}[row_name]
 
 
@@ -895,6 +927,8 @@ def _alg_bytes_host(row_name, W):
         return wb + T * H * Dq * 2 + T * H * c.out_dim * 2
     if row_name in ("p64", "p256"):
         return decompress_costs(probe_case(W, W.c1_decode(), 1 if row_name == "p64" else 4))[1]
+    if row_name == "p64_fp8":
+        return fp8_product(fp8_probe_case(W), 16384)
     raise SystemExit(f"no algorithmic bytes for {row_name}")
 
 

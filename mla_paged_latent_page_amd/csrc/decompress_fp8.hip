@@ -115,7 +115,8 @@ hipError_t launch_decompress_fp8(const DecompressArgs& a, hipStream_t s)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    return launch_product_fp8_ring(first_projection(a), num_cus(), s);
+    const DecompressArgs p = first_projection(a);
+    return small_fp8_fits(p) ? launch_small_fp8(p, s) : launch_product_fp8_ring(p, num_cus(), s);
 }
 
 // fp8 cache: the gather copies each row's codes and scales bit for bit into
@@ -132,7 +133,7 @@ hipError_t launch_decompress_fp8_cache(const DecompressArgs& a, hipStream_t s)
     p.q_scale = a.lat_scale;
     p.q_ld = a.D;
     p.qs_ld = a.nblk;
-    return launch_product_fp8_ring(p, num_cus(), s);
+    return small_fp8_fits(p) ? launch_small_fp8(p, s) : launch_product_fp8_ring(p, num_cus(), s);
 }
 
 // Fused K and V (fp8): one gather and quantisation pass, then one product

@@ -121,5 +121,9 @@ bool small_bf16_fits(const DecompressArgs& a);
 void log_launch(const char* kernel, unsigned grid, unsigned block, const char* fmt, ...)
     __attribute__((format(printf, 4, 5)));
 hipError_t launch_small_bf16(const DecompressArgs& a, int gather, hipStream_t s);
+// Few-rows fp8 product (at most 192 rows, K = 512, one projection) from the
+// activation codes and scales in a.q / a.q_scale.
+bool small_fp8_fits(const DecompressArgs& a);
+hipError_t launch_small_fp8(const DecompressArgs& a, hipStream_t s);
 
 }  // namespace mla

@@ -6,6 +6,8 @@ round-to-nearest-even), so they must match the oracle bit for bit; gathered
 rows bit for bit; k_buffer within 3e-2 * max|ref| of the oracle's block-scaled
 product.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -46,6 +48,29 @@ def _check(case, rows=None):
 @pytest.mark.parametrize("seed,ps,N", [(0, 16, 512), (1, 128, 1024), (2, 5, 256)])
 def test_small_fp8_full_compare(seed, ps, N):
     case = W.small_decompress(seed, batch=5, max_len=400, page_size=ps, K=512, rope=64, N=N, fp8=True)
+    _check(case)
+
+
+@pytest.mark.parametrize("lens,offs,N", [([1], [0], 256), ([31], [0], 512), ([40, 24], [5, 0], 1024), ([97], [3], 256),
+                                         ([100, 60, 30], [0, 10, 2], 512), ([192], [0], 256), ([193], [0], 256)])
+def test_few_rows_fp8(lens, offs, N):
+    """Decode-sized calls: up to 192 rows go to the few-rows product (1, 31,
+    59, 94, 178 and 192 rows); 193 is the first count past it."""
+    case = W.decompress_case("fp8_few", seed=41, cache_lengths=lens, cache_offsets=offs, page_size=16,
+                             kv_lora_rank=512, rope_dim=64, N=N, fp8=True)
+    _check(case)
+
+
+def test_fp8_decode_probe_full_width():
+    """The newest 16 tokens of each of C3's 4 requests (64 rows) against the
+    whole 16384-row e4m3 weight."""
+    base = W.c3_fp8()
+    lens = base.cache.cache_lengths.astype(np.int64)
+    bro = np.zeros(len(lens) + 1, np.uint32)
+    bro[1:] = np.cumsum(np.full(len(lens), 16))
+    case = dataclasses.replace(base, name="fp8_probe64", buffer_row_offsets=bro,
+                               cache_offsets=(lens - 16).astype(np.uint32))
+    assert case.M == 64
     _check(case)
 
 

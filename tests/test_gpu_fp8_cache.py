@@ -150,13 +150,25 @@ def test_k_and_v_from_the_fp8_cache_at_full_size_sampled():
     check_close(rows_as_f64(vout, rows, M), v, BF16_TOL, "c6 v_buffer (fused, sampled rows)")
 
 
-def test_zero_activation_scales():
+@pytest.mark.parametrize("lens,offs,N", [([1], [0], 128), ([64, 64], [0, 32], 512), ([150, 42], [0, 0], 1024),
+                                         ([193], [0], 256)])
+def test_few_rows_fp8_cache(lens, offs, N):
+    """Decode-sized calls on the e4m3 cache (1, 96 and 192 rows: the few-rows
+    product; 193: the large one)."""
+    _check(W.decompress_case("fp8c_few", seed=42, cache_lengths=lens, cache_offsets=offs, page_size=16,
+                             kv_lora_rank=512, rope_dim=64, N=N, dtype="e4m3", fp8=True))
+
+
+@pytest.mark.parametrize("max_len", [300, 60])
+def test_zero_activation_scales(max_len):
     """Scale blocks of 0 in the cache (a writer may store s = 0 for an all-zero
     block): a zero block after a non-zero one, a zero first block, and a row
     whose every block is zero.  The oracle's value for such a block is exactly
     0 * (its code sum); the product must stay finite and within the bound, and
-    the all-zero row must come out as zeros."""
-    case = _fp8_case(31, batch=4, max_len=300, page_size=16, K=512, rope=64, N=512)
+    the all-zero row must come out as zeros.  Long requests take the large
+    product, short ones (at most 192 rows) the few-rows one."""
+    case = _fp8_case(31, batch=4, max_len=max_len, page_size=16, K=512, rope=64, N=512)
+    assert (case.M > 192) == (max_len == 300)
     c = case.cache
     rng = np.random.default_rng(31)
     sc = c.scales.copy()
