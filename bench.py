@@ -67,7 +67,7 @@ KERNEL_SOURCES = {
     "gemm_fp8_ring": ("decompress_fp8_ring.hip", "decompress_fp8.hip", "bf16_tile_common.hpp"),
     "kv_matmul_ring": ("kv_matmul_ring.hip", "kv_matmul.hip", "bf16_tile_common.hpp"),
     "decompress_small_bf16": ("decompress_small.hip",),
-    "decompress_small_fp8": ("decompress_fp8_small.hip", "decompress_fp8.hip", "bf16_tile_common.hpp"),
+    "decompress_small_fp8_gq": ("decompress_fp8_small.hip", "decompress_fp8.hip", "bf16_tile_common.hpp"),
     "latent_write_kernel": ("latent_write.hip",),
     "absorb_bf16": ("absorb.hip",),
     "absorb_fp8": ("absorb.hip",),
@@ -310,8 +310,8 @@ def fp8_probe_case(W, newest=16):
 
 
 def probe_row_fp8(torch, mp, W, pc, copies=32):
-    """Few-rows fp8 call (the quantising gather, then the few-rows fp8 product):
-    each launch on its own copy of the 8 MiB weight."""
+    """Few-rows fp8 call (gather, quantisation and product in one launch): each
+    launch on its own copy of the 8 MiB weight."""
     dc, t = W.device_decompress(pc)
     M, D, N = pc.M, pc.D_c, pc.N
     lat = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
@@ -324,9 +324,9 @@ def probe_row_fp8(torch, mp, W, pc, copies=32):
         mp.mla_decompress_k_paged_fp8(t["buffer_row_offsets"], t["cache_offsets"], M, weights[i % copies],
                                       t["weight_scale"], cache, pc.layer_idx, lat, out, ws)
     f, b = decompress_costs(pc)
-    return Row(fn, "decompress_small_fp8", f, b, "hbm", PEAK_HBM_GBS, copies=copies,
+    return Row(fn, "decompress_small_fp8_gq", f, b, "hbm", PEAK_HBM_GBS, copies=copies,
                check=lambda: out.view(torch.int16).clone(),
-               info={"rows": M, "kernel": "gather_quant_fp8_kernel, then decompress_small_fp8 (two launches)"})
+               info={"rows": M, "kernel": "decompress_small_fp8_gq (gather, quantisation and product in one launch)"})
 
 
 def absorb_row(torch, mp, W, fp8, copies=32):
@@ -650,7 +650,7 @@ def _kernel_of(row_name):
             "c3_fp8": "gemm_fp8_ring", "c6_fp8_cache": "gemm_fp8_ring", "c6_fused_kv_fp8_cache": "gemm_fp8_ring",
             "c4_kv_matmul": "kv_matmul_ring", "c5_latent_write": "latent_write_kernel",
             "c5_latent_write_fp8": "latent_write_kernel", "c7_absorb": "absorb_bf16", "c7_absorb_fp8": "absorb_fp8",
-            "p64": "decompress_small_bf16", "p256": "decompress_small_bf16", "p64_fp8": "decompress_small_fp8",
+            "p64": "decompress_small_bf16", "p256": "decompress_small_bf16", "p64_fp8": "decompress_small_fp8_gq",
             "copy": "__amd_rocclr_copyBuffer"}[row_name]
 
 

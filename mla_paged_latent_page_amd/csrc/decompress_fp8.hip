@@ -110,6 +110,8 @@ inline int quant_blocks(int M) { return (M + 4 * QROWS - 1) / (4 * QROWS); }
 
 hipError_t launch_decompress_fp8(const DecompressArgs& a, hipStream_t s)
 {
+    if (small_fp8_gq_fits(first_projection(a)))
+        return launch_small_fp8_gq(first_projection(a), s);
     log_launch("gather_quant_fp8_kernel", quant_blocks(a.M), 256, "M=%d K=%d D=%d", a.M, a.K, a.D);
     hipLaunchKernelGGL(gather_quant_fp8_kernel, dim3(quant_blocks(a.M)), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();

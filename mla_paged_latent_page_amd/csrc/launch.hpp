@@ -125,5 +125,9 @@ hipError_t launch_small_bf16(const DecompressArgs& a, int gather, hipStream_t s)
 // activation codes and scales in a.q / a.q_scale.
 bool small_fp8_fits(const DecompressArgs& a);
 hipError_t launch_small_fp8(const DecompressArgs& a, hipStream_t s);
+// At most 64 rows from a bf16 cache gathered, quantised and multiplied in one
+// launch (K = 512, one projection); the workspace codes and scales are written too.
+bool small_fp8_gq_fits(const DecompressArgs& a);
+hipError_t launch_small_fp8_gq(const DecompressArgs& a, hipStream_t s);
 
 }  // namespace mla
