@@ -68,6 +68,7 @@ KERNEL_SOURCES = {
     "kv_matmul_ring": ("kv_matmul_ring.hip", "kv_matmul.hip", "bf16_tile_common.hpp"),
     "decompress_small_bf16": ("decompress_small.hip",),
     "decompress_small_fp8_gq": ("decompress_fp8_small.hip", "decompress_fp8.hip", "bf16_tile_common.hpp"),
+    "decompress_small_fp8_gc": ("decompress_fp8_small.hip", "decompress_fp8.hip", "bf16_tile_common.hpp"),
     "latent_write_kernel": ("latent_write.hip",),
     "absorb_bf16": ("absorb.hip",),
     "absorb_fp8": ("absorb.hip",),
@@ -329,6 +330,42 @@ def probe_row_fp8(torch, mp, W, pc, copies=32):
                info={"rows": M, "kernel": "decompress_small_fp8_gq (gather, quantisation and product in one launch)"})
 
 
+def fp8_cache_probe_case(W, newest=16):
+    """C6's 4 requests, the newest `newest` tokens of each (64 rows by default),
+    from its e4m3 cache: the decode-sized fp8-cache call."""
+    base = W.c6_fp8_cache()
+    q = probe_case(W, base, newest)
+    return dataclasses.replace(base, name=f"p{q.M}_fp8_cache", buffer_row_offsets=q.buffer_row_offsets,
+                               cache_offsets=q.cache_offsets)
+
+
+def fp8_cache_call_bytes(c):
+    """One fp8-cache call: each row's codes and scales read and written, its
+    k_buffer row written, the weight codes and scales read once."""
+    return c.M * (2 * (c.D_c + c.cache.scale_blocks * 4) + c.N * 2) + c.N * c.K + c.weight_scale.nbytes
+
+
+def probe_row_fp8_cache(torch, mp, W, pc, copies=32):
+    """Few-rows call on the e4m3 cache (codes and scales gathered into the
+    product's LDS layout and multiplied in one launch): each launch on its own
+    copy of the 8 MiB weight."""
+    dc, t = W.device_decompress(pc)
+    M, N = pc.M, pc.N
+    lat = torch.empty((M, pc.D_c), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((M, pc.cache.scale_blocks), dtype=torch.float32, device="cuda")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    cache = mp.PagedKVCache(dc.pool, dc.page_table, dc.cache_lengths, scales=dc.scales)
+    weights = [t["weight_q"].clone() for _ in range(copies)]
+
+    def fn(i=0):
+        mp.mla_decompress_k_paged_fp8_cache(t["buffer_row_offsets"], t["cache_offsets"], M, weights[i % copies],
+                                            t["weight_scale"], cache, pc.layer_idx, lat, sc, out)
+    return Row(fn, "decompress_small_fp8_gc", 2.0 * M * N * pc.K, fp8_cache_call_bytes(pc), "hbm", PEAK_HBM_GBS,
+               copies=copies, check=lambda: out.view(torch.int16).clone(),
+               info={"rows": M, "kernel": "decompress_small_fp8_gc (codes and scales gathered and multiplied in "
+                                          "one launch)"})
+
+
 def absorb_row(torch, mp, W, fp8, copies=32):
     c = W.c7_absorb_fp8() if fp8 else W.c7_absorb()
     t = W.device_absorb(c)
@@ -500,13 +537,15 @@ def build_row(name, torch, mp, W):
         return probe_row(torch, mp, W, probe_case(W, W.c1_decode(), 1 if name == "p64" else 4))
     if name == "p64_fp8":
         return probe_row_fp8(torch, mp, W, fp8_probe_case(W))
+    if name == "p64_fp8_cache":
+        return probe_row_fp8_cache(torch, mp, W, fp8_cache_probe_case(W))
     if name == "copy":
         return copy_row(torch)
     raise SystemExit(f"unknown row {name}")
 
 
-OTHER_ROWS = ("p64", "p256", "p64_fp8", "c2_prefill", "c3_fp8", "c6_fp8_cache", "c6_fused_kv_fp8_cache", "c2_fused_kv",
-              "c2_tp8_share", "c4_kv_matmul", "c5_latent_write", "c5_latent_write_fp8", "c7_absorb", "c7_absorb_fp8")
+OTHER_ROWS = ("p64", "p256", "p64_fp8", "p64_fp8_cache", "c2_prefill", "c3_fp8", "c6_fp8_cache",
+              "c6_fused_kv_fp8_cache", "c2_fused_kv", "c2_tp8_share", "c4_kv_matmul", "c5_latent_write", "c5_latent_write_fp8", "c7_absorb", "c7_absorb_fp8")
 PROFILE_ROWS = ("c1_decode", "c1_product", "c1_gather") + OTHER_ROWS + ("copy",)
 
 
@@ -650,7 +689,7 @@ def _kernel_of(row_name):
             "c3_fp8": "gemm_fp8_ring", "c6_fp8_cache": "gemm_fp8_ring", "c6_fused_kv_fp8_cache": "gemm_fp8_ring",
             "c4_kv_matmul": "kv_matmul_ring", "c5_latent_write": "latent_write_kernel",
             "c5_latent_write_fp8": "latent_write_kernel", "c7_absorb": "absorb_bf16", "c7_absorb_fp8": "absorb_fp8",
-            "p64": "decompress_small_bf16", "p256": "decompress_small_bf16", "p64_fp8": "decompress_small_fp8_gq",
+            "p64": "decompress_small_bf16", "p256": "decompress_small_bf16", "p64_fp8": "decompress_small_fp8_gq", "p64_fp8_cache": "decompress_small_fp8_gc",
             "copy": "__amd_rocclr_copyBuffer"}[row_name]
 
 
@@ -929,6 +968,8 @@ def _alg_bytes_host(row_name, W):
         return decompress_costs(probe_case(W, W.c1_decode(), 1 if row_name == "p64" else 4))[1]
     if row_name == "p64_fp8":
         return fp8_product(fp8_probe_case(W), 16384)
+    if row_name == "p64_fp8_cache":
+        return fp8_cache_call_bytes(fp8_cache_probe_case(W))
     raise SystemExit(f"no algorithmic bytes for {row_name}")
 
 

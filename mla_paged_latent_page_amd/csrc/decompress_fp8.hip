@@ -127,6 +127,8 @@ hipError_t launch_decompress_fp8(const DecompressArgs& a, hipStream_t s)
 // there is no quantisation pass.
 hipError_t launch_decompress_fp8_cache(const DecompressArgs& a, hipStream_t s)
 {
+    if (small_fp8_gc_fits(a))
+        return launch_small_fp8_gc(a, s);
     const hipError_t e = launch_gather_rows(a, 1, s);
     if (e != hipSuccess)
         return e;

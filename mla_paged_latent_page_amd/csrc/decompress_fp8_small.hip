@@ -282,8 +282,8 @@ constexpr int fg_late_chunks()
     return n;
 }
 
-template <int MB>
-__global__ void __launch_bounds__(FS_NT, 1) decompress_small_fp8_gq(DecompressArgs a)
+template <int MB, bool CACHE8>
+__device__ inline void fg_body(const DecompressArgs& a)
 {
     constexpr int ROWS = 32 * MB;
     constexpr int RB = ROWS * 256;            // one scale block of every row, bf16
@@ -296,6 +296,7 @@ __global__ void __launch_bounds__(FS_NT, 1) decompress_small_fp8_gq(DecompressAr
     __shared__ __attribute__((aligned(1024))) char xs[FG_XS_BYTES];
     __shared__ __attribute__((aligned(256))) float sa[FS_KB][ROWS];
     __shared__ __attribute__((aligned(16))) uint64_t rowaddr[ROWS];
+    __shared__ __attribute__((aligned(16))) uint64_t scaleaddr[ROWS];   // e4m3 cache: the rows' scales
     __shared__ uint32_t row_req[ROWS], row_pos[ROWS];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -370,6 +371,10 @@ __global__ void __launch_bounds__(FS_NT, 1) decompress_small_fp8_gq(DecompressAr
             const uint32_t pg = pgv < L.num_pages ? pgv : L.num_pages - 1;
             const int64_t off = valid ? (int64_t)pg * L.stride_page + (int64_t)slot * L.stride_token : 0;
             rowaddr[r] = (uint64_t)(L.base + off);
+            if constexpr (CACHE8) {
+                const int64_t soff = valid ? (int64_t)pg * a.Ls.stride_page + (int64_t)slot * a.Ls.stride_token : 0;
+                scaleaddr[r] = (uint64_t)(a.Ls.base + soff);
+            }
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);
     } else {
@@ -385,11 +390,25 @@ __global__ void __launch_bounds__(FS_NT, 1) decompress_small_fp8_gq(DecompressAr
     //    4 c .. 4 c + 3, 256 bytes of scale block kb each), and wave 3's
     //    k_latent_buffer copies.
     if (wave < 3) {
-        for (int t = wave; t < FS_KB * (ROWS / 4); t += 3) {
-            const int kb = t / (ROWS / 4), c = t - kb * (ROWS / 4);
-            const int r = 4 * c + (lane >> 4);
-            const char* src = reinterpret_cast<const char*>(rowaddr[r]) + kb * 256 + (lane & 15) * 16;
-            asm_gld16_lds(src, lds_addr(xs) + kb * RB + c * 1024);
+        if constexpr (CACHE8) {
+            // e4m3 rows: the codes straight into the product's layout
+            // (instruction t = (ROWS / 8) kb + c: rows 8 c .. 8 c + 7, lane l
+            // filling position l % 8 of row 8 c + l / 8 with its logical
+            // granule (l % 8) ^ ((row / 2) % 8) of scale block kb).
+            for (int t = wave; t < FS_KB * (ROWS / 8); t += 3) {
+                const int kb = t / (ROWS / 8), c = t - kb * (ROWS / 8);
+                const int r = 8 * c + (lane >> 3);
+                const int g = (lane & 7) ^ ((r >> 1) & 7);
+                const char* src = reinterpret_cast<const char*>(rowaddr[r]) + kb * FS_ROWB + g * 16;
+                asm_gld16_lds(src, lds_addr(aq[kb]) + c * 1024);
+            }
+        } else {
+            for (int t = wave; t < FS_KB * (ROWS / 4); t += 3) {
+                const int kb = t / (ROWS / 4), c = t - kb * (ROWS / 4);
+                const int r = 4 * c + (lane >> 4);
+                const char* src = reinterpret_cast<const char*>(rowaddr[r]) + kb * 256 + (lane & 15) * 16;
+                asm_gld16_lds(src, lds_addr(xs) + kb * RB + c * 1024);
+            }
         }
         const int t0 = 8 * E + (wave - 8 * E % 3 + 3) % 3;
         for (int t = t0; t < FG_W_CHUNKS; t += 3)
@@ -401,68 +420,85 @@ __global__ void __launch_bounds__(FS_NT, 1) decompress_small_fp8_gq(DecompressAr
         default: fs_vm_wait<fg_late_chunks<E, 2>()>(); break;
         }
     } else {
-        const int gpr = a.D / 8;                 // 16-byte granules per cache row
+        constexpr int EB = CACHE8 ? 1 : 2;       // bytes per cache element
+        if constexpr (CACHE8) {
+            // The rows' scales of the first K columns, one row per lane.
+            if (lane < ROWS) {
+                const float* sp = reinterpret_cast<const float*>(scaleaddr[lane]);
+#pragma unroll
+                for (int kb = 0; kb < FS_KB; ++kb)
+                    sa[kb][lane] = sp[kb];
+            }
+        }
+        const int gpr = a.D * EB / 16;           // 16-byte granules per cache row
         for (int r = blockIdx.x; r < M; r += grid) {
             const char* src = reinterpret_cast<const char*>(rowaddr[r]);
-            char* dst = static_cast<char*>(a.lat) + (int64_t)r * a.D * 2;
+            char* dst = static_cast<char*>(a.lat) + (int64_t)r * a.D * EB;
             for (int g = lane; g < gpr; g += 64)
                 st16(dst + g * 16, ld16(src + g * 16));
+            if constexpr (CACHE8) {
+                const float* sp = reinterpret_cast<const float*>(scaleaddr[r]);
+                for (int j = lane; j < a.nblk; j += 64)
+                    a.lat_scale[(int64_t)r * a.nblk + j] = sp[j];
+            }
         }
     }
     lds_barrier();
 
-    // 3. Quantisation: lanes 16 k .. 16 k + 15 of wave w hold row
-    //    16 p + 4 w + k of scale block kb, 8 values each.
-    const int lg = lane & 15, lr = lane >> 4;
-    u32x4 qv[FS_KB][NP];
-#pragma unroll
-    for (int kb = 0; kb < FS_KB; ++kb)
-#pragma unroll
-        for (int p = 0; p < NP; ++p)
-            qv[kb][p] = lds_ld16(xs + kb * RB + (16 * p + 4 * wave + lr) * 256 + lg * 16);
-    float my_am = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < FS_KB; ++kb)
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const u32x4 v = qv[kb][p];
-            float am = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                am = fmaxf(am, fmaxf(fabsf(bf16_lo(v[i])), fabsf(bf16_hi(v[i]))));
-            am = max16(am);
-            my_am = lg % NU == kb * NP + p ? am : my_am;
-        }
-    float my_s = 1.0f, my_inv = 1.0f;
-    if (my_am > 0.0f) {
-        my_s = my_am / 448.0f;
-        my_inv = 448.0f / my_am;
-    }
-#pragma unroll
-    for (int kb = 0; kb < FS_KB; ++kb)
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int r = 16 * p + 4 * wave + lr;
-            const u32x4 v = qv[kb][p];
-            float x[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[2 * i] = bf16_lo(v[i]);
-                x[2 * i + 1] = bf16_hi(v[i]);
+    if constexpr (!CACHE8) {
+        // 3. Quantisation: lanes 16 k .. 16 k + 15 of wave w hold row
+        //    16 p + 4 w + k of scale block kb, 8 values each.
+        const int lg = lane & 15, lr = lane >> 4;
+        u32x4 qv[FS_KB][NP];
+    #pragma unroll
+        for (int kb = 0; kb < FS_KB; ++kb)
+    #pragma unroll
+            for (int p = 0; p < NP; ++p)
+                qv[kb][p] = lds_ld16(xs + kb * RB + (16 * p + 4 * wave + lr) * 256 + lg * 16);
+        float my_am = 0.0f;
+    #pragma unroll
+        for (int kb = 0; kb < FS_KB; ++kb)
+    #pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const u32x4 v = qv[kb][p];
+                float am = 0.0f;
+    #pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    am = fmaxf(am, fmaxf(fabsf(bf16_lo(v[i])), fabsf(bf16_hi(v[i]))));
+                am = max16(am);
+                my_am = lg % NU == kb * NP + p ? am : my_am;
             }
-            const float inv = row16_lane(my_inv, kb * NP + p);
-            const u32x2 codes = {pack_e4m3x2(x[0] * inv, x[1] * inv) | (pack_e4m3x2(x[2] * inv, x[3] * inv) << 16),
-                                 pack_e4m3x2(x[4] * inv, x[5] * inv) | (pack_e4m3x2(x[6] * inv, x[7] * inv) << 16)};
-            lds_st8(aq[kb] + r * FS_ROWB + (((lg >> 1) ^ ((r >> 1) & 7)) * 16) + (lg & 1) * 8, codes);
-            const float sq = row16_lane(my_s, kb * NP + p);
-            if (lg == 0)
-                sa[kb][r] = sq;
+        float my_s = 1.0f, my_inv = 1.0f;
+        if (my_am > 0.0f) {
+            my_s = my_am / 448.0f;
+            my_inv = 448.0f / my_am;
         }
+    #pragma unroll
+        for (int kb = 0; kb < FS_KB; ++kb)
+    #pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int r = 16 * p + 4 * wave + lr;
+                const u32x4 v = qv[kb][p];
+                float x[8];
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x[2 * i] = bf16_lo(v[i]);
+                    x[2 * i + 1] = bf16_hi(v[i]);
+                }
+                const float inv = row16_lane(my_inv, kb * NP + p);
+                const u32x2 codes = {pack_e4m3x2(x[0] * inv, x[1] * inv) | (pack_e4m3x2(x[2] * inv, x[3] * inv) << 16),
+                                     pack_e4m3x2(x[4] * inv, x[5] * inv) | (pack_e4m3x2(x[6] * inv, x[7] * inv) << 16)};
+                lds_st8(aq[kb] + r * FS_ROWB + (((lg >> 1) ^ ((r >> 1) & 7)) * 16) + (lg & 1) * 8, codes);
+                const float sq = row16_lane(my_s, kb * NP + p);
+                if (lg == 0)
+                    sa[kb][r] = sq;
+            }
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);       // the rest of the weight has landed
     lds_barrier();
 
     // Wave 3: its own rows' codes and scales into the workspace.
-    if (wave == 3) {
+    if (!CACHE8 && wave == 3) {
         for (int r = blockIdx.x; r < M; r += grid) {
             if (lane < 32) {
                 const int kb = lane >> 3, g = lane & 7;
@@ -484,6 +520,22 @@ __global__ void __launch_bounds__(FS_NT, 1) decompress_small_fp8_gq(DecompressAr
     auto wscale = [&](int kb) __attribute__((always_inline)) { return ws_row[kb]; };
     fs_product<MB>(acc, ref, wq, aq, sa, ready, wscale, wave, lane);
     fs_store<MB>(acc, ref, xs, a, n0, wave, lane);
+}
+
+template <int MB>
+__global__ void __launch_bounds__(FS_NT, 1) decompress_small_fp8_gq(DecompressArgs a)
+{
+    fg_body<MB, false>(a);
+}
+
+// The same call on an e4m3 cache: the rows' codes go straight into the
+// product's layout and their scales into LDS (no quantisation); block b
+// copies rows b, b + grid, ... and their scales into k_latent_buffer and
+// k_latent_scales.
+template <int MB>
+__global__ void __launch_bounds__(FS_NT, 1) decompress_small_fp8_gc(DecompressArgs a)
+{
+    fg_body<MB, true>(a);
 }
 
 }  // namespace
@@ -530,6 +582,25 @@ hipError_t launch_small_fp8_gq(const DecompressArgs& a, hipStream_t s)
         hipLaunchKernelGGL(decompress_small_fp8_gq<1>, grid, block, 0, s, a);
     else
         hipLaunchKernelGGL(decompress_small_fp8_gq<2>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+bool small_fp8_gc_fits(const DecompressArgs& a)
+{
+    return a.M >= 1 && a.M <= FG_MAX_ROWS && a.K == FS_K && a.N % 128 == 0 && a.N2 == 0 && a.D % 16 == 0 &&
+           a.D >= FS_K && a.lat_scale != nullptr && a.nblk >= FS_KB;
+}
+
+// The rows' codes and scales from the e4m3 cache (a.L, a.Ls); k_latent_buffer,
+// k_latent_scales and k_buffer written.
+hipError_t launch_small_fp8_gc(const DecompressArgs& a, hipStream_t s)
+{
+    const dim3 grid(a.N / FS_N), block(FS_NT);
+    log_launch("decompress_small_fp8_gc", grid.x, block.x, "M=%d N=%d K=%d D=%d", a.M, a.N, a.K, a.D);
+    if (a.M <= 32)
+        hipLaunchKernelGGL(decompress_small_fp8_gc<1>, grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL(decompress_small_fp8_gc<2>, grid, block, 0, s, a);
     return hipGetLastError();
 }
 

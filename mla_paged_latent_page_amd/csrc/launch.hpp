@@ -129,5 +129,9 @@ hipError_t launch_small_fp8(const DecompressArgs& a, hipStream_t s);
 // launch (K = 512, one projection); the workspace codes and scales are written too.
 bool small_fp8_gq_fits(const DecompressArgs& a);
 hipError_t launch_small_fp8_gq(const DecompressArgs& a, hipStream_t s);
+// The same for at most 64 rows of an e4m3 cache (codes and scales gathered, no
+// quantisation).
+bool small_fp8_gc_fits(const DecompressArgs& a);
+hipError_t launch_small_fp8_gc(const DecompressArgs& a, hipStream_t s);
 
 }  // namespace mla

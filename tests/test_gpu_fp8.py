@@ -61,20 +61,25 @@ def test_few_rows_fp8(lens, offs, N):
     _check(case)
 
 
-@pytest.mark.parametrize("lens,offs,rows,ps,N", [
-    ([1], [0], None, 16, 128),                 # one row, two weight tiles
-    ([32], [0], None, 16, 256),                # 32 rows (one row block); every block writes 8 rows' copies
-    ([21, 15], [3, 0], None, 1, 512),          # 33 rows (two row blocks), one token per page
-    ([5] * 70, [4] * 70, [1] * 64 + [0] * 6, 2, 384),   # 70 requests (two rounds of offsets), 64 rows
-    ([20000, 30], [19980, 0], None, 1, 256),   # a 40,000-entry page table (looked up in memory)
-    ([65], [0], None, 16, 256),                # 65 rows: past the one-launch form
-])
-def test_one_launch_fp8_decode(lens, offs, rows, ps, N):
+ONE_LAUNCH_CASES = [
+    ([1], [0], None, 16, 128, 64),             # one row, two weight tiles
+    ([32], [0], None, 16, 256, 64),            # 32 rows (one row block); every block writes 8 rows' copies
+    ([21, 15], [3, 0], None, 1, 512, 64),      # 33 rows (two row blocks), one token per page
+    ([5] * 70, [4] * 70, [1] * 64 + [0] * 6, 2, 384, 64),   # 70 requests (two rounds of offsets), 64 rows
+    ([20000, 30], [19980, 0], None, 1, 256, 64),            # a 40,000-entry page table (looked up in memory)
+    ([40, 9], [0, 2], None, 16, 256, 0),       # rows of exactly the 512 latent columns
+    ([40, 9], [0, 2], None, 16, 256, 128),     # 640-column rows
+    ([65], [0], None, 16, 256, 64),            # 65 rows: past the one-launch form
+]
+
+
+@pytest.mark.parametrize("lens,offs,rows,ps,N,rope", ONE_LAUNCH_CASES)
+def test_one_launch_fp8_decode(lens, offs, rows, ps, N, rope):
     """Up to 64 rows from a bf16 cache are gathered, quantised and multiplied in
     one launch: rows, workspace codes and scales must match the oracle as for
     the two-launch form."""
     case = W.decompress_case("fp8_one_launch", seed=43, cache_lengths=lens, cache_offsets=offs, rows=rows,
-                             page_size=ps, kv_lora_rank=512, rope_dim=64, N=N, fp8=True)
+                             page_size=ps, kv_lora_rank=512, rope_dim=rope, N=N, fp8=True)
     assert case.M == (sum(rows) if rows else sum(l - o for l, o in zip(lens, offs)))
     # an all-zero latent block (scale 1, zero codes) in the first row
     c = case.cache

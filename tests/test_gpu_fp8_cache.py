@@ -159,16 +159,36 @@ def test_few_rows_fp8_cache(lens, offs, N):
                              kv_lora_rank=512, rope_dim=64, N=N, dtype="e4m3", fp8=True))
 
 
-@pytest.mark.parametrize("max_len", [300, 60])
+@pytest.mark.parametrize("lens,offs,rows,ps,N,rope", [
+    ([1], [0], None, 16, 128, 64),
+    ([32], [0], None, 16, 256, 64),
+    ([21, 15], [3, 0], None, 1, 512, 64),
+    ([5] * 70, [4] * 70, [1] * 64 + [0] * 6, 2, 384, 64),
+    ([20000, 30], [19980, 0], None, 1, 256, 64),
+    ([40, 9], [0, 2], None, 16, 256, 0),
+    ([40, 9], [0, 2], None, 16, 256, 128),
+    ([65], [0], None, 16, 256, 64),
+])
+def test_one_launch_fp8_cache_decode(lens, offs, rows, ps, N, rope):
+    """Up to 64 rows of the e4m3 cache: codes and scales gathered into the
+    product's LDS layout and multiplied in one launch (1, 32, 33 and 64 rows,
+    70 requests, a 40,000-entry page table, 512- and 640-column rows); 65 rows
+    take the two-launch form."""
+    _check(W.decompress_case("fp8c_one_launch", seed=44, cache_lengths=lens, cache_offsets=offs, rows=rows,
+                             page_size=ps, kv_lora_rank=512, rope_dim=rope, N=N, dtype="e4m3", fp8=True))
+
+
+@pytest.mark.parametrize("max_len", [300, 60, 14])
 def test_zero_activation_scales(max_len):
     """Scale blocks of 0 in the cache (a writer may store s = 0 for an all-zero
     block): a zero block after a non-zero one, a zero first block, and a row
     whose every block is zero.  The oracle's value for such a block is exactly
     0 * (its code sum); the product must stay finite and within the bound, and
     the all-zero row must come out as zeros.  Long requests take the large
-    product, short ones (at most 192 rows) the few-rows one."""
+    product, short ones (at most 192 rows) the few-rows one, at most 64 rows
+    the one-launch form."""
     case = _fp8_case(31, batch=4, max_len=max_len, page_size=16, K=512, rope=64, N=512)
-    assert (case.M > 192) == (max_len == 300)
+    assert (case.M > 192) == (max_len == 300) and (case.M <= 64) == (max_len == 14)
     c = case.cache
     rng = np.random.default_rng(31)
     sc = c.scales.copy()
