@@ -282,6 +282,28 @@ constexpr int fg_late_chunks()
     return n;
 }
 
+// Maximum over each 16-lane group of values that are >= 0 and not NaN, on
+// their bit patterns (for such floats the integer order is the float order):
+// one DPP maximum per step, where a float maximum also canonicalises its
+// operand first.
+__device__ inline float fg_max16_nonneg(float v)
+{
+    int x = __float_as_int(v);
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true));    // quad_perm [1, 0, 3, 2]
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));    // quad_perm [2, 3, 0, 1]
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true));   // row_half_mirror
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, true));   // row_mirror
+    return __int_as_float(x);
+}
+
+// Four floats -> four e4m3fn codes in one dword (hardware conversion, round
+// to nearest even): the second pair is converted straight into the high half.
+__device__ inline uint32_t fg_e4m3x4(float a, float b, float c, float d)
+{
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
 template <int MB, bool CACHE8>
 __device__ inline void fg_body(const DecompressArgs& a)
 {
@@ -450,22 +472,23 @@ __device__ inline void fg_body(const DecompressArgs& a)
         //    16 p + 4 w + k of scale block kb, 8 values each.
         const int lg = lane & 15, lr = lane >> 4;
         u32x4 qv[FS_KB][NP];
-    #pragma unroll
+#pragma unroll
         for (int kb = 0; kb < FS_KB; ++kb)
-    #pragma unroll
+#pragma unroll
             for (int p = 0; p < NP; ++p)
                 qv[kb][p] = lds_ld16(xs + kb * RB + (16 * p + 4 * wave + lr) * 256 + lg * 16);
         float my_am = 0.0f;
-    #pragma unroll
+#pragma unroll
         for (int kb = 0; kb < FS_KB; ++kb)
-    #pragma unroll
+#pragma unroll
             for (int p = 0; p < NP; ++p) {
                 const u32x4 v = qv[kb][p];
+                // am starts at 0 and fmaxf passes over NaN: am >= 0, not NaN.
                 float am = 0.0f;
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 4; ++i)
                     am = fmaxf(am, fmaxf(fabsf(bf16_lo(v[i])), fabsf(bf16_hi(v[i]))));
-                am = max16(am);
+                am = fg_max16_nonneg(am);
                 my_am = lg % NU == kb * NP + p ? am : my_am;
             }
         float my_s = 1.0f, my_inv = 1.0f;
@@ -473,21 +496,21 @@ __device__ inline void fg_body(const DecompressArgs& a)
             my_s = my_am / 448.0f;
             my_inv = 448.0f / my_am;
         }
-    #pragma unroll
+#pragma unroll
         for (int kb = 0; kb < FS_KB; ++kb)
-    #pragma unroll
+#pragma unroll
             for (int p = 0; p < NP; ++p) {
                 const int r = 16 * p + 4 * wave + lr;
                 const u32x4 v = qv[kb][p];
                 float x[8];
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     x[2 * i] = bf16_lo(v[i]);
                     x[2 * i + 1] = bf16_hi(v[i]);
                 }
                 const float inv = row16_lane(my_inv, kb * NP + p);
-                const u32x2 codes = {pack_e4m3x2(x[0] * inv, x[1] * inv) | (pack_e4m3x2(x[2] * inv, x[3] * inv) << 16),
-                                     pack_e4m3x2(x[4] * inv, x[5] * inv) | (pack_e4m3x2(x[6] * inv, x[7] * inv) << 16)};
+                const u32x2 codes = {fg_e4m3x4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv),
+                                     fg_e4m3x4(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv)};
                 lds_st8(aq[kb] + r * FS_ROWB + (((lg >> 1) ^ ((r >> 1) & 7)) * 16) + (lg & 1) * 8, codes);
                 const float sq = row16_lane(my_s, kb * NP + p);
                 if (lg == 0)
